@@ -1,0 +1,201 @@
+"""CPU oracle for per-row symmetric b-bit quantization, bit packing and the
+dequantized matmul.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check in
+``__graft_entry__`` and by the CPU-baseline leg of ``bench.py``.  The product
+package never imports it and shares no code with it.
+
+The arithmetic lives in ``dq_oracle.c`` (plain C, built with gcc, no fast-math,
+no FMA contraction).  This module only marshals numpy arrays.  Each function
+names the passage it follows:
+
+* quantizer -- "量化" tutorial (aiknowledge.cn), "how quantization works" and
+  "Step 1" symmetric per-channel code, one channel = one row of W[N, K];
+* packing -- DynaQuant page (zingnex.cn), "custom kernel architecture" (packed
+  N-bit storage) and "status and roadmap" (pack / unpack utilities);
+* matmul -- BPDQ article (devpress.csdn.net) section 3.2 (dequantize fused
+  with the product, fp32 scales, fp32 output), computed here in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libdq_oracle.so")
+
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+             "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+_default = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile ``src`` (default: the oracle) with gcc into the shared library ``out``."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, src, "-o", tmp])
+        os.replace(tmp, out)
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_bits(bits: int):
+    if not 2 <= bits <= 15:
+        raise ValueError("bits must be in [2, 15]")
+
+
+class Oracle:
+    """numpy marshalling around one build of ``dq_oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.oracle_row_bytes.argtypes = [i64, i32]
+        lib.oracle_row_bytes.restype = i64
+        lib.oracle_quantize_pack.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        lib.oracle_quantize_pack.restype = None
+        lib.oracle_pack.argtypes = [vp, i64, i64, i32, vp]
+        lib.oracle_pack.restype = None
+        lib.oracle_unpack.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+        lib.oracle_unpack.restype = None
+        lib.oracle_matmul.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp]
+        lib.oracle_matmul.restype = None
+        lib.oracle_matmul_pairs.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp, i64, vp, vp]
+        lib.oracle_matmul_pairs.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def row_bytes(self, K: int, bits: int) -> int:
+        """Bytes of one packed row: ceil(K*bits/8) rounded up to a multiple of 128."""
+        return int(self.lib.oracle_row_bytes(K, bits))
+
+    def quantize_pack(self, w: np.ndarray, bits: int):
+        """Quantize W[N, K] per row and pack it.
+
+        ``w`` is float32, or uint16 holding bf16 bit patterns.
+        Returns (packed uint32 [N, row_bytes/4], scales float32 [N], q int32 [N, K]).
+        """
+        _check_bits(bits)
+        w = np.ascontiguousarray(w)
+        if w.dtype == np.float32:
+            dtype = 0
+        elif w.dtype == np.uint16:
+            dtype = 1
+        else:
+            raise TypeError("w must be float32 or uint16 (bf16 bits)")
+        N, K = w.shape
+        packed = np.empty((N, self.row_bytes(K, bits) // 4), dtype=np.uint32)
+        scales = np.empty((N,), dtype=np.float32)
+        q = np.empty((N, K), dtype=np.int32)
+        self.lib.oracle_quantize_pack(_ptr(w), dtype, N, K, bits, _ptr(packed), _ptr(scales), _ptr(q))
+        return packed, scales, q
+
+    def pack(self, q: np.ndarray, bits: int) -> np.ndarray:
+        """Pack int32 codes q[N, K] (each in [-2^(b-1), 2^(b-1))) into [N, row_bytes/4] words."""
+        _check_bits(bits)
+        q = np.ascontiguousarray(q, dtype=np.int32)
+        N, K = q.shape
+        lim = 1 << (bits - 1)
+        if q.size and (q.min() < -lim or q.max() >= lim):
+            raise ValueError("code out of range for %d bits" % bits)
+        packed = np.empty((N, self.row_bytes(K, bits) // 4), dtype=np.uint32)
+        self.lib.oracle_pack(_ptr(q), N, K, bits, _ptr(packed))
+        return packed
+
+    def unpack(self, packed: np.ndarray, scales, N: int, K: int, bits: int):
+        """Inverse of the packing.  Returns (q int32 [N, K], w_hat float32 [N, K] or None)."""
+        _check_bits(bits)
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        assert packed.size == N * (self.row_bytes(K, bits) // 4)
+        q = np.empty((N, K), dtype=np.int32)
+        w_hat = None
+        if scales is not None:
+            scales = np.ascontiguousarray(scales, dtype=np.float32)
+            w_hat = np.empty((N, K), dtype=np.float32)
+        self.lib.oracle_unpack(_ptr(packed), _ptr(scales), N, K, bits, _ptr(q), _ptr(w_hat))
+        return q, w_hat
+
+    def matmul(self, x_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int,
+               bits: int):
+        """fp64 y[M, N] = s[n] * sum_k x[m,k] q[n,k] and bound[M, N] = |s| * sum_k |x q|."""
+        _check_bits(bits)
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M = x.shape[0]
+        assert x.shape == (M, K)
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        y = np.empty((M, N), dtype=np.float64)
+        bound = np.empty((M, N), dtype=np.float64)
+        self.lib.oracle_matmul(_ptr(x), M, _ptr(packed), _ptr(scales), N, K, bits, _ptr(y),
+                               _ptr(bound))
+        return y, bound
+
+    def matmul_pairs(self, x_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int,
+                     K: int, bits: int, ms, ns):
+        """``matmul`` for the listed (m, n) pairs only.  Returns (y, bound) 1-D fp64."""
+        _check_bits(bits)
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M = x.shape[0]
+        assert x.shape == (M, K)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        assert ms.shape == ns.shape
+        assert (ms >= 0).all() and (ms < M).all() and (ns >= 0).all() and (ns < N).all()
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        y = np.empty(ms.shape, dtype=np.float64)
+        bound = np.empty(ms.shape, dtype=np.float64)
+        self.lib.oracle_matmul_pairs(_ptr(x), M, _ptr(packed), _ptr(scales), N, K, bits,
+                                     _ptr(ms), _ptr(ns), ms.size, _ptr(y), _ptr(bound))
+        return y, bound
+
+
+def default() -> Oracle:
+    """The oracle built from ``dq_oracle.c`` (compiled on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def row_bytes(K: int, bits: int) -> int:
+    return default().row_bytes(K, bits)
+
+
+def quantize_pack(w: np.ndarray, bits: int):
+    return default().quantize_pack(w, bits)
+
+
+def pack(q: np.ndarray, bits: int) -> np.ndarray:
+    return default().pack(q, bits)
+
+
+def unpack(packed: np.ndarray, scales, N: int, K: int, bits: int):
+    return default().unpack(packed, scales, N, K, bits)
+
+
+def matmul(x_bf16, packed, scales, N: int, K: int, bits: int):
+    return default().matmul(x_bf16, packed, scales, N, K, bits)
+
+
+def matmul_pairs(x_bf16, packed, scales, N: int, K: int, bits: int, ms, ns):
+    return default().matmul_pairs(x_bf16, packed, scales, N, K, bits, ms, ns)
