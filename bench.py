@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed b-bit weight path on one MI355X.
+
+One step = one pass of the whole path over the synthetic workload:
+  1. quantize + pack the five 4096x4096 decode matrices (b = 4, 5, 6, 7, 8);
+  2. unpack them back to int32 codes;
+  3. quantize + pack the four 8192x8192 prefill matrices (b = 5, 6, 8, 12);
+  4. GEMM x[2048, 8192] . W^T for each prefill matrix;
+  5. GEMV x[1, 4096] . W^T for each decode matrix.
+The GEMVs run last, after ~1.5 GB of other traffic, so their packed weights
+are read from HBM rather than from the 256 MB last-level cache.
+
+Reported ``value`` is the metric's first half: packed-weight GB/s of the M=1
+GEMV (sum of packed bytes over the sum of the GEMV kernel times, measured with
+HIP events on the launch stream).  The GEMM's TFLOP/s (the metric's second
+half) is reported in ``roofline_gemm``.  Every input is resident in HBM before
+the timed region.  The CPU baseline is the oracle's fp64 GEMV on the same
+decode matrices, timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+
+DECODE = dict(N=4096, K=4096, bits=(4, 5, 6, 7, 8), M=1)
+PREFILL = dict(N=8192, K=8192, bits=(5, 6, 8, 12), M=2048)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixed_precision_weight_dq_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f in ("gemv.hip", "common.hpp"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary,
+    if it was taken on the current GEMV source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch_avg")
+
+
+def cpu_baseline(decode_w, x1, target_s: float):
+    """The oracle's fp64 GEMV (unpack bit by bit + dot product) over the decode
+    matrices, repeated until about target_s seconds of CPU time."""
+    import oracle
+    packs = []
+    for b, w in decode_w.items():
+        p, s, _ = oracle.quantize_pack(w, b)
+        packs.append((b, p, s))
+    done_bytes, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for b, p, s in packs:
+            oracle.matmul(x1, p, s, DECODE["N"], DECODE["K"], b)
+            done_bytes += DECODE["N"] * DECODE["K"] * b // 8
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "fp64 GEMV M=1 over the five 4096x4096 decode matrices (b=4..8), "
+                      "%d passes, %.1f s" % (reps, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixed_precision_weight_dq_amd as dq
+    import workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def bf16(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs (seeded, synthetic), resident in HBM before timing
+    wl2, wl4 = workload.WORKLOADS[2], workload.WORKLOADS[4]
+    decode_np = {b: workload.workload_weights(wl2, i) for i, b in enumerate(DECODE["bits"])}
+    x1_np = workload.activations(2, 0, DECODE["M"], DECODE["K"])
+    W2 = {b: bf16(w) for b, w in decode_np.items()}
+    X1 = bf16(x1_np)
+    W4 = {b: bf16(workload.workload_weights(wl4, i)) for i, b in enumerate(PREFILL["bits"])}
+    X4 = bf16(workload.activations(4, 0, PREFILL["M"], PREFILL["K"]))
+
+    def rw(K, b):
+        return dq.packed_row_bytes(K, b) // 4
+
+    P2 = {b: torch.empty((DECODE["N"], rw(DECODE["K"], b)), dtype=torch.int32, device=dev) for b in W2}
+    S2 = {b: torch.empty((DECODE["N"],), dtype=torch.float32, device=dev) for b in W2}
+    Q2 = {b: torch.empty((DECODE["N"], DECODE["K"]), dtype=torch.int32, device=dev) for b in W2}
+    Y1 = {b: torch.empty((1, DECODE["N"]), dtype=torch.float32, device=dev) for b in W2}
+    P4 = {b: torch.empty((PREFILL["N"], rw(PREFILL["K"], b)), dtype=torch.int32, device=dev) for b in W4}
+    S4 = {b: torch.empty((PREFILL["N"],), dtype=torch.float32, device=dev) for b in W4}
+    Y4 = torch.empty((PREFILL["M"], PREFILL["N"]), dtype=torch.float32, device=dev)
+
+    ops = []  # (kind, b, callable)
+    for b in W2:
+        ops.append(("quantize_pack_4096", b, lambda b=b: dq.quantize_pack(W2[b], b, P2[b], S2[b])))
+    for b in W2:
+        ops.append(("unpack_4096", b, lambda b=b: dq._check(dq.dq_unpack(
+            P2[b].data_ptr(), 0, DECODE["N"], DECODE["K"], b, Q2[b].data_ptr(), 0,
+            stream.cuda_stream), "dq_unpack")))
+    for b in W4:
+        ops.append(("quantize_pack_8192", b, lambda b=b: dq.quantize_pack(W4[b], b, P4[b], S4[b])))
+    for b in W4:
+        ops.append(("gemm_2048", b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
+    for b in W2:
+        ops.append(("gemv_m1", b, lambda b=b: dq.gemv(X1, P2[b], S2[b], DECODE["K"], b, Y1[b])))
+
+    nops = len(ops)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        for i, (_, _, fn) in enumerate(ops):
+            fn()
+            if events is not None:
+                events[i + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-op durations (ms), averaged over steps
+    dur = np.zeros((args.steps, nops))
+    for s in range(args.steps):
+        for i in range(nops):
+            dur[s, i] = ev[s][i].elapsed_time(ev[s][i + 1])
+    avg = dur.mean(axis=0)
+
+    def pick(kind):
+        return [(ops[i][1], avg[i]) for i in range(nops) if ops[i][0] == kind]
+
+    Nd, Kd = DECODE["N"], DECODE["K"]
+    Np, Kp, Mp = PREFILL["N"], PREFILL["K"], PREFILL["M"]
+    gemv = pick("gemv_m1")
+    gemv_bytes = {b: Nd * Kd * b // 8 for b, _ in gemv}
+    gemv_ms = sum(t for _, t in gemv)
+    value = sum(gemv_bytes.values()) / (gemv_ms * 1e-3) / 1e9
+    gemm = pick("gemm_2048")
+    gemm_flop = 2.0 * Mp * Np * Kp
+    gemm_tflops = {b: gemm_flop / (t * 1e-3) / 1e12 for b, t in gemm}
+    gemm_avg_ms = float(np.mean([t for _, t in gemm]))
+    gemm_le9 = [t for b, t in gemm if b <= 9]
+
+    def qp_gbs(kind, N, K):
+        return {str(b): round((N * K * 2 + N * K * b // 8) / (t * 1e-3) / 1e9, 1) for b, t in pick(kind)}
+
+    traffic = recorded_traffic()
+    out = {
+        "metric": "packed-weight GB/s & % HBM peak (M=1 GEMV); TFLOP/s & % MFMA peak (M=2048)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; bf16 W ~ N(0, 0.02^2) with 0.1% x20 outliers, x ~ N(0, 1))",
+        "config": {
+            "workload": "decode GEMV 4096x4096 b=4..8 M=1 (value) + prefill GEMM "
+                        "M=2048 N=K=8192 b=5,6,8,12 (roofline_gemm)",
+            "gemv": {"N": Nd, "K": Kd, "M": 1, "bits": list(DECODE["bits"])},
+            "gemm": {"N": Np, "K": Kp, "M": Mp, "bits": list(PREFILL["bits"]),
+                     "mfma_dtype": "bf16", "accumulate": "f32"},
+            "step": "quantize+pack(5 decode) -> unpack(5) -> quantize+pack(4 prefill) -> "
+                    "gemm(4) -> gemv(5)",
+        },
+        "roofline": {
+            "kernel": "dq_gemv M=1 (five launches, b=4..8)",
+            "bound": "hbm",
+            "achieved": round(value, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "roofline_gemm": {
+            "kernel": "dq_gemm M=2048 N=K=8192",
+            "bound": "mfma",
+            "achieved": round(gemm_flop / (float(np.mean(gemm_le9)) * 1e-3) / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_flop / (float(np.mean(gemm_le9)) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "over": "b <= 9 launches (b >= 10 issues twice the MFMA work by design)",
+            "per_bits": {str(b): round(v, 1) for b, v in gemm_tflops.items()},
+        },
+        "components_ms": {
+            kind: {str(b): round(float(t), 5) for b, t in pick(kind)}
+            for kind in ("quantize_pack_4096", "unpack_4096", "quantize_pack_8192", "gemm_2048", "gemv_m1")
+        },
+        "gemv_gbs_per_bits": {str(b): round(gemv_bytes[b] / (t * 1e-3) / 1e9, 1) for b, t in gemv},
+        "quantize_pack_gbs": {"4096": qp_gbs("quantize_pack_4096", Nd, Kd),
+                              "8192": qp_gbs("quantize_pack_8192", Np, Kp)},
+        "gemm_avg_ms": round(gemm_avg_ms, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(decode_np, x1_np, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

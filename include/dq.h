@@ -1,0 +1,122 @@
+/*
+ * dq.h -- C ABI of the packed b-bit weight library for MI355X (gfx950).
+ *
+ * What it computes (pages as titled on the web):
+ *  - Quantizer: the symmetric per-channel scheme of the "量化" (Quantization)
+ *    tutorial, aiknowledge.cn, sections "量化怎么工作" (how quantization works)
+ *    and "Step 1" (per-channel code), with one channel = one row of W[N, K]:
+ *      qmax = 2^(b-1) - 1;  s[n] = fl32(max_k |W[n,k]| / qmax)  (1.0 replaces a
+ *      zero max before the divide);  q = clip(rint(fl32(W / s)), -qmax-1, qmax)
+ *    with IEEE fp32 arithmetic, a correctly rounded divide and
+ *    round-half-to-even.  One bit width b in [2, 15] per call (per matrix), the
+ *    recipe application step of the DynaQuant page (zingnex.cn), section
+ *    "第三步：应用配方".
+ *  - Packed storage: DynaQuant page, "自定义内核架构" (packed N-bit codes in
+ *    memory, expanded in registers before the matrix unit) and "项目现状与路线图"
+ *    (pack / unpack utilities).  Code u = q + 2^(b-1) (offset binary); the K
+ *    codes of a row form one bit stream, code k at stream bits [k*b, k*b+b),
+ *    stream bit i = bit (i mod 32) of 32-bit word i/32 (little-endian words);
+ *    each row is zero-padded to dq_packed_row_bytes(K, b), a multiple of 128.
+ *  - Dequantized matmul: BPDQ article (devpress.csdn.net), section 3.2
+ *    (dequantize fused into the matrix product; int weights, fp32 scales, fp32
+ *    output):  y[m,n] = s[n] * sum_k x[m,k] * q[n,k],  i.e. y = x . W_hat^T.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers (memory of the current HIP
+ *    device).  The caller allocates and owns every buffer; the library
+ *    allocates nothing, keeps no state between calls and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously; nothing is synchronised.
+ *  - Argument errors are detected on the host and returned BEFORE any HIP call;
+ *    then nothing is enqueued and no output is touched.  A launch failure
+ *    returns DQ_ERR_HIP; dq_last_error() then gives the HIP message (per
+ *    calling thread).
+ *  - Layouts are row-major and contiguous:
+ *      W       [N, K]          fp32 or bf16 bit patterns (uint16)
+ *      packed  [N, row_words]  uint32, row_words = dq_packed_row_bytes(K,b)/4
+ *      scales  [N]             fp32
+ *      x       [M, K]          bf16 bit patterns (uint16)
+ *      y       [M, N]          fp32 (overwritten, never accumulated into)
+ *  - Sizes: 1 <= N <= 2^31-1, 1 <= K <= DQ_MAX_K; dq_gemv: 1 <= M <= 16;
+ *    dq_gemm: 1 <= M <= 2^31-1.
+ *  - Alignment: W, packed and x must be 16-byte aligned (DQ_ERR_ALIGN);
+ *    scales, q_out, w_out and y 4-byte aligned.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dq_status;
+
+#define DQ_OK 0
+#define DQ_ERR_NULL 1  /* a required pointer is NULL                         */
+#define DQ_ERR_BITS 2  /* bits outside [2, 15]                               */
+#define DQ_ERR_SHAPE 3 /* N, K or M outside the ranges above                 */
+#define DQ_ERR_ALIGN 4 /* a pointer is not aligned as required               */
+#define DQ_ERR_DTYPE 5 /* w_dtype is neither DQ_F32 nor DQ_BF16              */
+#define DQ_ERR_HIP 6   /* a HIP launch or runtime call failed                */
+
+#define DQ_F32 0  /* W holds IEEE fp32 values                               */
+#define DQ_BF16 1 /* W holds bf16 bit patterns (uint16)                     */
+
+#define DQ_MIN_BITS 2
+#define DQ_MAX_BITS 15
+#define DQ_GEMV_MAX_M 16
+#define DQ_MAX_K (1LL << 22)
+
+/* Bytes of one packed row: ceil(K*bits/8) rounded up to a multiple of 128.
+ * Returns 0 when K or bits is out of range.  Host-only, no HIP call. */
+size_t dq_packed_row_bytes(int64_t K, int32_t bits);
+
+/* Quantize W[N, K] row by row to `bits` bits and pack it.
+ *   w       in   device, [N, K], dtype w_dtype (DQ_F32 or DQ_BF16)
+ *   packed  out  device, [N, row_words] uint32, fully written (padding = 0)
+ *   scales  out  device, [N] fp32
+ * A row holding a NaN or +-Inf gets scale = quiet NaN (bits 0x7FC00000) and
+ * every code = 2^(b-1) (q = 0).  A row whose max|W| / qmax underflows to 0 is
+ * treated like an all-zero row: scale = fl32(1/qmax), q = 0. */
+dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                           uint32_t* packed, float* scales, void* stream);
+
+/* Inverse of the packing.
+ *   packed  in   device, [N, row_words] uint32
+ *   scales  in   device, [N] fp32; may be NULL when w_out is NULL
+ *   q_out   out  device, [N, K] int32, q = u - 2^(b-1); may be NULL
+ *   w_out   out  device, [N, K] fp32, fl32(q * s[n]); may be NULL
+ * At least one of q_out and w_out must be non-NULL. */
+dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
+                    int32_t bits, int32_t* q_out, float* w_out, void* stream);
+
+/* Decode-shaped product, 1 <= M <= 16:  y[m,n] = s[n] * sum_k x[m,k] q[n,k].
+ *   x       in   device, [M, K] bf16 bits
+ *   packed  in   device, [N, row_words] uint32 (from dq_quantize_pack)
+ *   scales  in   device, [N] fp32
+ *   y       out  device, [M, N] fp32
+ * Accumulates in fp32; the scale is applied once per output after the sum. */
+dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                  int64_t N, int64_t K, int32_t bits, float* y, void* stream);
+
+/* Prefill-shaped product, any M >= 1 (tuned for M >= 256).  Same arguments
+ * and result as dq_gemv.  Codes are expanded exactly to bf16 (for b >= 10 as
+ * two exact bf16 halves, 64*hi + lo) and multiplied on the bf16 matrix cores
+ * with fp32 accumulation. */
+dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                  int64_t N, int64_t K, int32_t bits, float* y, void* stream);
+
+/* Static text for a status code. */
+const char* dq_status_string(dq_status status);
+
+/* Text of the last DQ_ERR_HIP on the calling thread ("" if none). */
+const char* dq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ_H */

@@ -1,0 +1,209 @@
+"""Python binding of ``libdq.so``: packed b-bit weight quantization and the
+dequantized GEMV / GEMM on MI355X (gfx950).
+
+Two layers, both argument marshalling only (every step runs in the HIP
+kernels behind the C ABI declared in ``include/dq.h``):
+
+* ``dq_packed_row_bytes``, ``dq_quantize_pack``, ``dq_unpack``, ``dq_gemv``,
+  ``dq_gemm`` -- the C entry points under their own names, taking integer
+  device addresses and sizes; they return the ``dq_status`` code.
+* ``quantize_pack``, ``unpack``, ``gemv``, ``gemm`` -- the same calls on torch
+  tensors (torch provides device memory and the current stream); they check
+  device, dtype and contiguity, allocate outputs with torch and raise
+  ``DQError`` on a non-zero status.
+
+There is no fallback: if the library is missing or the device is not a GPU,
+the calls fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "DQError", "DQ_F32", "DQ_BF16", "library_path", "dq_packed_row_bytes", "dq_quantize_pack",
+    "dq_unpack", "dq_gemv", "dq_gemm", "dq_status_string", "dq_last_error", "packed_row_bytes",
+    "quantize_pack", "unpack", "gemv", "gemm", "load",
+]
+
+DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP = range(7)
+DQ_F32, DQ_BF16 = 0, 1
+GEMV_MAX_M = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdq.so")
+_lib = None
+
+
+class DQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = "%s: %s" % (where, dq_status_string(status))
+        if status == DQ_ERR_HIP:
+            msg += " (%s)" % dq_last_error()
+        super().__init__(msg)
+        self.status = status
+
+
+def load():
+    """Load libdq.so (built in-tree by ``mixed_precision_weight_dq_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError("libdq.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m mixed_precision_weight_dq_amd.build" % library_path)
+    lib = ctypes.CDLL(library_path)
+    i64, i32, vp, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32
+    lib.dq_packed_row_bytes.argtypes = [i64, i32]
+    lib.dq_packed_row_bytes.restype = ctypes.c_size_t
+    lib.dq_quantize_pack.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+    lib.dq_quantize_pack.restype = st
+    lib.dq_unpack.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+    lib.dq_unpack.restype = st
+    lib.dq_gemv.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemv.restype = st
+    lib.dq_gemm.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemm.restype = st
+    lib.dq_status_string.argtypes = [st]
+    lib.dq_status_string.restype = ctypes.c_char_p
+    lib.dq_last_error.argtypes = []
+    lib.dq_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+
+def dq_packed_row_bytes(K: int, bits: int) -> int:
+    return int(load().dq_packed_row_bytes(K, bits))
+
+
+def dq_quantize_pack(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int, scales: int,
+                     stream: int = 0) -> int:
+    return int(load().dq_quantize_pack(w, w_dtype, N, K, bits, packed, scales, stream))
+
+
+def dq_unpack(packed: int, scales: int, N: int, K: int, bits: int, q_out: int, w_out: int,
+              stream: int = 0) -> int:
+    return int(load().dq_unpack(packed, scales, N, K, bits, q_out, w_out, stream))
+
+
+def dq_gemv(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, y: int,
+            stream: int = 0) -> int:
+    return int(load().dq_gemv(x, M, packed, scales, N, K, bits, y, stream))
+
+
+def dq_gemm(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, y: int,
+            stream: int = 0) -> int:
+    return int(load().dq_gemm(x, M, packed, scales, N, K, bits, y, stream))
+
+
+def dq_status_string(status: int) -> str:
+    return load().dq_status_string(status).decode()
+
+
+def dq_last_error() -> str:
+    return load().dq_last_error().decode()
+
+
+# ----------------------------------------------------------- torch tensors
+
+def packed_row_bytes(K: int, bits: int) -> int:
+    rb = dq_packed_row_bytes(K, bits)
+    if rb == 0:
+        raise DQError(DQ_ERR_SHAPE if 2 <= bits <= 15 else DQ_ERR_BITS, "packed_row_bytes")
+    return rb
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtypes, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s dtype %s not in %s" % (name, t.dtype, dtypes))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-D tensor" % (name, ndim))
+
+
+def _check(status: int, where: str):
+    if status != DQ_OK:
+        raise DQError(status, where)
+
+
+def quantize_pack(w, bits: int, packed=None, scales=None):
+    """W[N, K] (float32 or bfloat16, on the GPU) -> (packed int32 [N, row_bytes/4] holding
+    the uint32 words, scales float32 [N])."""
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16), 2)
+    N, K = w.shape
+    rw = packed_row_bytes(K, bits) // 4
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _need(packed, "packed", (torch.int32,), 2)
+    _need(scales, "scales", (torch.float32,), 1)
+    if tuple(packed.shape) != (N, rw) or tuple(scales.shape) != (N,):
+        raise ValueError("packed/scales shape mismatch")
+    dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
+    _check(dq_quantize_pack(w.data_ptr(), dt, N, K, bits, packed.data_ptr(), scales.data_ptr(),
+                            _stream(w)), "dq_quantize_pack")
+    return packed, scales
+
+
+def unpack(packed, scales, K: int, bits: int, want_q: bool = True, want_w: bool = False):
+    """packed [N, row_words] -> (q int32 [N, K] or None, w_hat float32 [N, K] or None)."""
+    torch = _torch()
+    _need(packed, "packed", (torch.int32,), 2)
+    N = packed.shape[0]
+    if packed.shape[1] != packed_row_bytes(K, bits) // 4:
+        raise ValueError("packed row length does not match K and bits")
+    q = torch.empty((N, K), dtype=torch.int32, device=packed.device) if want_q else None
+    w = torch.empty((N, K), dtype=torch.float32, device=packed.device) if want_w else None
+    if scales is not None:
+        _need(scales, "scales", (torch.float32,), 1)
+    _check(dq_unpack(packed.data_ptr(), scales.data_ptr() if scales is not None else 0, N, K, bits,
+                     q.data_ptr() if q is not None else 0, w.data_ptr() if w is not None else 0,
+                     _stream(packed)), "dq_unpack")
+    return q, w
+
+
+def _matmul(fn, name, x, packed, scales, K: int, bits: int, y=None):
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(packed, "packed", (torch.int32,), 2)
+    _need(scales, "scales", (torch.float32,), 1)
+    M = x.shape[0]
+    N = packed.shape[0]
+    if x.shape[1] != K or packed.shape[1] != packed_row_bytes(K, bits) // 4 or scales.shape[0] != N:
+        raise ValueError("shape mismatch between x, packed, scales, K and bits")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(fn(x.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K, bits, y.data_ptr(),
+              _stream(x)), name)
+    return y
+
+
+def gemv(x, packed, scales, K: int, bits: int, y=None):
+    """y[M, N] = x . dequant(W)^T for 1 <= M <= 16 (fp32 accumulate)."""
+    return _matmul(dq_gemv, "dq_gemv", x, packed, scales, K, bits, y)
+
+
+def gemm(x, packed, scales, K: int, bits: int, y=None):
+    """y[M, N] = x . dequant(W)^T on the bf16 matrix cores (any M >= 1)."""
+    return _matmul(dq_gemm, "dq_gemm", x, packed, scales, K, bits, y)

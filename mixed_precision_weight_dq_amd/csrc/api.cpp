@@ -1,0 +1,110 @@
+// C ABI of the library (declared in include/dq.h): argument validation on the
+// host, then one kernel launch on the caller's stream.  No allocation, no
+// synchronisation, no state beyond the per-thread text of the last HIP error.
+#include "../../include/dq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+dq_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return DQ_OK;
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e),
+                  hipGetErrorString(e));
+    return DQ_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+dq_status check_common(int64_t N, int64_t K, int32_t bits)
+{
+    if (bits < DQ_MIN_BITS || bits > DQ_MAX_BITS) return DQ_ERR_BITS;
+    if (N < 1 || N > 0x7fffffffLL || K < 1 || K > DQ_MAX_K) return DQ_ERR_SHAPE;
+    return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dq_packed_row_bytes(int64_t K, int32_t bits)
+{
+    if (bits < DQ_MIN_BITS || bits > DQ_MAX_BITS || K < 1 || K > DQ_MAX_K) return 0;
+    return (size_t)dq::packed_row_words(K, bits) * 4;
+}
+
+dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                           uint32_t* packed, float* scales, void* stream)
+{
+    if (!w || !packed || !scales) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_quantize_pack(w, w_dtype == DQ_BF16, N, K, bits, packed, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
+                    int32_t bits, int32_t* q_out, float* w_out, void* stream)
+{
+    if (!packed || (!q_out && !w_out) || (w_out && !scales)) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(q_out, 4) || !aligned(w_out, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_unpack(packed, scales, N, K, bits, q_out, w_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                  int64_t N, int64_t K, int32_t bits, float* y, void* stream)
+{
+    if (!x || !packed || !scales || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(
+        dq::launch_gemv(x, M, packed, scales, N, K, bits, y, static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                  int64_t N, int64_t K, int32_t bits, float* y, void* stream)
+{
+    if (!x || !packed || !scales || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > 0x7fffffffLL) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(
+        dq::launch_gemm(x, M, packed, scales, N, K, bits, y, static_cast<hipStream_t>(stream)));
+}
+
+const char* dq_status_string(dq_status status)
+{
+    switch (status) {
+    case DQ_OK: return "ok";
+    case DQ_ERR_NULL: return "a required pointer is NULL";
+    case DQ_ERR_BITS: return "bits must be in [2, 15]";
+    case DQ_ERR_SHAPE: return "N, K or M out of range";
+    case DQ_ERR_ALIGN: return "pointer not aligned (W, packed, x: 16 bytes; others: 4 bytes)";
+    case DQ_ERR_DTYPE: return "w_dtype must be DQ_F32 or DQ_BF16";
+    case DQ_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* dq_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Shared device helpers for the packed b-bit kernels (gfx950, wave64).
+//
+// Packed layout (DynaQuant page, "自定义内核架构": b-bit codes stored densely and
+// expanded in registers): code u = q + 2^(b-1) of element k of a row sits at
+// stream bits [k*b, k*b+b); stream bit i is bit (i & 31) of word i >> 5.
+// A run of 32 consecutive codes therefore fills exactly b whole words, which
+// is the unit ("chunk") every kernel here works on: one lane owns one chunk and
+// never shares a word with another lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 32;  // codes per chunk; a chunk is exactly B words
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Word i of a chunk holds the top bit of every code whose last bit lands in it.
+// XOR-ing a word with this mask turns each offset-binary code (q + 2^(b-1))
+// into the b-bit two's complement of q, so a signed bit-field extract yields q.
+template <int B>
+__host__ __device__ constexpr uint32_t code_msb_mask(int word)
+{
+    uint32_t m = 0;
+    for (int j = 0; j < kChunk; ++j) {
+        const int pos = j * B + B - 1;
+        if ((pos >> 5) == word) m |= 1u << (pos & 31);
+    }
+    return m;
+}
+
+// Signed code j (0..31) of a chunk whose words were XOR-ed with code_msb_mask.
+// j is a compile-time constant after unrolling, so this is a bfe_i32 or an
+// alignbit + bfe_i32.
+template <int B>
+__device__ __forceinline__ int32_t chunk_code_signed(const uint32_t* w, int j)
+{
+    const int pos = j * B;
+    const int wi = pos >> 5;
+    const int off = pos & 31;
+    uint32_t v;
+    if (off + B <= 32) {
+        v = w[wi] >> off;
+    } else {
+        v = (uint32_t)((((uint64_t)w[wi + 1]) << 32 | w[wi]) >> off);
+    }
+    return ((int32_t)(v << (32 - B))) >> (32 - B);
+}
+
+// Unsigned (offset-binary) code j of an unmodified chunk.
+template <int B>
+__device__ __forceinline__ uint32_t chunk_code_unsigned(const uint32_t* w, int j)
+{
+    const int pos = j * B;
+    const int wi = pos >> 5;
+    const int off = pos & 31;
+    uint32_t v;
+    if (off + B <= 32) {
+        v = w[wi] >> off;
+    } else {
+        v = (uint32_t)((((uint64_t)w[wi + 1]) << 32 | w[wi]) >> off);
+    }
+    return v & ((1u << B) - 1u);
+}
+
+// Loads the B words of chunk c of a packed row.  Words at or beyond row_words
+// (possible only in a row's last chunk) read as zero.
+template <int B>
+__device__ __forceinline__ void load_chunk_words(const uint32_t* __restrict__ row, int64_t c,
+                                                 int64_t row_words, uint32_t* w)
+{
+    const int64_t base = c * B;
+    if (base + B <= row_words) {
+        const uint32_t* p = row + base;
+#pragma unroll
+        for (int i = 0; i < B; ++i) w[i] = p[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i) w[i] = (base + i < row_words) ? row[base + i] : 0u;
+    }
+}
+
+// Wave-wide reductions through cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)v, o, kWave);
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+}  // namespace dq

@@ -1,0 +1,45 @@
+// Host-side launchers of the kernels (internal to the library; the public
+// surface is the C ABI in include/dq.h).  Arguments are validated by the
+// caller; each launcher only picks a configuration and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                uint32_t* packed, float* scales, hipStream_t stream);
+hipError_t launch_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
+                         int bits, int32_t* q_out, float* w_out, hipStream_t stream);
+hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       int64_t N, int64_t K, int bits, float* y, hipStream_t stream);
+hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       int64_t N, int64_t K, int bits, float* y, hipStream_t stream);
+
+inline int64_t packed_row_words(int64_t K, int bits)
+{
+    return ((K * bits + 7) / 8 + 127) / 128 * 128 / 4;
+}
+
+// Expands CALL(B) for the run-time bit width, one template instance per width.
+#define DQ_BITS_SWITCH(bits, CALL)                                                                \
+    switch (bits) {                                                                               \
+    case 2: return CALL(2);                                                                       \
+    case 3: return CALL(3);                                                                       \
+    case 4: return CALL(4);                                                                       \
+    case 5: return CALL(5);                                                                       \
+    case 6: return CALL(6);                                                                       \
+    case 7: return CALL(7);                                                                       \
+    case 8: return CALL(8);                                                                       \
+    case 9: return CALL(9);                                                                       \
+    case 10: return CALL(10);                                                                     \
+    case 11: return CALL(11);                                                                     \
+    case 12: return CALL(12);                                                                     \
+    case 13: return CALL(13);                                                                     \
+    case 14: return CALL(14);                                                                     \
+    case 15: return CALL(15);                                                                     \
+    default: return hipErrorInvalidValue;                                                         \
+    }
+
+}  // namespace dq

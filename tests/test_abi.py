@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/dq.h declares, sizes rows as documented, and rejects every invalid
+argument on the host before any HIP call (so these run on a CPU-only machine:
+the fake device addresses below are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_weight_dq_amd as dq
+from pins import row_bytes_formula
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dq.h")
+
+A = 1 << 20  # a 16-byte aligned fake device address; never touched
+MIS = A + 4  # 4-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
+                 "dq_status_string", "dq_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dq.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_row_bytes():
+    for bits in range(2, 16):
+        for K in (1, 2, 31, 32, 33, 255, 256, 614, 4096, 5120, 8192, 17408, 1 << 22):
+            assert dq.dq_packed_row_bytes(K, bits) == row_bytes_formula(K, bits)
+    assert dq.dq_packed_row_bytes(0, 4) == 0
+    assert dq.dq_packed_row_bytes((1 << 22) + 1, 4) == 0
+    assert dq.dq_packed_row_bytes(64, 1) == 0
+    assert dq.dq_packed_row_bytes(64, 16) == 0
+
+
+def test_status_strings():
+    for s in range(7):
+        assert dq.dq_status_string(s)
+    assert dq.dq_status_string(99) == "unknown status"
+    assert dq.dq_last_error() == ""
+
+
+@pytest.mark.parametrize("bits", [0, 1, 16, 32, -3])
+def test_bits_rejected(bits):
+    assert dq.dq_quantize_pack(A, dq.DQ_BF16, 4, 64, bits, A, A) == dq.DQ_ERR_BITS
+    assert dq.dq_unpack(A, A, 4, 64, bits, A, 0) == dq.DQ_ERR_BITS
+    assert dq.dq_gemv(A, 1, A, A, 4, 64, bits, A) == dq.DQ_ERR_BITS
+    assert dq.dq_gemm(A, 1, A, A, 4, 64, bits, A) == dq.DQ_ERR_BITS
+
+
+@pytest.mark.parametrize("N,K", [(0, 64), (4, 0), (-1, 64), (4, -5), (1 << 31, 64),
+                                 (4, (1 << 22) + 1)])
+def test_shape_rejected(N, K):
+    assert dq.dq_quantize_pack(A, dq.DQ_F32, N, K, 6, A, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_unpack(A, A, N, K, 6, A, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_gemv(A, 1, A, A, N, K, 6, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_gemm(A, 1, A, A, N, K, 6, A) == dq.DQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("M", [0, -1, 17, 1000])
+def test_gemv_m_rejected(M):
+    assert dq.dq_gemv(A, M, A, A, 4, 64, 6, A) == dq.DQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("M", [0, -2, 1 << 31])
+def test_gemm_m_rejected(M):
+    assert dq.dq_gemm(A, M, A, A, 4, 64, 6, A) == dq.DQ_ERR_SHAPE
+
+
+def test_null_rejected():
+    assert dq.dq_quantize_pack(0, dq.DQ_BF16, 4, 64, 6, A, A) == dq.DQ_ERR_NULL
+    assert dq.dq_quantize_pack(A, dq.DQ_BF16, 4, 64, 6, 0, A) == dq.DQ_ERR_NULL
+    assert dq.dq_quantize_pack(A, dq.DQ_BF16, 4, 64, 6, A, 0) == dq.DQ_ERR_NULL
+    assert dq.dq_unpack(0, A, 4, 64, 6, A, A) == dq.DQ_ERR_NULL
+    assert dq.dq_unpack(A, A, 4, 64, 6, 0, 0) == dq.DQ_ERR_NULL  # no output requested
+    assert dq.dq_unpack(A, 0, 4, 64, 6, 0, A) == dq.DQ_ERR_NULL  # w_out needs scales
+    for fn in (dq.dq_gemv, dq.dq_gemm):
+        assert fn(0, 1, A, A, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, 1, 0, A, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, 1, A, 0, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, 1, A, A, 4, 64, 6, 0) == dq.DQ_ERR_NULL
+
+
+def test_dtype_rejected():
+    for dt in (-1, 2, 7):
+        assert dq.dq_quantize_pack(A, dt, 4, 64, 6, A, A) == dq.DQ_ERR_DTYPE
+
+
+def test_alignment_rejected():
+    assert dq.dq_quantize_pack(MIS, dq.DQ_F32, 4, 64, 6, A, A) == dq.DQ_ERR_ALIGN
+    assert dq.dq_quantize_pack(A, dq.DQ_F32, 4, 64, 6, MIS, A) == dq.DQ_ERR_ALIGN
+    assert dq.dq_quantize_pack(A, dq.DQ_F32, 4, 64, 6, A, A + 2) == dq.DQ_ERR_ALIGN
+    assert dq.dq_unpack(MIS, A, 4, 64, 6, A, 0) == dq.DQ_ERR_ALIGN
+    assert dq.dq_unpack(A, A, 4, 64, 6, A + 1, 0) == dq.DQ_ERR_ALIGN
+    for fn in (dq.dq_gemv, dq.dq_gemm):
+        assert fn(MIS, 1, A, A, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, MIS, A, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, A, A + 2, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, A, A, 4, 64, 6, A + 2) == dq.DQ_ERR_ALIGN
+
+
+def test_tensor_wrappers_refuse_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        dq.quantize_pack(w, 6)
+    with pytest.raises(dq.DQError):
+        dq.packed_row_bytes(64, 1)

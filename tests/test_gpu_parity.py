@@ -1,0 +1,206 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+inputs at sizes the oracle finishes quickly: several tiles and ragged tails,
+every bit width, special rows and special activations.
+
+Bars: quantize / pack / unpack bit-exact (packed words, scale bit patterns,
+codes, dequantized fp32); GEMV / GEMM |y - y_ref| <= 1e-4 * sum_k |x * w_hat|
+with y_ref in fp64 (exactly 0 where that sum is 0)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import mixed_precision_weight_dq_amd as dq
+import oracle
+import workload
+from gpu_util import bf16_gpu, f32_bits, report, torch, u32, weights_gpu
+from pins import within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+QUANT_SHAPES = [(1, 1), (3, 31), (5, 33), (7, 255), (2, 614), (64, 256), (33, 1000), (9, 8192 + 40)]
+
+
+def special_rows(K: int, bits: int) -> np.ndarray:
+    """fp32 rows exercising the quantizer's corner cases."""
+    qmax = (1 << (bits - 1)) - 1
+    s0 = 2.0 ** -6
+    rows = np.zeros((10, K), np.float32)
+    idx = np.arange(K)
+    rows[1] = 0.7 * np.where(idx % 2 == 0, 1, -1)  # constant magnitude, +-absmax
+    lv = (idx % (2 * qmax + 1)) - qmax  # every level exactly: w = j * s0
+    rows[2] = lv * s0
+    ties = ((idx % 12) - 6 + 0.5) * s0  # exact (j + 1/2) * s0
+    ties[0] = qmax * s0
+    rows[3] = ties
+    rows[4] = -0.0  # signed zeros
+    rows[5] = np.where(idx % 3 == 0, 3e-39, -1e-39)  # subnormal absmax
+    rows[5][0] = 5e-45
+    rows[6] = 1.4e-45 * (idx % 2)  # smallest subnormal / zero
+    rows[7] = np.where(idx % 2 == 0, 3.0e38, -1.0e38)  # near the top of the range
+    rows[8] = np.where(idx % 5 == 0, 0.5, 2.0 ** -30)  # wide dynamic range
+    rows[9] = 0.01 * (idx - K / 2) / max(K, 1)
+    rows[9][K // 2] = np.nan if K > 1 else np.inf  # a non-finite row
+    return rows
+
+
+def run_quantize(w_np: np.ndarray, bits: int):
+    report("quantize_pack shape=%s dtype=%s bits=%d" % (w_np.shape, w_np.dtype, bits))
+    packed, scales = dq.quantize_pack(weights_gpu(w_np), bits)
+    torch().cuda.synchronize()
+    return u32(packed), f32_bits(scales)
+
+
+def assert_quantize_parity(w_np: np.ndarray, bits: int):
+    packed, scales = run_quantize(w_np, bits)
+    o_packed, o_scales, o_q = oracle.quantize_pack(w_np, bits)
+    assert np.array_equal(scales, o_scales.view(np.uint32)), "scale bits differ"
+    if not np.array_equal(packed, o_packed):
+        bad = np.argwhere(packed != o_packed)[:5]
+        pytest.fail("packed words differ at %s" % bad.tolist())
+    return o_packed, o_scales, o_q
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_quantize_pack_bitexact_bf16(bits):
+    for i, (N, K) in enumerate(QUANT_SHAPES):
+        w = workload.weights(11, bits * 100 + i, N, K, outlier_frac=0.01 if N * K > 100 else 0.0)
+        assert_quantize_parity(w, bits)
+    t5 = workload.weights(12, bits, 40, 2000, dist="t5")
+    assert_quantize_parity(t5, bits)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_quantize_pack_bitexact_f32(bits):
+    for i, (N, K) in enumerate(QUANT_SHAPES):
+        w = workload.weights(13, bits * 100 + i, N, K, dtype="f32")
+        assert_quantize_parity(w, bits)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_quantize_special_rows(bits):
+    for K in (1, 7, 33, 300):
+        rows = special_rows(K, bits)
+        assert_quantize_parity(rows, bits)
+        bf = workload.bf16_from_f32(rows)
+        assert_quantize_parity(bf, bits)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_unpack_bitexact(bits):
+    for i, (N, K) in enumerate(QUANT_SHAPES):
+        w = workload.weights(14, bits * 100 + i, N, K)
+        o_packed, o_scales, o_q = oracle.quantize_pack(w, bits)
+        q_ref, w_ref = oracle.unpack(o_packed, o_scales, N, K, bits)
+        report("unpack N=%d K=%d bits=%d" % (N, K, bits))
+        P = torch().from_numpy(o_packed.view(np.int32)).cuda()
+        S = torch().from_numpy(o_scales).cuda()
+        q, w_hat = dq.unpack(P, S, K, bits, want_q=True, want_w=True)
+        q_only, _ = dq.unpack(P, None, K, bits, want_q=True, want_w=False)
+        _, w_only = dq.unpack(P, S, K, bits, want_q=False, want_w=True)
+        torch().cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), q_ref)
+        assert np.array_equal(q_only.cpu().numpy(), q_ref)
+        assert np.array_equal(f32_bits(w_hat), w_ref.view(np.uint32))
+        assert np.array_equal(f32_bits(w_only), w_ref.view(np.uint32))
+
+
+def run_matmul(kind: str, x_np, packed_np, scales_np, K: int, bits: int):
+    fn = dq.gemv if kind == "gemv" else dq.gemm
+    report("%s M=%d N=%d K=%d bits=%d" % (kind, x_np.shape[0], packed_np.shape[0], K, bits))
+    P = torch().from_numpy(packed_np.view(np.int32)).cuda()
+    S = torch().from_numpy(scales_np).cuda()
+    y = fn(bf16_gpu(x_np), P, S, K, bits)
+    torch().cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_matmul_parity(kind: str, M: int, N: int, K: int, bits: int, seed: int):
+    w = workload.weights(21, seed, N, K, outlier_frac=0.001)
+    x = workload.activations(21, seed, M, K)
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
+    y = run_matmul(kind, x, o_packed, o_scales, K, bits)
+    ok = within_tolerance(y, y_ref, bound)
+    if not ok.all():
+        m, n = np.argwhere(~ok)[0]
+        pytest.fail("%s M=%d N=%d K=%d b=%d: y[%d,%d]=%r ref %r bound %r (%d bad)" % (
+            kind, M, N, K, bits, m, n, y[m, n], y_ref[m, n], bound[m, n], int((~ok).sum())))
+
+
+GEMV_SHAPES = [(1, 1), (37, 1000), (300, 4096 + 37), (8, 17408)]
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemv_parity(bits):
+    for M in (1, 2, 3, 5, 8, 13, 16):
+        for i, (N, K) in enumerate(GEMV_SHAPES):
+            assert_matmul_parity("gemv", M, N, K, bits, seed=bits * 1000 + M * 10 + i)
+
+
+GEMM_SHAPES = [(1, 64, 64), (7, 129, 100), (128, 128, 1000), (200, 259, 517), (257, 300, 2048)]
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemm_parity(bits):
+    for i, (M, N, K) in enumerate(GEMM_SHAPES):
+        assert_matmul_parity("gemm", M, N, K, bits, seed=bits * 1000 + 500 + i)
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("bits", [2, 6, 9, 10, 15])
+def test_one_hot_is_exact(kind, bits):
+    """x = e_k picks column k of the dequantized matrix: y[k, n] = fl32(s[n] * q[n, k])."""
+    N, K = 70, 16 if kind == "gemv" else 40
+    w = workload.weights(22, bits, N, K)
+    o_packed, o_scales, o_q = oracle.quantize_pack(w, bits)
+    eye = workload.bf16_from_f32(np.eye(K, dtype=np.float32))
+    y = run_matmul(kind, eye, o_packed, o_scales, K, bits)
+    want = (o_scales[None, :] * o_q.T.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_zero_rows_and_nan_scale(kind):
+    bits, N, K = 6, 20, 96
+    w = workload.weights(23, 0, N, K, dtype="f32")
+    w[3] = 0
+    w[7, 5] = np.nan
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    x = workload.activations(23, 0, 4, K)
+    y = run_matmul(kind, x, o_packed, o_scales, K, bits)
+    assert np.all(y[:, 3] == 0)
+    assert np.all(np.isnan(y[:, 7]))
+    y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
+    keep = np.arange(N) != 7
+    assert within_tolerance(y[:, keep], y_ref[:, keep], bound[:, keep]).all()
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_deterministic(kind):
+    bits, M, N, K = 5, 3, 500, 3000
+    w = workload.weights(24, 0, N, K)
+    x = workload.activations(24, 0, M, K)
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    y1 = run_matmul(kind, x, o_packed, o_scales, K, bits)
+    y2 = run_matmul(kind, x, o_packed, o_scales, K, bits)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_quantize_then_matmul_end_to_end():
+    """Whole path on the GPU: W -> dq_quantize_pack -> dq_gemv / dq_gemm, checked
+    against the oracle's own quantization and fp64 product."""
+    bits, M, N, K = 6, 4, 256, 256
+    w = workload.weights(1, 0, N, K, dtype="f32")
+    x = workload.activations(1, 0, M, K)
+    report("end-to-end N=%d K=%d bits=%d" % (N, K, bits))
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    X = bf16_gpu(x)
+    yv = dq.gemv(X, P, S, K, bits)
+    ym = dq.gemm(X, P, S, K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    assert np.array_equal(u32(P), o_packed)
+    y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
+    assert within_tolerance(yv.cpu().numpy(), y_ref, bound).all()
+    assert within_tolerance(ym.cpu().numpy(), y_ref, bound).all()
