@@ -47,7 +47,7 @@ __device__ __forceinline__ int32_t chunk_code_signed(const uint32_t* w, int j)
     if (off + B <= 32) {
         v = w[wi] >> off;
     } else {
-        v = (uint32_t)((((uint64_t)w[wi + 1]) << 32 | w[wi]) >> off);
+        v = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off);  // bits [off, off+32) of {w1:w0}
     }
     return ((int32_t)(v << (32 - B))) >> (32 - B);
 }
@@ -63,9 +63,42 @@ __device__ __forceinline__ uint32_t chunk_code_unsigned(const uint32_t* w, int j
     if (off + B <= 32) {
         v = w[wi] >> off;
     } else {
-        v = (uint32_t)((((uint64_t)w[wi + 1]) << 32 | w[wi]) >> off);
+        v = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off);  // bits [off, off+32) of {w1:w0}
     }
     return v & ((1u << B) - 1u);
+}
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Loads B consecutive words with as few instructions as possible (dwordx4
+// pieces, then x3/x2/x1); global memory only needs dword alignment for these.
+template <int B>
+__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t* w)
+{
+#pragma unroll
+    for (int i = 0; i + 4 <= B; i += 4) {
+        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p + i);
+        w[i] = v.x;
+        w[i + 1] = v.y;
+        w[i + 2] = v.z;
+        w[i + 3] = v.w;
+    }
+    constexpr int r = B & 3;
+    constexpr int o = B - r;
+    if (r == 3) {
+        const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(p + o);
+        w[o] = v.x;
+        w[o + 1] = v.y;
+        w[o + 2] = v.z;
+    } else if (r == 2) {
+        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(p + o);
+        w[o] = v.x;
+        w[o + 1] = v.y;
+    } else if (r == 1) {
+        w[o] = p[o];
+    }
 }
 
 // Loads the B words of chunk c of a packed row.  Words at or beyond row_words
@@ -76,9 +109,7 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t* __restrict__ ro
 {
     const int64_t base = c * B;
     if (base + B <= row_words) {
-        const uint32_t* p = row + base;
-#pragma unroll
-        for (int i = 0; i < B; ++i) w[i] = p[i];
+        load_words<B>(row + base, w);
     } else {
 #pragma unroll
         for (int i = 0; i < B; ++i) w[i] = (base + i < row_words) ? row[base + i] : 0u;

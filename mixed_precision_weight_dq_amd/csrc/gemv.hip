@@ -109,6 +109,309 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// M <= 2: x is staged per K-slice of 64 chunks (2048 codes) in LDS by the whole
+// workgroup (coalesced 16-byte loads); each wave owns kRows rows and each lane
+// one chunk of each of them per slice.  The next slice's packed words and x are
+// loaded into registers before the current slice is computed, so every wave
+// keeps two slices of loads in flight.
+constexpr int kSlice = 64;            // chunks per slice (one per lane)
+constexpr int kXPitch = 40;           // LDS slot per chunk in bf16 units (64 B + 16 B pad)
+
+// E (8 or 4) consecutive x elements of each of the MT rows starting at element
+// k, packed as bf16 pairs; zero past K or for rows m >= M.
+template <int MT, int E>
+__device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int M, int64_t K,
+                                             int64_t k, bool xvec, uint4 (&v)[MT])
+{
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint16_t* src = x + (int64_t)m * K + k;
+        if (m < M && xvec && k + E <= K) {
+            if constexpr (E == 8) {
+                v[m] = *reinterpret_cast<const uint4*>(src);
+            } else {
+                const uint2 d = *reinterpret_cast<const uint2*>(src);
+                v[m] = make_uint4(d.x, d.y, 0u, 0u);
+            }
+        } else {
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i) {
+                const uint32_t lo = (m < M && k + 2 * i < K) ? src[2 * i] : 0u;
+                const uint32_t hi = (m < M && k + 2 * i + 1 < K) ? src[2 * i + 1] : 0u;
+                d[i] = lo | hi << 16;
+            }
+            v[m] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+    }
+}
+
+// LDS slot of x row m is dst + m * kSlice * kXPitch elements.
+template <int MT, int E>
+__device__ __forceinline__ void stage_x_store(uint16_t* dst, const uint4 (&v)[MT])
+{
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if constexpr (E == 8)
+            *reinterpret_cast<uint4*>(dst + m * kSlice * kXPitch) = v[m];
+        else
+            *reinterpret_cast<uint2*>(dst + m * kSlice * kXPitch) = make_uint2(v[m].x, v[m].y);
+    }
+}
+
+template <int B, int kRows>
+__device__ __forceinline__ void stage_w_load(const uint32_t* const (&rowp)[kRows], int64_t c,
+                                             int64_t nchunks, int64_t row_words,
+                                             uint32_t (&w)[kRows][B])
+{
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        if (c < nchunks) {
+            load_chunk_words<B>(rowp[r], c, row_words, w[r]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < B; ++i) w[r][i] = 0;
+        }
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t bf16_pair(float lo, float hi)
+{
+    return __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);  // v_cvt_pk_bf16_f32
+}
+
+// acc + q.lo * x.lo + q.hi * x.hi (v_dot2c_f32_bf16; both products are exact in fp32)
+__device__ __forceinline__ float dot2(bf16x2_t q, uint32_t xpair, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(q, __builtin_bit_cast(bf16x2_t, xpair), acc, false);
+}
+
+__device__ __forceinline__ float sbyte(uint32_t w, int j) { return (float)(int8_t)(w >> (8 * j)); }
+
+// log2 of the factor by which chunk_dot<B> scales its sums (codes are
+// converted from the top bits of a byte, i.e. multiplied by 2^(8-B)).
+template <int B>
+__host__ __device__ constexpr int chunk_dot_shift() { return B == 2 ? 6 : (B == 4 ? 4 : 0); }
+
+// acc[m] += 2^shift * sum_j x[m][j] q[j] over one chunk of 32 codes.  xw[m][p]
+// is the bf16 pair (x[2p], x[2p+1]); w the chunk's B raw words.  Codes are made
+// exact bf16 pairs (|q| <= 256, or 2^(8-B) q for B = 2, 4) and multiplied with
+// v_dot2c_f32_bf16.  Widths 2, 4 and 8 convert whole bytes (signed byte select)
+// after one XOR flips every code's top bit (offset binary -> two's complement).
+template <int B, int MT>
+__device__ __forceinline__ void chunk_dot(const uint32_t (&w)[B], const uint32_t (&xw)[MT][16],
+                                          float (&acc)[MT])
+{
+    static_assert(B <= 9, "bf16 holds the codes exactly only up to 9 bits");
+    if constexpr (B == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = w[i] ^ 0x80808080u;
+            const bf16x2_t p0 = bf16_pair(sbyte(v, 0), sbyte(v, 1));
+            const bf16x2_t p1 = bf16_pair(sbyte(v, 2), sbyte(v, 3));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                acc[m] = dot2(p0, xw[m][2 * i], acc[m]);
+                acc[m] = dot2(p1, xw[m][2 * i + 1], acc[m]);
+            }
+        }
+    } else if constexpr (B == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = w[i] ^ 0x88888888u;
+            const uint32_t lo = (v << 4) & 0xf0f0f0f0u;  // codes 8i+2j, times 16
+            const uint32_t hi = v & 0xf0f0f0f0u;         // codes 8i+2j+1, times 16
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2_t p = bf16_pair(sbyte(lo, j), sbyte(hi, j));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = dot2(p, xw[m][4 * i + j], acc[m]);
+            }
+        }
+    } else if constexpr (B == 2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t v = w[i] ^ 0xaaaaaaaau;
+            const uint32_t t0 = (v << 6) & 0xc0c0c0c0u;  // code 16i+4j+0 at the top of byte j
+            const uint32_t t1 = (v << 4) & 0xc0c0c0c0u;
+            const uint32_t t2 = (v << 2) & 0xc0c0c0c0u;
+            const uint32_t t3 = v & 0xc0c0c0c0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2_t p0 = bf16_pair(sbyte(t0, j), sbyte(t1, j));
+                const bf16x2_t p1 = bf16_pair(sbyte(t2, j), sbyte(t3, j));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    acc[m] = dot2(p0, xw[m][8 * i + 2 * j], acc[m]);
+                    acc[m] = dot2(p1, xw[m][8 * i + 2 * j + 1], acc[m]);
+                }
+            }
+        }
+    } else {
+        uint32_t v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) v[i] = w[i] ^ code_msb_mask<B>(i);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const bf16x2_t q = bf16_pair((float)chunk_code_signed<B>(v, 2 * p),
+                                         (float)chunk_code_signed<B>(v, 2 * p + 1));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = dot2(q, xw[m][p], acc[m]);
+        }
+    }
+}
+
+// Same contract for 10 <= B <= 15 (codes too wide for bf16): fp32 FMAs on x
+// widened exactly from its bf16 pairs.
+template <int B, int MT>
+__device__ __forceinline__ void chunk_fma(const uint32_t (&w)[B], const uint32_t (&xw)[MT][16],
+                                          float (&acc)[MT])
+{
+    uint32_t v[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) v[i] = w[i] ^ code_msb_mask<B>(i);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const float q0 = (float)chunk_code_signed<B>(v, 2 * p);
+        const float q1 = (float)chunk_code_signed<B>(v, 2 * p + 1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            acc[m] = fmaf(__uint_as_float(xw[m][p] << 16), q0, acc[m]);
+            acc[m] = fmaf(__uint_as_float(xw[m][p] & 0xffff0000u), q1, acc[m]);
+        }
+    }
+}
+
+template <int B, int MT, int kRows, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y)
+{
+    constexpr int kThreads = kWaves * kWave;
+    constexpr int kXPerThread = kSlice * kChunk / kThreads;  // x elements staged per thread
+    static_assert(kXPerThread == 8 || kXPerThread == 4, "staging is 16 or 8 bytes per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][kSlice * kXPitch];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t n0 = ((int64_t)blockIdx.x * kWaves + wave) * kRows;
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int64_t nslices = ceil_div(nchunks, kSlice);
+    const bool xvec = (K & 7) == 0;
+
+    // rows of this wave (clamped for loads; stores are guarded)
+    const uint32_t* rowp_[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        rowp_[r] = packed + n * row_words;
+    }
+    const uint32_t* const(&rowp)[kRows] = rowp_;
+
+    // x staging: thread t moves kXPerThread elements of each x row per slice
+    const int xc = tid * kXPerThread / kChunk;                 // chunk within the slice
+    const int xp = (tid * kXPerThread) % kChunk;               // element offset within the chunk
+
+    float acc[kRows][MT];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+    uint32_t wcur[kRows][B], wnxt[kRows][B];
+    uint4 xnxt[MT];
+    stage_x_load<MT, kXPerThread>(x, M, K, (0 * kSlice + xc) * kChunk + xp, xvec, xnxt);
+    stage_x_store<MT, kXPerThread>(&xs[0][0][xc * kXPitch + xp], xnxt);
+    stage_w_load<B, kRows>(rowp, 0 * kSlice + lane, nchunks, row_words, wcur);
+
+    for (int64_t s = 0; s < nslices; ++s) {
+        const bool more = s + 1 < nslices;
+        if (more) {
+            stage_x_load<MT, kXPerThread>(x, M, K, ((s + 1) * kSlice + xc) * kChunk + xp, xvec, xnxt);
+            stage_w_load<B, kRows>(rowp, (s + 1) * kSlice + lane, nchunks, row_words, wnxt);
+        }
+        __syncthreads();
+        const int buf = (int)(s & 1);
+        if (s * kSlice + lane < nchunks) {
+            uint32_t xw[MT][16];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint4* src = reinterpret_cast<const uint4*>(&xs[buf][m][lane * kXPitch]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 d = src[i];
+                    xw[m][4 * i + 0] = d.x;
+                    xw[m][4 * i + 1] = d.y;
+                    xw[m][4 * i + 2] = d.z;
+                    xw[m][4 * i + 3] = d.w;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                if constexpr (B <= 9)
+                    chunk_dot<B, MT>(wcur[r], xw, acc[r]);
+                else
+                    chunk_fma<B, MT>(wcur[r], xw, acc[r]);
+            }
+        }
+        if (more) {
+            stage_x_store<MT, kXPerThread>(&xs[buf ^ 1][0][xc * kXPitch + xp], xnxt);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+#pragma unroll
+                for (int i = 0; i < B; ++i) wcur[r][i] = wnxt[r][i];
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
+    if (lane == 0) {
+        constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int64_t n = n0 + r;
+            if (n < N) {
+                const float s = scales[n];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (m < M) y[(int64_t)m * N + n] = s * (acc[r][m] * kUnscale);
+            }
+        }
+    }
+}
+
+#ifndef DQ_GEMV_ROWS_NARROW
+#define DQ_GEMV_ROWS_NARROW 1
+#endif
+#ifndef DQ_GEMV_ROWS_WIDE
+#define DQ_GEMV_ROWS_WIDE 1
+#endif
+#ifndef DQ_GEMV_WAVES
+#define DQ_GEMV_WAVES 8
+#endif
+
+template <int B, int MT>
+hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
+                           const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+{
+    constexpr int kRows = B <= 8 ? DQ_GEMV_ROWS_NARROW : DQ_GEMV_ROWS_WIDE;
+    constexpr int kWaves = DQ_GEMV_WAVES;
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t rows_per_block = kWaves * kRows;
+    const int64_t blocks = ceil_div(N, rows_per_block);
+    gemv_lds_kernel<B, MT, kRows, kWaves><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
+        x, (int)M, packed, scales, N, K, rw, y);
+    return hipGetLastError();
+}
+
 template <int B, int MT>
 hipError_t launch_gemv_bm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                           int64_t N, int64_t K, float* y, hipStream_t stream)
@@ -126,8 +429,8 @@ template <int B>
 hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                          int64_t N, int64_t K, float* y, hipStream_t stream)
 {
-    if (M <= 1) return launch_gemv_bm<B, 1>(x, M, packed, scales, N, K, y, stream);
-    if (M <= 2) return launch_gemv_bm<B, 2>(x, M, packed, scales, N, K, y, stream);
+    if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, stream);
+    if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, stream);
     if (M <= 4) return launch_gemv_bm<B, 4>(x, M, packed, scales, N, K, y, stream);
     if (M <= 8) return launch_gemv_bm<B, 8>(x, M, packed, scales, N, K, y, stream);
     return launch_gemv_bm<B, 16>(x, M, packed, scales, N, K, y, stream);
