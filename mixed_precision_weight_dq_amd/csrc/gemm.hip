@@ -15,6 +15,8 @@
 // stages a 128 x 64 slice of x and the matching 128 x 64 slice of expanded
 // codes in LDS (k contiguous for both), and each wave issues
 // v_mfma_f32_16x16x32_bf16 over its 64 x 64 sub-tile.
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm_tiles.hpp"
 #include "launch.hpp"
@@ -161,99 +163,106 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel (K a multiple of 64).  256 threads = 4 waves in a 2 x 2 grid; a
-// wave owns a (32*kMT) x (32*kNT) block of y as kMT x kNT tiles of
-// v_mfma_f32_32x32x16_bf16, so the workgroup tile is (64*kMT) x (64*kNT).
+// Main kernel (K a multiple of 64).  256 threads = 4 waves side by side along
+// N: wave w owns columns [w*32*kNT, (w+1)*32*kNT) of the workgroup tile and all
+// 32*kMT of its rows, as kMT x kNT tiles of v_mfma_f32_32x32x16_bf16.  No two
+// waves expand the same codes.
 //
 // K order inside a 64-wide step: MFMA substep t (0..3) multiplies, for lane
 // half h (lanes 32h .. 32h+31), the 8 elements k = 32h + 8t + e.  Any fixed
 // permutation of k is fine as long as x and the codes use the same one; this
-// one lets lane (c, h) take all of its B operands from chunk h (32 codes = B
-// whole words) of its own weight row, so codes go from HBM to registers to the
-// matrix cores with no LDS round trip.
+// one lets lane (c, h) take all of its operands for one weight row from chunk
+// h (32 codes = B whole words) of that row, so codes go from HBM to registers
+// to the matrix cores with no LDS round trip.
 //
-// x goes through LDS: each step's tile (rows x 64 bf16, 128 B per row) is
-// copied with global_load_lds_dwordx4 into a double buffer; 16-byte piece p of
-// row r is stored at slot p ^ (r & 7) so the fragment reads are bank-conflict
-// free.  Rows past M are clamped to M-1 and weight rows past N to N-1 (their
-// outputs are never stored).
+// x goes through LDS: each step's tile (rows x 64 bf16 = 128 B per row) is
+// loaded with coalesced 16-byte buffer loads into registers and written to a
+// double buffer after the step's MFMAs are issued; 16-byte piece p of row r
+// sits at slot p ^ ((r >> 1) & 7), which spreads the 16 rows that one
+// ds_read_b128 pass touches over all 64 banks.  Loads for step ks+1 (x and
+// codes) are issued right after the barrier that opens step ks; kOcc
+// workgroups share a CU so one's MFMAs cover another's waits.
+// Rows past M are clamped to M-1 and weight rows past N to N-1; their outputs
+// are never stored.
+#ifndef DQ_GEMM_MT
+#define DQ_GEMM_MT 4
+#endif
+#ifndef DQ_GEMM_NT
+#define DQ_GEMM_NT 2
+#endif
+#ifndef DQ_GEMM_OCC
+#define DQ_GEMM_OCC 2
+#endif
+
 template <int kMT, int kNT>
-struct BigTile {
-    static constexpr int BM = 64 * kMT;
-    static constexpr int BN = 64 * kNT;
+struct MfmaTile {
+    static constexpr int BM = 32 * kMT;
+    static constexpr int BN = 4 * 32 * kNT;
     static constexpr int BK = 64;
-    static constexpr int kPiecesPerBuf = BM * 8;  // 16-byte pieces of one x tile
+    static constexpr int kStages = 2;
+    static constexpr int kPieces = BM * 8;  // 16-byte pieces of one x tile
 };
 
-template <int B, int kMT, int kNT>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(
+__device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
+
+template <int B, int kMT, int kNT, int kOcc>
+__global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
     float* __restrict__ y)
 {
-    using T = BigTile<kMT, kNT>;
+    using T = MfmaTile<kMT, kNT>;
     constexpr bool kSplit = B >= 10;
-    __shared__ __attribute__((aligned(16))) uint4 As[2][T::kPiecesPerBuf];
+    constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
+    __shared__ __attribute__((aligned(16))) uint4 As[T::kStages][T::kPieces];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
     const int c = lane & 31;
     const int h = lane >> 5;
 
-    // tile order: consecutive workgroups go to different XCDs (round robin over 8);
-    // give each XCD a contiguous range of column tiles so the weight rows it
-    // streams stay in its own L2.
+    // tile order: consecutive workgroups go to different XCDs (round robin over
+    // 8); give each XCD a contiguous range of tiles, column tiles outermost, so
+    // the weight rows an XCD streams stay in its own L2.
     const int64_t ntm = ceil_div(M, T::BM);
     const int64_t ntn = ceil_div(N, T::BN);
     const int64_t tiles = ntm * ntn;
     int64_t L = blockIdx.x;
     if ((tiles & 7) == 0) L = (L & 7) * (tiles >> 3) + (L >> 3);
-    const int64_t tm = L % ntm;
-    const int64_t tn = L / ntm;
-    const int64_t m0 = tm * T::BM;
-    const int64_t n0 = tn * T::BN;
+    const int64_t m0 = (L % ntm) * T::BM;
+    const int64_t n0 = (L / ntm) * T::BN;
     const int64_t nk = K / T::BK;
 
-    // x tile copy: wave w moves rows [w*BM/4, (w+1)*BM/4); one instruction moves
-    // 8 rows x 8 pieces; lane -> (row r = 8i + lane/8, slot lane&7) <- piece slot^(r&7).
-    // Buffer loads straight into LDS; the per-lane byte offsets are loop invariant
-    // and the step advances the scalar offset.
-    constexpr int kRowsPerWave = T::BM / 4;
-    constexpr int kCopyInstr = kRowsPerWave / 8;
+    // x copy: thread t moves 16-byte piece p = t & 7 of rows r = 32 i + t / 8
+    // (i < BM / 32), global -> registers during step ks -> LDS slot
+    // 8 r + (p ^ xswz(r)) of the other stage once the step's MFMAs are issued.
     const int64_t mrows = M - m0 < T::BM ? M - m0 : T::BM;
-    const BufRef xbuf{x + m0 * K, (uint32_t)(mrows * K * 2)};
+    const BufRef xbuf = uniform_buf(x + m0 * K, (uint32_t)(mrows * K * 2));
     uint32_t xoff[kCopyInstr];
+    int xslot[kCopyInstr];
 #pragma unroll
     for (int i = 0; i < kCopyInstr; ++i) {
-        const int r = wave * kRowsPerWave + i * 8 + (lane >> 3);
+        const int r = i * 32 + (tid >> 3);
+        const int p = tid & 7;
         const int64_t rl = r < mrows ? r : mrows - 1;
-        xoff[i] = (uint32_t)(rl * K * 2 + 16 * ((lane & 7) ^ (r & 7)));
+        xoff[i] = (uint32_t)(rl * K * 2 + 16 * p);
+        xslot[i] = r * 8 + (p ^ xswz(r));
     }
-    auto copy_x = [&](int64_t ks, int buf) {
-#pragma unroll
-        for (int i = 0; i < kCopyInstr; ++i) {
-            buf_load_lds16(xbuf, &As[buf][(wave * kRowsPerWave + i * 8) * 8], xoff[i],
-                           (uint32_t)(ks * T::BK * 2));
-        }
-    };
-
-    // weight rows of this lane (one per n tile): chunk h of step ks starts at
-    // byte (ks * 2 + h) * 4B of the row
+    // weight rows of this lane: chunk h of step ks starts at byte (2 ks + h) * 4B
     const int64_t nrows = N - n0 < T::BN ? N - n0 : T::BN;
-    const BufRef wbuf{packed + n0 * row_words, (uint32_t)(nrows * row_words * 4)};
+    const BufRef wbuf = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
     uint32_t woff[kNT];
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-        const int64_t nl = wn * 32 * kNT + j * 32 + c;
+        const int64_t nl = wave * 32 * kNT + j * 32 + c;
         woff[j] = (uint32_t)((nl < nrows ? nl : nrows - 1) * row_words * 4 + h * B * 4);
     }
-    auto load_w = [&](int64_t ks, uint32_t (&w)[kNT][B]) {
+    // LDS slot of this lane's x fragment for tile i, substep t: row r = 32i + c,
+    // and xswz(32i + c) = xswz(c), so the slot is 256 i + a constant per t
+    int abase[4];
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) buf_load_words<B>(wbuf, woff[j], (uint32_t)(ks * 8 * B), w[j]);
-    };
+    for (int t = 0; t < 4; ++t) abase[t] = c * 8 + ((4 * h + t) ^ xswz(c));
 
     f32x16_t acc[kMT][kNT];
 #pragma unroll
@@ -263,85 +272,102 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // LDS slot of x fragment (row r of this wave's tile i, piece p)
-    int arow_lds[kMT];
+    // codes, ping-pong by step parity: stage st holds step ks (loaded during
+    // step ks-1) and is expanded to MFMA operands at the top of step ks while
+    // step ks+1 loads into stage st^1
+    uint32_t w[2][kNT][B];
+    uint4 xr[kCopyInstr];
+    auto load_x = [&](int64_t ks) {
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) arow_lds[i] = wm * 32 * kMT + i * 32 + c;
-
-    uint32_t wcur[kNT][B];
-    copy_x(0, 0);
-    load_w(0, wcur);
-    __builtin_amdgcn_s_waitcnt(0);  // all of step 0 in LDS / registers
-    __syncthreads();
-
-    for (int64_t ks = 0; ks < nk; ++ks) {
-        const int cur = (int)(ks & 1);
-        // x fragments of this step, all four substeps
-        bf16x8_t a[4][kMT];
+        for (int i = 0; i < kCopyInstr; ++i) {
+            const u32x4v_t v = buf_load_b128(xbuf, xoff[i], (uint32_t)(ks * T::BK * 2));
+            xr[i] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    auto store_x = [&](auto S) {
+        constexpr int st = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < kCopyInstr; ++i) As[st][xslot[i]] = xr[i];
+    };
+    auto load_w = [&](auto S, int64_t ks) {
+        constexpr int st = decltype(S)::value;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) buf_load_words<B>(wbuf, woff[j], (uint32_t)(ks * 8 * B), w[st][j]);
+    };
+    auto step = [&](auto S, int64_t ks) {  // MFMAs of step ks from stage S
+        constexpr int st = decltype(S)::value;
+        __syncthreads();  // step ks in LDS for every wave; stage st^1 free again
+        bf16x8_t bh[4][kNT], bl[4][kNT];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) {
-                const int r = arow_lds[i];
-                a[t][i] = __builtin_bit_cast(bf16x8_t, As[cur][r * 8 + ((4 * h + t) ^ (r & 7))]);
-            }
-        const bool more = ks + 1 < nk;
-        uint32_t wnxt[kNT][B];
-        if (more) {
-            copy_x(ks + 1, cur ^ 1);
-            load_w(ks + 1, wnxt);
-        }
+            for (int j = 0; j < kNT; ++j) expand8<B>(w[st][j], t, bh[t][j], bl[t][j]);
+        // step ks+1 (past the last step these read beyond the buffers' ends,
+        // which buffer loads return as zeros; the data is never used)
+        load_w(std::integral_constant<int, st ^ 1>{}, ks + 1);
+        load_x(ks + 1);
+        // keep the loads here, a whole step ahead of their use (the scheduler
+        // would otherwise sink them next to the LDS stores to save registers)
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t a[2][kMT];  // x fragments of substep t (and t+1, read ahead)
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) a[0][i] = __builtin_bit_cast(bf16x8_t, As[st][abase[0] + 256 * i]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            if (t < 3) {
 #pragma unroll
-            for (int j = 0; j < kNT; ++j) {
-                bf16x8_t bh, bl;
-                expand8<B>(wcur[j], t, bh, bl);
-#pragma unroll
-                for (int i = 0; i < kMT; ++i) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][i], bh, acc[i][j], 0, 0, 0);
-                    if constexpr (kSplit)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][i], bl, acc[i][j], 0, 0, 0);
-                }
+                for (int i = 0; i < kMT; ++i)
+                    a[(t + 1) & 1][i] = __builtin_bit_cast(bf16x8_t, As[st][abase[t + 1] + 256 * i]);
             }
-        }
-        if (more) {
 #pragma unroll
-            for (int j = 0; j < kNT; ++j)
+            for (int i = 0; i < kMT; ++i)
 #pragma unroll
-                for (int e = 0; e < B; ++e) wcur[j][e] = wnxt[j][e];
+                for (int j = 0; j < kNT; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[t][j], acc[i][j], 0, 0, 0);
+                    if constexpr (kSplit)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bl[t][j], acc[i][j], 0, 0, 0);
+                }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        store_x(std::integral_constant<int, st ^ 1>{});
+    };
+
+    load_x(0);
+    load_w(std::integral_constant<int, 0>{}, 0);
+    store_x(std::integral_constant<int, 0>{});
+    int64_t ks = 0;
+    for (; ks + 2 <= nk; ks += 2) {
+        step(std::integral_constant<int, 0>{}, ks);
+        step(std::integral_constant<int, 1>{}, ks + 1);
     }
+    if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
 
     // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-        const int64_t n = n0 + wn * 32 * kNT + j * 32 + c;
+        const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
         const float s = scales[n];
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 32 * kMT + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
             }
         }
     }
 }
 
-template <int B, int kMT, int kNT>
-hipError_t launch_gemm_big(const uint16_t* x, int64_t M, const uint32_t* packed,
-                           const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+template <int B, int kMT, int kNT, int kOcc>
+hipError_t launch_gemm_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
+                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
 {
-    using T = BigTile<kMT, kNT>;
+    using T = MfmaTile<kMT, kNT>;
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, T::BN) * ceil_div(M, T::BM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    gemm_big_kernel<B, kMT, kNT><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
+    gemm_mfma_kernel<B, kMT, kNT, kOcc><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
         x, M, packed, scales, N, K, rw, y);
     return hipGetLastError();
 }
@@ -351,10 +377,15 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
                          int64_t N, int64_t K, float* y, hipStream_t stream)
 {
     if (K % 64 == 0) {
-        // 256 x 256 tiles when they fill the 256 CUs, else 128 x 128
-        if (ceil_div(M, 256) * ceil_div(N, 256) >= 240)
-            return launch_gemm_big<B, 4, 4>(x, M, packed, scales, N, K, y, stream);
-        return launch_gemm_big<B, 2, 2>(x, M, packed, scales, N, K, y, stream);
+        // 128 x 256 tiles (codes up to 8 bits: wider ones need more registers
+        // than two workgroups per CU leave), when they fill the 256 CUs twice
+        // over; else 128 x 128
+        if constexpr (B <= 8) {
+            if (ceil_div(M, 128) * ceil_div(N, 256) >= 400)
+                return launch_gemm_mfma<B, DQ_GEMM_MT, DQ_GEMM_NT, DQ_GEMM_OCC>(x, M, packed, scales,
+                                                                               N, K, y, stream);
+        }
+        return launch_gemm_mfma<B, 4, 1, 2>(x, M, packed, scales, N, K, y, stream);
     }
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, kBN) * ceil_div(M, kBM);

@@ -93,6 +93,17 @@ struct BufRef {
     uint32_t bytes;
 };
 
+// A BufRef whose fields are provably wave-uniform (scalar registers), so the
+// descriptor is built once with scalar ops and hoisted out of loops.
+__device__ __forceinline__ BufRef uniform_buf(const void* base, uint32_t bytes)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return BufRef{reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                  (uint32_t)__builtin_amdgcn_readfirstlane(bytes)};
+}
+
 // B consecutive words at byte offset voff + soff of a buffer, in as few
 // buffer loads as possible (dwordx4 pieces, then x3/x2/x1).
 template <int B>
@@ -122,6 +133,11 @@ __device__ __forceinline__ void buf_load_words(BufRef buf, uint32_t voff, uint32
     } else if constexpr (r == 1) {
         w[o] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * o, soff, 0);
     }
+}
+
+__device__ __forceinline__ u32x4v_t buf_load_b128(BufRef buf, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(buf.base, buf.bytes), voff, soff, 0);
 }
 
 // 16 bytes per lane from byte offset voff + soff of a buffer straight into LDS
