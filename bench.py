@@ -143,21 +143,31 @@ def main():
             stream.cuda_stream), "dq_unpack")))
     for b in W4:
         ops.append(("quantize_pack_8192", b, lambda b=b: dq.quantize_pack(W4[b], b, P4[b], S4[b])))
-    for b in W4:
-        ops.append(("gemm_2048", b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
+    for b in W4:  # one event group per GEMM (each runs for hundreds of microseconds)
+        ops.append(("gemm_2048_b%d" % b, b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
     for b in W2:
         ops.append(("gemv_m1", b, lambda b=b: dq.gemv(X1, P2[b], S2[b], DECODE["K"], b, Y1[b])))
 
-    nops = len(ops)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
+    # one HIP event at every group boundary (events between every launch would
+    # add their own dispatch gaps to the tiny GEMV launches)
+    kinds = []
+    for kind, _, _ in ops:
+        if not kinds or kinds[-1] != kind:
+            kinds.append(kind)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)]
+          for _ in range(args.steps)]
 
     def step(events=None):
+        g = 0
         if events is not None:
             events[0].record(stream)
-        for i, (_, _, fn) in enumerate(ops):
+        for i, (kind, _, fn) in enumerate(ops):
             fn()
-            if events is not None:
-                events[i + 1].record(stream)
+            last = i + 1 == len(ops) or ops[i + 1][0] != kind
+            if last:
+                g += 1
+                if events is not None:
+                    events[g].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -169,30 +179,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-op durations (ms), averaged over steps
-    dur = np.zeros((args.steps, nops))
-    for s in range(args.steps):
-        for i in range(nops):
-            dur[s, i] = ev[s][i].elapsed_time(ev[s][i + 1])
-    avg = dur.mean(axis=0)
-
-    def pick(kind):
-        return [(ops[i][1], avg[i]) for i in range(nops) if ops[i][0] == kind]
+    # per-group time (ms) averaged over steps, split evenly over the group's launches
+    group_ms = {kind: float(np.mean([ev[s][g].elapsed_time(ev[s][g + 1]) for s in range(args.steps)]))
+                for g, kind in enumerate(kinds)}
+    count = {kind: sum(1 for k, _, _ in ops if k == kind) for kind in kinds}
 
     Nd, Kd = DECODE["N"], DECODE["K"]
     Np, Kp, Mp = PREFILL["N"], PREFILL["K"], PREFILL["M"]
-    gemv = pick("gemv_m1")
-    gemv_bytes = {b: Nd * Kd * b // 8 for b, _ in gemv}
-    gemv_ms = sum(t for _, t in gemv)
+    gemv_bytes = {b: Nd * Kd * b // 8 for b in DECODE["bits"]}
+    gemv_ms = group_ms["gemv_m1"]
     value = sum(gemv_bytes.values()) / (gemv_ms * 1e-3) / 1e9
-    gemm = pick("gemm_2048")
     gemm_flop = 2.0 * Mp * Np * Kp
-    gemm_tflops = {b: gemm_flop / (t * 1e-3) / 1e12 for b, t in gemm}
-    gemm_avg_ms = float(np.mean([t for _, t in gemm]))
-    gemm_le9 = [t for b, t in gemm if b <= 9]
+    gemm_ms = {b: group_ms["gemm_2048_b%d" % b] for b in PREFILL["bits"]}
+    gemm_tflops = {b: gemm_flop / (t * 1e-3) / 1e12 for b, t in gemm_ms.items()}
+    gemm_le9_ms = float(np.mean([t for b, t in gemm_ms.items() if b <= 9]))
+    gemm_le9 = gemm_flop / (gemm_le9_ms * 1e-3) / 1e12
 
-    def qp_gbs(kind, N, K):
-        return {str(b): round((N * K * 2 + N * K * b // 8) / (t * 1e-3) / 1e9, 1) for b, t in pick(kind)}
+    def gbs(kind, bits, N, K, read_bits, write_bits):
+        """(read + write) bytes of the group's launches over the group time"""
+        total = sum(N * K * (read_bits(b) + write_bits(b)) / 8 for b in bits)
+        return round(total / (group_ms[kind] * 1e-3) / 1e9, 1)
 
     traffic = recorded_traffic()
     out = {
@@ -216,34 +222,39 @@ def main():
                      "mfma_dtype": "bf16", "accumulate": "f32"},
             "step": "quantize+pack(5 decode) -> unpack(5) -> quantize+pack(4 prefill) -> "
                     "gemm(4) -> gemv(5)",
+            "timing": "HIP events at group boundaries on the launch stream; per-launch "
+                      "figures are group time / launches (inter-launch gaps included)",
         },
         "roofline": {
-            "kernel": "dq_gemv M=1 (five launches, b=4..8)",
+            "kernel": "dq_gemv M=1 N=K=4096 (five launches, b=4..8, back to back)",
             "bound": "hbm",
             "achieved": round(value, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "per_launch_us": round(gemv_ms / count["gemv_m1"] * 1e3, 3),
         },
         "roofline_gemm": {
-            "kernel": "dq_gemm M=2048 N=K=8192",
+            "kernel": "dq_gemm M=2048 N=K=8192, b=5,6,8 (b=12 listed in per_bits)",
             "bound": "mfma",
-            "achieved": round(gemm_flop / (float(np.mean(gemm_le9)) * 1e-3) / 1e12, 2),
+            "achieved": round(gemm_le9, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(gemm_flop / (float(np.mean(gemm_le9)) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "over": "b <= 9 launches (b >= 10 issues twice the MFMA work by design)",
+            "frac": round(gemm_le9 / MFMA_BF16_PEAK_TFLOPS, 4),
             "per_bits": {str(b): round(v, 1) for b, v in gemm_tflops.items()},
+            "note": "algorithmic 2*M*N*K flops; b >= 10 issues twice the MFMA work (exact hi/lo "
+                    "bf16 split), so its ceiling is half the peak",
+            "per_launch_us": round(gemm_le9_ms * 1e3, 2),
         },
-        "components_ms": {
-            kind: {str(b): round(float(t), 5) for b, t in pick(kind)}
-            for kind in ("quantize_pack_4096", "unpack_4096", "quantize_pack_8192", "gemm_2048", "gemv_m1")
+        "groups_ms": {kind: round(group_ms[kind], 5) for kind in kinds},
+        "throughput_gbs": {
+            "quantize_pack_4096": gbs("quantize_pack_4096", DECODE["bits"], Nd, Kd,
+                                      lambda b: 16, lambda b: b),
+            "unpack_4096": gbs("unpack_4096", DECODE["bits"], Nd, Kd, lambda b: b, lambda b: 32),
+            "quantize_pack_8192": gbs("quantize_pack_8192", PREFILL["bits"], Np, Kp,
+                                      lambda b: 16, lambda b: b),
         },
-        "gemv_gbs_per_bits": {str(b): round(gemv_bytes[b] / (t * 1e-3) / 1e9, 1) for b, t in gemv},
-        "quantize_pack_gbs": {"4096": qp_gbs("quantize_pack_4096", Nd, Kd),
-                              "8192": qp_gbs("quantize_pack_8192", Np, Kp)},
-        "gemm_avg_ms": round(gemm_avg_ms, 4),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -1,0 +1,230 @@
+"""Parity at the full sizes of the five synthetic workloads, through the same
+calls (and so the same kernels and launch configurations) the benchmark
+times.  Where the oracle can cover every output it does; at the largest sizes
+it checks sampled rows (quantize / pack are per-row, so a row is checked whole)
+and sampled (m, n) outputs of the products.
+
+Bars as in the small-shape parity tests: bit-exact packed words and scales,
+|y - y_ref| <= 1e-4 * sum_k |x * w_hat| with y_ref in fp64."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import mixed_precision_weight_dq_amd as dq
+import oracle
+import workload
+from gpu_util import bf16_gpu, f32_bits, report, torch, u32, weights_gpu
+from pins import within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(N, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(N, size=min(count, N), replace=False)
+    return np.unique(np.concatenate([rows, [0, N - 1]]))
+
+
+def check_rows(w_np, rows, packed_gpu, scales_gpu, bits):
+    """The oracle on the given rows must reproduce the GPU's packed rows and scales."""
+    o_packed, o_scales, _ = oracle.quantize_pack(np.ascontiguousarray(w_np[rows]), bits)
+    idx = torch().from_numpy(rows).cuda()
+    assert np.array_equal(u32(packed_gpu.index_select(0, idx)), o_packed), "packed rows differ"
+    assert np.array_equal(f32_bits(scales_gpu.index_select(0, idx)), o_scales.view(np.uint32))
+    return o_packed, o_scales
+
+
+def check_products(kind, x_np, y_gpu, o_packed_rows, o_scales_rows, rows, K, bits, max_pairs=None,
+                   seed=0):
+    """y[:, rows] against the oracle (all m, or max_pairs sampled (m, n))."""
+    M = x_np.shape[0]
+    y = y_gpu.cpu().numpy()
+    if max_pairs is None:
+        y_ref, bound = oracle.matmul(x_np, o_packed_rows, o_scales_rows, len(rows), K, bits)
+        got = y[:, rows]
+        ok = within_tolerance(got, y_ref, bound)
+        bad = np.argwhere(~ok)
+        assert ok.all(), "%s b=%d: %d outputs out of tolerance, first (m, row) %s: %r vs %r" % (
+            kind, bits, len(bad), bad[0], got[tuple(bad[0])], y_ref[tuple(bad[0])])
+    else:
+        rng = np.random.default_rng(seed)
+        ms = rng.integers(0, M, size=max_pairs)
+        js = rng.integers(0, len(rows), size=max_pairs)
+        y_ref, bound = oracle.matmul_pairs(x_np, o_packed_rows, o_scales_rows, len(rows), K, bits,
+                                           ms, js)
+        got = y[ms, rows[js]]
+        ok = within_tolerance(got, y_ref, bound)
+        assert ok.all(), "%s b=%d: %d sampled outputs out of tolerance" % (kind, bits, int((~ok).sum()))
+
+
+def test_workload1_single_matrix_fp32():
+    """256 x 256 fp32 W, b = 6, x 1 x 256: every output checked."""
+    wl = workload.WORKLOADS[1]
+    w = workload.workload_weights(wl, 0)
+    x = workload.activations(1, 0, 1, wl.K)
+    bits = 6
+    report("workload 1")
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    q, w_hat = dq.unpack(P, S, wl.K, bits, want_q=True, want_w=True)
+    X = bf16_gpu(x)
+    yv = dq.gemv(X, P, S, wl.K, bits)
+    ym = dq.gemm(X, P, S, wl.K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, o_q = oracle.quantize_pack(w, bits)
+    assert np.array_equal(u32(P), o_packed)
+    assert np.array_equal(f32_bits(S), o_scales.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), o_q)
+    _, o_w = oracle.unpack(o_packed, o_scales, wl.N, wl.K, bits)
+    assert np.array_equal(f32_bits(w_hat), o_w.view(np.uint32))
+    y_ref, bound = oracle.matmul(x, o_packed, o_scales, wl.N, wl.K, bits)
+    assert within_tolerance(yv.cpu().numpy(), y_ref, bound).all()
+    assert within_tolerance(ym.cpu().numpy(), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("bits", [4, 5, 6, 7, 8])
+def test_workload2_decode_gemv(bits):
+    """4096 x 4096 bf16 with 0.1% x20 outliers, M = 1: every packed word and output."""
+    wl = workload.WORKLOADS[2]
+    i = list(wl.bits).index(bits)
+    w = workload.workload_weights(wl, i)
+    x = workload.activations(2, 0, 1, wl.K)
+    report("workload 2 b=%d" % bits)
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    y = dq.gemv(bf16_gpu(x), P, S, wl.K, bits)
+    q, _ = dq.unpack(P, None, wl.K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, o_q = oracle.quantize_pack(w, bits)
+    assert np.array_equal(u32(P), o_packed)
+    assert np.array_equal(f32_bits(S), o_scales.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), o_q)
+    rows = np.arange(wl.N)
+    check_products("gemv", x, y, o_packed, o_scales, rows, wl.K, bits)
+
+
+def test_workload3_layer_stack():
+    """The 448-matrix stack (per layer 4 x 5120x5120, 2 x 17408x5120, 5120x17408) at
+    the knee recipe; GEMV at M = 1 and M = 8 over every matrix in order.  Weights
+    are drawn on the GPU (seeded) to keep the 47.6 GB of bf16 out of host memory;
+    the oracle checks sampled rows of every matrix, copied back bit for bit."""
+    t = torch()
+    shapes, recipe = workload.stack_shapes(), workload.stack_bits()
+    gen = t.Generator(device="cuda")
+    xs = {}
+    for idx, ((N, K), bits) in enumerate(zip(shapes, recipe)):
+        if K not in xs:
+            xs[K] = workload.activations(3, K, 8, K)
+        x8 = xs[K]
+        gen.manual_seed(3000 + idx)
+        W = (t.randn((N, K), generator=gen, device="cuda", dtype=t.float32) * 0.02).to(t.bfloat16)
+        if idx % 64 == 0:
+            report("workload 3 matrix %d (%d x %d, b=%d)" % (idx, N, K, bits))
+        P, S = dq.quantize_pack(W, bits)
+        y1 = dq.gemv(bf16_gpu(x8[:1]), P, S, K, bits)
+        y8 = dq.gemv(bf16_gpu(x8), P, S, K, bits)
+        rows = sample_rows(N, 6, idx)
+        w_rows = W.index_select(0, t.from_numpy(rows).cuda()).view(t.int16).cpu().numpy().view(np.uint16)
+        o_packed, o_scales, _ = oracle.quantize_pack(w_rows, bits)
+        idx_t = t.from_numpy(rows).cuda()
+        assert np.array_equal(u32(P.index_select(0, idx_t)), o_packed), "matrix %d packed" % idx
+        assert np.array_equal(f32_bits(S.index_select(0, idx_t)), o_scales.view(np.uint32))
+        check_products("gemv", x8[:1], y1, o_packed, o_scales, rows, K, bits)
+        check_products("gemv", x8, y8, o_packed, o_scales, rows, K, bits)
+
+
+@pytest.mark.parametrize("bits", [5, 6, 8, 12])
+def test_workload4_prefill_gemm(bits):
+    """8192 x 8192 bf16, x 2048 x 8192: packed words in full, outputs sampled."""
+    wl = workload.WORKLOADS[4]
+    i = list(wl.bits).index(bits)
+    w = workload.workload_weights(wl, i)
+    x = workload.activations(4, 0, 2048, wl.K)
+    report("workload 4 b=%d" % bits)
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    y = dq.gemm(bf16_gpu(x), P, S, wl.K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    assert np.array_equal(u32(P), o_packed)
+    assert np.array_equal(f32_bits(S), o_scales.view(np.uint32))
+    rows = np.arange(wl.N)
+    check_products("gemm", x, y, o_packed, o_scales, rows, wl.K, bits, max_pairs=3000, seed=bits)
+    # one whole output row and one whole output column as well
+    yy = y.cpu().numpy()
+    y_ref, bound = oracle.matmul_pairs(x, o_packed, o_scales, wl.N, wl.K, bits,
+                                       np.full(wl.N, 777), np.arange(wl.N))
+    assert within_tolerance(yy[777], y_ref, bound).all()
+    y_ref, bound = oracle.matmul_pairs(x, o_packed, o_scales, wl.N, wl.K, bits,
+                                       np.arange(2048), np.full(2048, 4321))
+    assert within_tolerance(yy[:, 4321], y_ref, bound).all()
+
+
+_T5 = {}
+
+
+def t5_weights():
+    if "w" not in _T5:
+        wl = workload.WORKLOADS[5]
+        _T5["w"] = workload.workload_weights(wl, 0)
+        _T5["W"] = weights_gpu(_T5["w"])
+    return _T5["w"], _T5["W"]
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_workload5_sweep(bits):
+    """28672 x 8192 Student-t(5) bf16, every b: quantize + pack (sampled rows, each
+    whole), GEMV at M = 1 and 16 and GEMM at M = 256 (sampled rows / outputs)."""
+    wl = workload.WORKLOADS[5]
+    w, W = t5_weights()
+    report("workload 5 b=%d" % bits)
+    P, S = dq.quantize_pack(W, bits)
+    x16 = workload.activations(5, bits, 16, wl.K)
+    x256 = workload.activations(5, 100 + bits, 256, wl.K)
+    y1 = dq.gemv(bf16_gpu(x16[:1]), P, S, wl.K, bits)
+    y16 = dq.gemv(bf16_gpu(x16), P, S, wl.K, bits)
+    y256 = dq.gemm(bf16_gpu(x256), P, S, wl.K, bits)
+    torch().cuda.synchronize()
+    rows = sample_rows(wl.N, 192, bits)
+    o_packed, o_scales = check_rows(w, rows, P, S, bits)
+    check_products("gemv", x16[:1], y1, o_packed, o_scales, rows, wl.K, bits)
+    check_products("gemv", x16, y16, o_packed, o_scales, rows, wl.K, bits)
+    check_products("gemm", x256, y256, o_packed, o_scales, rows, wl.K, bits, max_pairs=2000,
+                   seed=bits)
+
+
+@pytest.mark.parametrize("bits", [2, 9, 15])
+def test_largest_k(bits):
+    """K at the library's maximum (2^22), ragged N, every output checked."""
+    N, K = 3, 1 << 22
+    w = workload.weights(6, bits, N, K)
+    x = workload.activations(6, bits, 2, K)
+    report("largest K b=%d" % bits)
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    yv = dq.gemv(bf16_gpu(x), P, S, K, bits)
+    ym = dq.gemm(bf16_gpu(x), P, S, K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    assert np.array_equal(u32(P), o_packed)
+    y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
+    assert within_tolerance(yv.cpu().numpy(), y_ref, bound).all()
+    assert within_tolerance(ym.cpu().numpy(), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("bits", [4, 6, 9, 13])
+def test_big_gemm_ragged(bits):
+    """The large-tile GEMM with ragged M and N (tiles cut at both edges) and a K
+    that is a multiple of 64 but not of 128 (odd number of K steps)."""
+    M, N, K = 2048 + 37, 7936 + 91, 64 * 27
+    w = workload.weights(7, bits, N, K)
+    x = workload.activations(7, bits, M, K)
+    report("ragged big gemm b=%d" % bits)
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    y = dq.gemm(bf16_gpu(x), P, S, K, bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    check_products("gemm", x, y, o_packed, o_scales, np.arange(N), K, bits, max_pairs=4000,
+                   seed=bits)
+    yy = y.cpu().numpy()
+    edge_m = np.array([0, M - 1, M - 1, M - 37, 2047, 2048])
+    edge_n = np.array([N - 1, 0, N - 91, N - 1, 7935, 7936])
+    y_ref, bound = oracle.matmul_pairs(x, o_packed, o_scales, N, K, bits, edge_m, edge_n)
+    assert within_tolerance(yy[edge_m, edge_n], y_ref, bound).all()
