@@ -64,17 +64,73 @@ __device__ __forceinline__ void load_row_chunk(const void* __restrict__ w, int64
     }
 }
 
+// q = clip(rint(fl32(w / s))) for the 32 elements of a chunk, as offset-binary
+// codes packed into B words (elements at or past K give code 0 = zero bits).
+//
+// The divide: with r = fl32(1/s) (one IEEE divide per row), t' = fl32(w * r)
+// differs from w/s by at most 2^-23 |w/s|, and fl32(w/s) by at most 2^-24 |w/s|,
+// so |t' - fl32(w/s)| <= 1.5 * 2^-23 |w/s| <= 2^-22 (qmax + 1) for every element
+// of the row (|w/s| <= qmax (1 + 2^-23)).  rint gives the same integer for both
+// unless a half-integer lies within that distance of t'; only those elements
+// (and any non-finite t', e.g. when 1/s overflows) take the IEEE divide.
+template <int B>
+__device__ __forceinline__ void quantize_chunk(const float (&v)[kChunk], float s, float r,
+                                               float margin, bool zero_codes, int64_t k0,
+                                               int64_t K, uint32_t (&out)[B])
+{
+    constexpr int32_t kQmax = (1 << (B - 1)) - 1;
+    constexpr float kLo = (float)(-kQmax - 1);
+    constexpr float kHi = (float)kQmax;
+    constexpr float kBias = (float)(1 << (B - 1));
+#pragma unroll
+    for (int i = 0; i < B; ++i) out[i] = 0;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        float t = v[j] * r;
+        float q = rintf(t);
+        if (!(fabsf(t - q) < margin)) q = rintf(v[j] / s);  // near a tie, or not finite
+        q = fminf(fmaxf(q, kLo), kHi);
+        // code u = q + 2^(B-1) in [0, 2^B): exact in fp32, converted once
+        const uint32_t u = (zero_codes || k0 + j >= K) ? (k0 + j >= K ? 0u : (uint32_t)kBias)
+                                                         : (uint32_t)(q + kBias);
+        const int pos = j * B;
+        const int wi = pos >> 5;
+        const int off = pos & 31;
+        out[wi] |= u << off;
+        if (off + B > 32) out[wi + 1] |= u >> (32 - off);
+    }
+}
+
+template <int B>
+__device__ __forceinline__ void store_chunk(uint32_t* __restrict__ prow, int64_t c, int64_t row_words,
+                                            const uint32_t (&out)[B])
+{
+    const int64_t base = c * B;
+    if (base + B <= row_words) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) prow[base + i] = out[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+            if (base + i < row_words) prow[base + i] = out[i];
+    }
+}
+
+// One workgroup of 64..256 threads per row (enough for one chunk per thread
+// when K <= 8192).  Each thread keeps its first chunk in registers between the
+// max pass and the quantize pass; further chunks (long rows) are read again.
 template <int B, bool BF16>
 __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t K, int64_t row_words, uint32_t* __restrict__ packed,
     float* __restrict__ scales)
 {
     constexpr int32_t kQmax = (1 << (B - 1)) - 1;
-    constexpr uint32_t kBias = 1u << (B - 1);
     __shared__ uint32_t red[kQuantThreads / kWave];
 
     const int64_t n = blockIdx.x;
     const int tid = threadIdx.x;
+    const int threads = blockDim.x;
+    const int waves = threads / kWave;
     const int64_t nchunks = ceil_div(K, kChunk);
     const int64_t row_off = n * K;
     const int esize = BF16 ? 2 : 4;
@@ -82,8 +138,17 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     const bool vec_ok = ((K * esize) & 15) == 0;
 
     // ---- pass 1: max |w| as an integer max over sign-cleared bit patterns
+    float v0[kChunk];
     uint32_t amax = 0;
-    for (int64_t c = tid; c < nchunks; c += kQuantThreads) {
+    if (tid < nchunks) {
+        load_row_chunk<BF16>(w, row_off, K, tid, vec_ok, v0);
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const uint32_t m = __float_as_uint(v0[j]) & 0x7fffffffu;
+            amax = m > amax ? m : amax;
+        }
+    }
+    for (int64_t c = tid + threads; c < nchunks; c += threads) {
         float v[kChunk];
         load_row_chunk<BF16>(w, row_off, K, c, vec_ok, v);
 #pragma unroll
@@ -95,8 +160,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     amax = wave_max_u32(amax);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kQuantThreads / kWave; ++i) amax = red[i] > amax ? red[i] : amax;
+    for (int i = 0; i < waves; ++i) amax = red[i] > amax ? red[i] : amax;
 
     // ---- scale
     const float qmaxf = (float)kQmax;
@@ -115,70 +179,75 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
         }
     }
     if (tid == 0) scales[n] = s;
+    const float r = 1.0f / s;
+    const float margin = 0.5f - ldexpf(qmaxf + 1.0f, -21);
 
     // ---- pass 2: quantize, offset, pack 32 codes into B whole words
     uint32_t* __restrict__ prow = packed + n * row_words;
-    for (int64_t c = tid; c < nchunks; c += kQuantThreads) {
+    if (tid < nchunks) {
+        uint32_t out[B];
+        quantize_chunk<B>(v0, s, r, margin, zero_codes, (int64_t)tid * kChunk, K, out);
+        store_chunk<B>(prow, tid, row_words, out);
+    }
+    for (int64_t c = tid + threads; c < nchunks; c += threads) {
         float v[kChunk];
         load_row_chunk<BF16>(w, row_off, K, c, vec_ok, v);
         uint32_t out[B];
-#pragma unroll
-        for (int i = 0; i < B; ++i) out[i] = 0;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            float r = rintf(v[j] / s);
-            r = fminf(fmaxf(r, -qmaxf - 1.0f), qmaxf);
-            const int32_t q = zero_codes ? 0 : (int32_t)r;
-            const uint32_t u = (c * kChunk + j < K) ? (uint32_t)(q + (int32_t)kBias) : 0u;
-            const int pos = j * B;
-            const int wi = pos >> 5;
-            const int off = pos & 31;
-            out[wi] |= u << off;
-            if (off + B > 32) out[wi + 1] |= u >> (32 - off);
-        }
-        const int64_t base = c * B;
-        if (base + B <= row_words) {
-#pragma unroll
-            for (int i = 0; i < B; ++i) prow[base + i] = out[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < B; ++i)
-                if (base + i < row_words) prow[base + i] = out[i];
-        }
+        quantize_chunk<B>(v, s, r, margin, zero_codes, c * kChunk, K, out);
+        store_chunk<B>(prow, c, row_words, out);
     }
     // words past the last chunk are row padding
-    for (int64_t i = nchunks * B + tid; i < row_words; i += kQuantThreads) prow[i] = 0u;
+    for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
 }
 
-// One thread per chunk: B words -> 32 int32 codes (and fl32(q * s)).
+// One workgroup per row; thread t turns codes 4t .. 4t+3 (then + 1024, ...)
+// into int32 q (and fl32(q * s)), so every store instruction of a wave writes
+// one contiguous 1 KB run (or 256 B of dword stores when rows are not 16-byte
+// aligned).  The 4 codes occupy 4B bits from bit 4tB of the row stream: at most
+// three words, read through the L1 (neighbouring lanes share them), with
+// run-time funnel shifts.
+constexpr int kUnpackThreads = 256;
+
 template <int B>
-__global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
-                                                     const float* __restrict__ scales, int64_t N,
-                                                     int64_t K, int64_t row_words,
-                                                     int32_t* __restrict__ q_out,
-                                                     float* __restrict__ w_out)
+__global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
+    const uint32_t* __restrict__ packed, const float* __restrict__ scales, int64_t K,
+    int64_t row_words, int32_t* __restrict__ q_out, float* __restrict__ w_out)
 {
     constexpr int32_t kBias = 1 << (B - 1);
-    const int64_t nchunks = ceil_div(K, kChunk);
-    const int64_t total = N * nchunks;
-    for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
-         gid += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = gid / nchunks;
-    const int64_t c = gid - n * nchunks;
-    uint32_t wd[B];
-    load_chunk_words<B>(packed + n * row_words, c, row_words, wd);
+    constexpr uint32_t kMask = (1u << B) - 1u;
+    const int64_t n = blockIdx.x;
+    const uint32_t* __restrict__ row = packed + n * row_words;
     const float s = w_out ? scales[n] : 0.0f;
-    const int64_t k0 = c * kChunk;
-    const int64_t o = n * K + k0;
-    const bool full = k0 + kChunk <= K;
+    // 16-byte stores need every output row start 16-byte aligned
+    const bool vec = (K & 3) == 0 && ((reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(w_out)) & 15) == 0;
+    for (int64_t k0 = 4 * (int64_t)threadIdx.x; k0 < K; k0 += 4 * kUnpackThreads) {
+        const int64_t bit = k0 * B;
+        const int64_t wi = bit >> 5;
+        const uint32_t off = (uint32_t)(bit & 31);
+        const uint32_t w0 = row[wi];
+        const uint32_t w1 = wi + 1 < row_words ? row[wi + 1] : 0u;
+        const uint32_t w2 = wi + 2 < row_words ? row[wi + 2] : 0u;
+        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, off);  // stream bits [bit, bit+32)
+        const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, off);  // [bit+32, bit+64)
+        const uint64_t v = (uint64_t)hi << 32 | lo;
+        int32_t q[4];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-        if (full || k0 + j < K) {
-            const int32_t q = (int32_t)chunk_code_unsigned<B>(wd, j) - kBias;
-            if (q_out) q_out[o + j] = q;
-            if (w_out) w_out[o + j] = (float)q * s;
+        for (int j = 0; j < 4; ++j) q[j] = (int32_t)((uint32_t)(v >> (j * B)) & kMask) - kBias;
+        const int64_t o = n * K + k0;
+        if (vec) {
+            if (q_out) *reinterpret_cast<int4*>(q_out + o) = make_int4(q[0], q[1], q[2], q[3]);
+            if (w_out)
+                *reinterpret_cast<float4*>(w_out + o) =
+                    make_float4((float)q[0] * s, (float)q[1] * s, (float)q[2] * s, (float)q[3] * s);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (k0 + j < K) {
+                    if (q_out) q_out[o + j] = q[j];
+                    if (w_out) w_out[o + j] = (float)q[j] * s;
+                }
+            }
         }
-    }
     }
 }
 
@@ -187,11 +256,15 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
                                   float* scales, hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
+    // one chunk per thread where the row allows, in whole waves, 64..256 threads
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
+                                                       : ceil_div(nchunks, kWave) * kWave);
     if (bf16)
-        quantize_pack_kernel<B, true><<<dim3((unsigned)N), dim3(kQuantThreads), 0, stream>>>(
+        quantize_pack_kernel<B, true><<<dim3((unsigned)N), dim3(threads), 0, stream>>>(
             w, K, rw, packed, scales);
     else
-        quantize_pack_kernel<B, false><<<dim3((unsigned)N), dim3(kQuantThreads), 0, stream>>>(
+        quantize_pack_kernel<B, false><<<dim3((unsigned)N), dim3(threads), 0, stream>>>(
             w, K, rw, packed, scales);
     return hipGetLastError();
 }
@@ -201,10 +274,8 @@ hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, int64_t 
                            int32_t* q_out, float* w_out, hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
-    const int64_t threads = N * ceil_div(K, kChunk);
-    const int64_t blocks = ceil_div(threads, 256) < 65536 ? ceil_div(threads, 256) : 65536;
-    unpack_kernel<B><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(packed, scales, N, K, rw,
-                                                                       q_out, w_out);
+    unpack_kernel<B><<<dim3((unsigned)N), dim3(kUnpackThreads), 0, stream>>>(packed, scales, K, rw,
+                                                                            q_out, w_out);
     return hipGetLastError();
 }
 
