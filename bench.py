@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed steps, copy 256 MiB device to device once (a plain copy "
+                        "of known size for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -257,6 +260,13 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(decode_np, x1_np, args.cpu_seconds)
     print(json.dumps(out))
