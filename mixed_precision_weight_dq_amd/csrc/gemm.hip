@@ -302,10 +302,11 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int j = 0; j < kNT; ++j) expand8<B>(w[st][j], t, bh[t][j], bl[t][j]);
-        // step ks+1 (past the last step these read beyond the buffers' ends,
-        // which buffer loads return as zeros; the data is never used)
-        load_w(std::integral_constant<int, st ^ 1>{}, ks + 1);
-        load_x(ks + 1);
+        // step ks+1 (after the last step, the last step again: loads stay
+        // inside the buffers and the data is never used)
+        const int64_t kn = ks + 1 < nk ? ks + 1 : nk - 1;
+        load_w(std::integral_constant<int, st ^ 1>{}, kn);
+        load_x(kn);
         // keep the loads here, a whole step ahead of their use (the scheduler
         // would otherwise sink them next to the LDS stores to save registers)
         __builtin_amdgcn_sched_barrier(0);
@@ -359,6 +360,245 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel for large M and N (K a multiple of 64): one 256-thread workgroup
+// per CU computes a 256 x (128 kNT) tile.  Each wave owns all 256 rows and
+// 32 kNT columns, so every expanded code operand feeds eight MFMAs (one per
+// 32-row sub-tile of x): half the expansion work per MFMA of the 128-row
+// kernel above.  The accumulators fill the 256 AGPRs (kNT = 2), which leaves
+// one wave per SIMD, so the step is software-pipelined inside the wave:
+//   * x goes from global memory straight into LDS (buffer_load ... lds; three
+//     stages, same swizzle as above), a step ahead of its use;
+//   * codes of step ks+2 are loaded at the top of step ks (three register
+//     stages), so they have two steps to arrive;
+//   * the operands of substep t+1 (and of the next step's substep 0) are
+//     expanded while the MFMAs of substep t run.
+// Tile order: consecutive workgroups go round robin to the 8 XCDs; each XCD
+// gets a contiguous range of tiles laid out as groups of 4 row tiles by all
+// column tiles, so an XCD streams half of x and a quarter of W (at 8 x 32
+// tiles) instead of all of x.
+template <int kNT>
+struct WideTile {
+    static constexpr int BM = 256;
+    static constexpr int BN = 4 * 32 * kNT;
+    static constexpr int BK = 64;
+    static constexpr int kPieces = BM * 8;  // 16-byte pieces of one x tile
+};
+
+template <int B, int kNT>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
+    const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y)
+{
+    using T = WideTile<kNT>;
+    constexpr int kMT = T::BM / 32;
+    constexpr bool kSplit = B >= 10;
+    constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
+    __shared__ __attribute__((aligned(16))) uint4 As[3][T::kPieces];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int c = lane & 31;
+    const int h = lane >> 5;
+
+    const int64_t ntm = ceil_div(M, T::BM);
+    const int64_t ntn = ceil_div(N, T::BN);
+    const int64_t tiles = ntm * ntn;
+    int64_t L = blockIdx.x;
+    if ((tiles & 7) == 0) L = (L & 7) * (tiles >> 3) + (L >> 3);
+    const int64_t gm = (ntm & 3) == 0 ? 4 : 1;
+    const int64_t grp = L / (gm * ntn), rem = L % (gm * ntn);
+    const int64_t m0 = (grp * gm + rem % gm) * T::BM;
+    const int64_t n0 = (rem / gm) * T::BN;
+    const int64_t nk = K / T::BK;
+
+    // x copy, global -> LDS directly (buffer_load ... lds): instruction i of
+    // wave w fills the 64 consecutive 16-byte LDS slots (8 w + i) * 64 + lane,
+    // so lane l fetches the piece that belongs in its slot: row r = slot / 8,
+    // piece p = (slot % 8) ^ xswz(r)
+    const int64_t mrows = M - m0 < T::BM ? M - m0 : T::BM;
+    const BufRef xbuf = uniform_buf(x + m0 * K, (uint32_t)(mrows * K * 2));
+    uint32_t xoff[kCopyInstr];
+#pragma unroll
+    for (int i = 0; i < kCopyInstr; ++i) {
+        const int slot = (wave * kCopyInstr + i) * 64 + lane;
+        const int r = slot >> 3;
+        const int p = (slot & 7) ^ xswz(r);
+        const int64_t rl = r < mrows ? r : mrows - 1;
+        xoff[i] = (uint32_t)(rl * K * 2 + 16 * p);
+    }
+    const int64_t nrows = N - n0 < T::BN ? N - n0 : T::BN;
+    const BufRef wbuf = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
+    uint32_t woff[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+        const int64_t nl = wave * 32 * kNT + j * 32 + c;
+        woff[j] = (uint32_t)((nl < nrows ? nl : nrows - 1) * row_words * 4 + h * B * 4);
+    }
+    int abase[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) abase[t] = c * 8 + ((4 * h + t) ^ xswz(c));
+
+    f32x16_t acc[kMT][kNT];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint32_t w[3][kNT][B];  // codes of steps ks, ks+1, ks+2 (stage = step % 3)
+    bf16x8_t bh[kNT], bl[kNT];  // operands of the current substep
+    auto load_x = [&](auto S, int64_t ks) {  // x of step ks -> LDS stage S
+        constexpr int st = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < kCopyInstr; ++i)
+            buf_load_lds16(xbuf, &As[st][(wave * kCopyInstr + i) * 64], xoff[i],
+                           (uint32_t)(ks * T::BK * 2));
+    };
+    auto load_w = [&](auto S, int64_t ks) {
+        constexpr int st = decltype(S)::value;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) buf_load_words<B>(wbuf, woff[j], (uint32_t)(ks * 8 * B), w[st][j]);
+    };
+    // MFMAs of one substep and the instructions that prepare the next one,
+    // interleaved: every MFMA (32 cycles) covers a share of the next
+    // substep's LDS reads and code expansion.
+    constexpr int kMfmaPerSub = kMT * kNT * (kSplit ? 2 : 1);
+    auto interleave = [&]() {
+#pragma unroll
+        for (int g = 0; g < kMT; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                // 6 VALU
+#pragma unroll
+            for (int e = 1; e < kMfmaPerSub / kMT; ++e) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+    };
+    bf16x8_t a[2][kMT];  // x operands of the current and the next substep
+    auto read_a = [&](auto S, int t, bf16x8_t (&dst)[kMT]) {
+        constexpr int st = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) dst[i] = __builtin_bit_cast(bf16x8_t, As[st][abase[t] + 256 * i]);
+    };
+    // Loads still in flight when a wave waits before its barrier: the codes of
+    // step ks+2, issued at the top of step ks after the copy of x(ks+1).
+    constexpr int kWLoads = kNT * (B / 4 + (B % 4 != 0 ? 1 : 0));
+    // s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+    // vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum)
+    constexpr int kWaitX = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (7 << 4) | (15 << 8);
+    constexpr int kPro = 2 * kWLoads + kCopyInstr;
+    constexpr int kWaitPro = (kPro & 15) | ((kPro >> 4) << 14) | (7 << 4) | (15 << 8);
+    static_assert(kPro < 64, "vmcnt holds at most 63");
+
+    // step ks with its x in LDS stage S and its codes in register stage S
+    // (both ks % 3).  Top: the codes of step ks+2 are loaded.  After substep 2
+    // each wave waits for its copy of x(ks+1) into LDS (issued a step earlier;
+    // only the code loads issued since may remain), and a barrier makes stage
+    // ks+1 visible; substep 3 reads its first operands, and x of step ks+2 is
+    // copied into stage ks+2, which no wave reads any more (its last reads
+    // came before the barrier of step ks-1).  After the last step the loads
+    // fetch the last step again (in bounds, never used).
+    auto step = [&](auto S, int64_t ks) {
+        constexpr int st = decltype(S)::value;
+        constexpr int s1 = (st + 1) % 3, s2 = (st + 2) % 3;
+        const int64_t k2 = ks + 2 < nk ? ks + 2 : nk - 1;
+        load_w(std::integral_constant<int, s2>{}, k2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < 3)
+                read_a(S, t + 1, a[(t + 1) & 1]);
+            else
+                read_a(std::integral_constant<int, s1>{}, 0, a[0]);
+            bf16x8_t nh[kNT], nl[kNT];
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                if (t < 3)
+                    expand8<B>(w[st][j], t + 1, nh[j], nl[j]);
+                else
+                    expand8<B>(w[s1][j], 0, nh[j], nl[j]);
+            }
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                for (int j = 0; j < kNT; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[j], acc[i][j], 0, 0, 0);
+                    if constexpr (kSplit)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bl[j], acc[i][j], 0, 0, 0);
+                }
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                bh[j] = nh[j];
+                bl[j] = nl[j];
+            }
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t == 2) {
+                __builtin_amdgcn_s_waitcnt(kWaitX);
+                __syncthreads();  // stage ks+1 written by every wave
+                load_x(std::integral_constant<int, s2>{}, k2);
+            }
+        }
+    };
+
+    load_x(std::integral_constant<int, 0>{}, 0);
+    load_x(std::integral_constant<int, 1>{}, nk > 1 ? 1 : 0);
+    load_w(std::integral_constant<int, 0>{}, 0);
+    load_w(std::integral_constant<int, 1>{}, nk > 1 ? 1 : 0);
+    __builtin_amdgcn_s_waitcnt(kWaitPro);  // x(0) in LDS
+    __syncthreads();
+    read_a(std::integral_constant<int, 0>{}, 0, a[0]);
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) expand8<B>(w[0][j], 0, bh[j], bl[j]);
+    int64_t ks = 0;
+    for (; ks + 3 <= nk; ks += 3) {
+        step(std::integral_constant<int, 0>{}, ks);
+        step(std::integral_constant<int, 1>{}, ks + 1);
+        step(std::integral_constant<int, 2>{}, ks + 2);
+    }
+    if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+    // the copies into LDS issued by the last step are never waited for by a
+    // barrier; let them land before the workgroup ends, so they cannot write
+    // into the LDS of the next workgroup placed on this CU
+    __builtin_amdgcn_s_waitcnt(0);
+
+    constexpr float kUnscale = 1.0f / expand8_scale<B>();
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+        const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
+        if (n >= N) continue;
+        const float s = scales[n];
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
+            }
+        }
+    }
+}
+
+template <int B, int kNT>
+hipError_t launch_gemm_wide(const uint16_t* x, int64_t M, const uint32_t* packed,
+                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+{
+    using T = WideTile<kNT>;
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t tiles = ceil_div(N, T::BN) * ceil_div(M, T::BM);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    gemm_wide_kernel<B, kNT><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(x, M, packed, scales, N,
+                                                                             K, rw, y);
+    return hipGetLastError();
+}
+
 template <int B, int kMT, int kNT, int kOcc>
 hipError_t launch_gemm_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
@@ -377,6 +617,12 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
                          int64_t N, int64_t K, float* y, hipStream_t stream)
 {
     if (K % 64 == 0) {
+        // 256-row tiles with one workgroup per CU when they fill the 256 CUs
+        // in whole rounds (at least 80 % of the last round busy)
+        constexpr int kWideNT = B <= 8 ? 2 : 1;
+        const int64_t wide = ceil_div(M, 256) * ceil_div(N, WideTile<kWideNT>::BN);
+        if (M >= 256 && wide >= 256 && wide * 5 >= ceil_div(wide, 256) * 256 * 4)
+            return launch_gemm_wide<B, kWideNT>(x, M, packed, scales, N, K, y, stream);
         // 128 x 256 tiles (codes up to 8 bits: wider ones need more registers
         // than two workgroups per CU leave), when they fill the 256 CUs twice
         // over; else 128 x 128

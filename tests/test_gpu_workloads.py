@@ -228,3 +228,39 @@ def test_big_gemm_ragged(bits):
     edge_n = np.array([N - 1, 0, N - 91, N - 1, 7935, 7936])
     y_ref, bound = oracle.matmul_pairs(x, o_packed, o_scales, N, K, bits, edge_m, edge_n)
     assert within_tolerance(yy[edge_m, edge_n], y_ref, bound).all()
+
+
+WIDE_CASES = [
+    # (M, N, K): 8 x 32 (or 8 x 64) tiles of 256 rows with ragged last row and
+    # column tiles and 7 or 8 K steps (one or two steps after the 3-step loop);
+    # 6 x 42 tiles (no 4-tile grouping, tile count not a multiple of 8) and 9 steps
+    (2000, 8100, 64 * 7),
+    (2000, 8100, 64 * 8),
+    (1300, 10700, 64 * 9),
+]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 15])
+def test_wide_gemm_ragged(bits):
+    """The 256-row-tile GEMM (one workgroup per CU) on ragged shapes that select it."""
+    for ci, (M, N, K) in enumerate(WIDE_CASES):
+        if ci == 2 and bits not in (4, 6, 9, 12):
+            continue
+        w = workload.weights(8, bits * 10 + ci, N, K)
+        x = workload.activations(8, bits * 10 + ci, M, K)
+        report("wide gemm M=%d N=%d K=%d b=%d" % (M, N, K, bits))
+        P, S = dq.quantize_pack(weights_gpu(w), bits)
+        y = dq.gemm(bf16_gpu(x), P, S, K, bits)
+        torch().cuda.synchronize()
+        o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+        check_products("gemm", x, y, o_packed, o_scales, np.arange(N), K, bits, max_pairs=3000,
+                       seed=bits + 100 * ci)
+        yy = y.cpu().numpy()
+        rows = np.array([0, 255, 256, M - 1, M - 1, M // 2, 1791, 1792])
+        cols = np.array([N - 1, 127, 128, 0, N - 1 - (N % 128), 4095, N - 2, N - 1])
+        rows = np.minimum(rows, M - 1)
+        y_ref, bound = oracle.matmul_pairs(x, o_packed, o_scales, N, K, bits, rows, cols)
+        assert within_tolerance(yy[rows, cols], y_ref, bound).all()
+        # one whole output row and column through the oracle
+        y_ref_row, bound_row = oracle.matmul(x[M - 1:M], o_packed, o_scales, N, K, bits)
+        assert within_tolerance(yy[M - 1:M], y_ref_row, bound_row).all()
