@@ -342,8 +342,25 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     }
     if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
 
-    // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4
+    // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4;
+    // whole tiles store without bounds checks, as streaming stores
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
+    if (m0 + T::BM <= M && n0 + T::BN <= N) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
+            const float s = scales[n];
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) {
+                float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    __builtin_nontemporal_store(s * (acc[i][j][r] * kUnscale),
+                                                yp + (8 * (r >> 2) + (r & 3)) * N);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
@@ -377,6 +394,10 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 // gets a contiguous range of tiles laid out as groups of 4 row tiles by all
 // column tiles, so an XCD streams half of x and a quarter of W (at 8 x 32
 // tiles) instead of all of x.
+#ifndef DQ_WIDE_DEPTH
+#define DQ_WIDE_DEPTH 2
+#endif
+
 template <int kNT>
 struct WideTile {
     static constexpr int BM = 256;
@@ -385,17 +406,18 @@ struct WideTile {
     static constexpr int kPieces = BM * 8;  // 16-byte pieces of one x tile
 };
 
-template <int B, int kNT>
+template <int B, int kNT, int kDepth>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
     float* __restrict__ y)
 {
     using T = WideTile<kNT>;
+    constexpr int kStages = kDepth + 1;  // x (LDS) and code (register) stages
     constexpr int kMT = T::BM / 32;
     constexpr bool kSplit = B >= 10;
     constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
-    __shared__ __attribute__((aligned(16))) uint4 As[3][T::kPieces];
+    __shared__ __attribute__((aligned(16))) uint4 As[kStages][T::kPieces];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -449,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint32_t w[3][kNT][B];  // codes of steps ks, ks+1, ks+2 (stage = step % 3)
+    uint32_t w[kStages][kNT][B];  // codes of steps ks .. ks+kDepth (stage = step % kStages)
     bf16x8_t bh[kNT], bl[kNT];  // operands of the current substep
     auto load_x = [&](auto S, int64_t ks) {  // x of step ks -> LDS stage S
         constexpr int st = decltype(S)::value;
@@ -486,29 +508,33 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
         for (int i = 0; i < kMT; ++i) dst[i] = __builtin_bit_cast(bf16x8_t, As[st][abase[t] + 256 * i]);
     };
-    // Loads still in flight when a wave waits before its barrier: the codes of
-    // step ks+2, issued at the top of step ks after the copy of x(ks+1).
+    // Vector-memory operations a wave may leave in flight when it waits for
+    // its copy of x(ks+1) before the barrier of step ks: the code loads issued
+    // at the tops of steps ks+2-kDepth .. ks and the x copies issued in the
+    // middle of steps ks+2-kDepth .. ks-1 (all issued after that copy).
     constexpr int kWLoads = kNT * (B / 4 + (B % 4 != 0 ? 1 : 0));
+    constexpr int kAfter = (kDepth - 1) * kWLoads + (kDepth - 2) * kCopyInstr;
     // s_waitcnt with only the vector-memory count limited (gfx9 encoding:
     // vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum)
-    constexpr int kWaitX = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (7 << 4) | (15 << 8);
-    constexpr int kPro = 2 * kWLoads + kCopyInstr;
+    constexpr int kWaitX = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+    // prologue: x(0) .. x(kDepth-1), then the codes of steps 0 .. kDepth-1
+    constexpr int kPro = (kDepth - 1) * kCopyInstr + kDepth * kWLoads;
     constexpr int kWaitPro = (kPro & 15) | ((kPro >> 4) << 14) | (7 << 4) | (15 << 8);
-    static_assert(kPro < 64, "vmcnt holds at most 63");
+    static_assert(kPro < 64 && kAfter < 64, "vmcnt holds at most 63");
 
     // step ks with its x in LDS stage S and its codes in register stage S
-    // (both ks % 3).  Top: the codes of step ks+2 are loaded.  After substep 2
-    // each wave waits for its copy of x(ks+1) into LDS (issued a step earlier;
-    // only the code loads issued since may remain), and a barrier makes stage
-    // ks+1 visible; substep 3 reads its first operands, and x of step ks+2 is
-    // copied into stage ks+2, which no wave reads any more (its last reads
-    // came before the barrier of step ks-1).  After the last step the loads
-    // fetch the last step again (in bounds, never used).
+    // (both ks % kStages).  Top: the codes of step ks+kDepth are loaded.
+    // After substep 2 each wave waits for its copy of x(ks+1) into LDS (only
+    // operations issued after it may remain), and a barrier makes stage ks+1
+    // visible; substep 3 reads its first operands, and x of step ks+kDepth is
+    // copied into its stage, which no wave reads any more (its last reads came
+    // before the barrier of step ks-1).  After the last step the loads fetch
+    // the last step again (in bounds, never used).
     auto step = [&](auto S, int64_t ks) {
         constexpr int st = decltype(S)::value;
-        constexpr int s1 = (st + 1) % 3, s2 = (st + 2) % 3;
-        const int64_t k2 = ks + 2 < nk ? ks + 2 : nk - 1;
-        load_w(std::integral_constant<int, s2>{}, k2);
+        constexpr int s1 = (st + 1) % kStages, sd = (st + kDepth) % kStages;
+        const int64_t kd = ks + kDepth < nk ? ks + kDepth : nk - 1;
+        load_w(std::integral_constant<int, sd>{}, kd);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -542,34 +568,60 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
             if (t == 2) {
                 __builtin_amdgcn_s_waitcnt(kWaitX);
                 __syncthreads();  // stage ks+1 written by every wave
-                load_x(std::integral_constant<int, s2>{}, k2);
+                load_x(std::integral_constant<int, sd>{}, kd);
             }
         }
     };
 
+    static_assert(kDepth == 2 || kDepth == 3, "pipeline depth 2 or 3");
     load_x(std::integral_constant<int, 0>{}, 0);
-    load_x(std::integral_constant<int, 1>{}, nk > 1 ? 1 : 0);
+    load_x(std::integral_constant<int, 1>{}, nk > 1 ? 1 : nk - 1);
+    if constexpr (kDepth > 2) load_x(std::integral_constant<int, 2 % kStages>{}, nk > 2 ? 2 : nk - 1);
     load_w(std::integral_constant<int, 0>{}, 0);
-    load_w(std::integral_constant<int, 1>{}, nk > 1 ? 1 : 0);
+    load_w(std::integral_constant<int, 1>{}, nk > 1 ? 1 : nk - 1);
+    if constexpr (kDepth > 2) load_w(std::integral_constant<int, 2 % kStages>{}, nk > 2 ? 2 : nk - 1);
     __builtin_amdgcn_s_waitcnt(kWaitPro);  // x(0) in LDS
     __syncthreads();
     read_a(std::integral_constant<int, 0>{}, 0, a[0]);
 #pragma unroll
     for (int j = 0; j < kNT; ++j) expand8<B>(w[0][j], 0, bh[j], bl[j]);
     int64_t ks = 0;
-    for (; ks + 3 <= nk; ks += 3) {
+    for (; ks + kStages <= nk; ks += kStages) {
         step(std::integral_constant<int, 0>{}, ks);
         step(std::integral_constant<int, 1>{}, ks + 1);
         step(std::integral_constant<int, 2>{}, ks + 2);
+        if constexpr (kStages > 3) step(std::integral_constant<int, 3 % kStages>{}, ks + 3);
     }
     if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
     if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+    if constexpr (kStages > 3)
+        if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
     // the copies into LDS issued by the last step are never waited for by a
     // barrier; let them land before the workgroup ends, so they cannot write
     // into the LDS of the next workgroup placed on this CU
     __builtin_amdgcn_s_waitcnt(0);
 
+    // epilogue: lane (c, h) holds column c of each 32 x 32 tile, rows
+    // 8 (r / 4) + 4 h + r % 4 of accumulator register r.  Whole tiles store
+    // without bounds checks, as streaming (nontemporal) stores: y is written
+    // once and not read back by this kernel.
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
+    if (m0 + T::BM <= M && n0 + T::BN <= N) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
+            const float s = scales[n];
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) {
+                float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    __builtin_nontemporal_store(s * (acc[i][j][r] * kUnscale),
+                                                yp + (8 * (r >> 2) + (r & 3)) * N);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
@@ -586,7 +638,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     }
 }
 
-template <int B, int kNT>
+template <int B, int kNT, int kDepth>
 hipError_t launch_gemm_wide(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
 {
@@ -594,7 +646,7 @@ hipError_t launch_gemm_wide(const uint16_t* x, int64_t M, const uint32_t* packed
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, T::BN) * ceil_div(M, T::BM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    gemm_wide_kernel<B, kNT><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(x, M, packed, scales, N,
+    gemm_wide_kernel<B, kNT, kDepth><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(x, M, packed, scales, N,
                                                                              K, rw, y);
     return hipGetLastError();
 }
@@ -622,7 +674,7 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
         constexpr int kWideNT = B <= 8 ? 2 : 1;
         const int64_t wide = ceil_div(M, 256) * ceil_div(N, WideTile<kWideNT>::BN);
         if (M >= 256 && wide >= 256 && wide * 5 >= ceil_div(wide, 256) * 256 * 4)
-            return launch_gemm_wide<B, kWideNT>(x, M, packed, scales, N, K, y, stream);
+            return launch_gemm_wide<B, kWideNT, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, stream);
         // 128 x 256 tiles (codes up to 8 bits: wider ones need more registers
         // than two workgroups per CU leave), when they fill the 256 CUs twice
         // over; else 128 x 128
