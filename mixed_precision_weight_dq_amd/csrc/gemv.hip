@@ -6,14 +6,20 @@
 // bound by the bytes of the packed weights (decode is memory-bound, as the
 // Quantization tutorial's closing remark on prefill vs decode puts it).
 //
-// Work split: a wave owns kRows rows; lane l walks the chunks l, l+64, ... of
-// those rows (a chunk = 32 codes = B whole words, so a wave's loads of one row
-// cover 64*B contiguous words).  Codes are turned into signed integers with one
-// XOR per word plus a signed bit-field extract, converted to fp32 and
-// accumulated with fp32 FMAs against x (widened exactly from bf16).  The row
-// scale multiplies the reduced sum once.
+// Three kernels by M (the row scale always multiplies the reduced sum once):
+//   * M <= 2 (gemv_lds_kernel): a wave owns a row; lane l walks the chunks
+//     l, l+64, ... of it (a chunk = 32 codes = B whole words, so a wave's
+//     loads of one row cover 64*B contiguous words); x is staged in LDS; codes
+//     become signed integers with one XOR per word plus a signed bit-field
+//     extract and meet x in bf16 pair dot products (fp32 FMAs for B >= 10);
+//   * 3 <= M <= 4 (gemv_kernel): the same per-lane decoding with x read per
+//     chunk from the caches;
+//   * 5 <= M <= 16 (gemv_mfma_kernel): codes expanded to exact bf16 operands
+//     of v_mfma_f32_16x16x32_bf16, so the VALU cost per code no longer grows
+//     with M.
 #include "common.hpp"
 #include "launch.hpp"
+#include "gemm_tiles.hpp"
 
 namespace dq {
 
@@ -388,6 +394,176 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 3 <= M <= 16 on the matrix cores (v_mfma_f32_16x16x32_bf16): with 16 rows of
+// x the VALU dot products would cost 8 instructions per code, so the codes
+// are expanded once into exact bf16 operands (2-3 instructions per code) and
+// the products run on the MFMA units, leaving the kernel bound by the bytes of
+// the packed weights again.
+//
+// A workgroup owns 16 kNT weight rows; its 4 waves take the 128-code K steps
+// w, w+4, w+8, ... (together they stream each row's consecutive 512-code
+// blocks) and add their partial 16 x 16 sums in LDS at the end.  In a step,
+// lane l = 16 g + c takes chunk 4 ks + g of row c (B whole words) and, for
+// MFMA substep t, its codes 8t .. 8t+7 as the B operand (column c, k rows
+// 8g .. 8g+7 of the 16x16x32 shape); the A operand of lane l is x[c][32 (4 ks
+// + g) + 8 t .. + 8], so both sides use the same order of k.  Rows m >= M of x
+// are zero.  The codes and x of the next kDepth steps are loaded before this
+// step is computed.
+constexpr int kGemvMfmaWaves = 4;
+
+template <int B, int kNT, int kDepth>
+__global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y)
+{
+    typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
+    typedef float f32x4m_t __attribute__((ext_vector_type(4)));
+    constexpr bool kSplit = B >= 10;
+    constexpr int kStages = kDepth + 1;
+    __shared__ float red[kGemvMfmaWaves - 1][kNT][4][kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * kNT;
+    const uint32_t* rowp[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+        const int64_t n = n0 + 16 * j + c;
+        rowp[j] = packed + (n < N ? n : N - 1) * row_words;
+    }
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int64_t nsteps = ceil_div(nchunks, 4);
+    const bool xrow = c < M;
+    const uint16_t* xr = x + (int64_t)(xrow ? c : 0) * K;
+    const bool xvec = (K & 7) == 0;
+
+    uint32_t w[kStages][kNT][B];
+    uint4 xa[kStages][4];
+    auto load = [&](auto P, int64_t ks) {
+        constexpr int p = decltype(P)::value;
+        const int64_t ch = 4 * ks + g;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            if (ks < nsteps && ch < nchunks) {
+                load_chunk_words<B>(rowp[j], ch, row_words, w[p][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < B; ++i) w[p][j][i] = 0;
+            }
+        }
+        const int64_t k0 = ch * kChunk;
+        if (xrow && ks < nsteps && xvec && k0 + kChunk <= K) {
+            const uint4* src = reinterpret_cast<const uint4*>(xr + k0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[p][i] = src[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t d[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t k = k0 + 8 * i + 2 * e;
+                    const uint32_t lo = (xrow && ks < nsteps && k < K) ? xr[k] : 0u;
+                    const uint32_t hi = (xrow && ks < nsteps && k + 1 < K) ? xr[k + 1] : 0u;
+                    d[e] = lo | hi << 16;
+                }
+                xa[p][i] = make_uint4(d[0], d[1], d[2], d[3]);
+            }
+        }
+    };
+    f32x4m_t acc[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](auto P) {
+        constexpr int p = decltype(P)::value;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8m_t a = __builtin_bit_cast(bf16x8m_t, xa[p][t]);
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                bf16x8_t bh, bl;
+                expand8<B>(w[p][j], t, bh, bl);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
+                if constexpr (kSplit) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
+            }
+        }
+    };
+    constexpr int64_t kW = kGemvMfmaWaves;
+    int64_t ks = wave;
+    load(std::integral_constant<int, 0>{}, ks);
+    if constexpr (kDepth > 1) load(std::integral_constant<int, 1>{}, ks + kW);
+    if constexpr (kDepth == 1) {
+        for (; ks + kW < nsteps; ks += 2 * kW) {
+            load(std::integral_constant<int, 1>{}, ks + kW);
+            compute(std::integral_constant<int, 0>{});
+            load(std::integral_constant<int, 0>{}, ks + 2 * kW);
+            compute(std::integral_constant<int, 1>{});
+        }
+        if (ks < nsteps) compute(std::integral_constant<int, 0>{});
+    } else {
+        for (; ks + 2 * kW < nsteps; ks += 3 * kW) {
+            load(std::integral_constant<int, 2>{}, ks + 2 * kW);
+            compute(std::integral_constant<int, 0>{});
+            load(std::integral_constant<int, 0>{}, ks + 3 * kW);
+            compute(std::integral_constant<int, 1>{});
+            load(std::integral_constant<int, 1>{}, ks + 4 * kW);
+            compute(std::integral_constant<int, 2>{});
+        }
+        if (ks < nsteps) compute(std::integral_constant<int, 0>{});
+        if (ks + kW < nsteps) compute(std::integral_constant<int, 1>{});
+    }
+
+    // lane (g, c) holds rows 4 g + r of column c; waves 1..3 hand theirs to wave 0
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][j][r][lane] = acc[j][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr float kUnscale = 1.0f / expand8_scale<B>();
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            const int64_t n = n0 + 16 * j + c;
+            if (n >= N) continue;
+            const float s = scales[n];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = acc[j][r];
+#pragma unroll
+                for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
+                const int m = 4 * g + r;
+                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
+            }
+        }
+    }
+}
+
+#ifndef DQ_GEMV_MFMA_NT
+#define DQ_GEMV_MFMA_NT 1
+#endif
+#ifndef DQ_GEMV_MFMA_DEPTH
+#define DQ_GEMV_MFMA_DEPTH 1
+#endif
+
+template <int B>
+hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
+                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+{
+    constexpr int kNT = DQ_GEMV_MFMA_NT;
+    const int64_t rw = packed_row_words(K, B);
+    gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH>
+        <<<dim3((unsigned)ceil_div(N, 16 * kNT)), dim3(kGemvMfmaWaves * kWave), 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
+    return hipGetLastError();
+}
+
 #ifndef DQ_GEMV_ROWS_NARROW
 #define DQ_GEMV_ROWS_NARROW 1
 #endif
@@ -432,8 +608,7 @@ hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
     if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, stream);
     if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, stream);
     if (M <= 4) return launch_gemv_bm<B, 4>(x, M, packed, scales, N, K, y, stream);
-    if (M <= 8) return launch_gemv_bm<B, 8>(x, M, packed, scales, N, K, y, stream);
-    return launch_gemv_bm<B, 16>(x, M, packed, scales, N, K, y, stream);
+    return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, stream);
 }
 
 }  // namespace
