@@ -198,6 +198,24 @@ def main():
     gemm_le9_ms = float(np.mean([t for b, t in gemm_ms.items() if b <= 9]))
     gemm_le9 = gemm_flop / (gemm_le9_ms * 1e-3) / 1e12
 
+    # context for the GEMM figure, outside the timed steps: the plain bf16
+    # library GEMM (torch.matmul -> hipBLASLt) on the same shape and GPU, with
+    # the dense bf16 weights the prefill matrices were quantized from
+    WT = W4[PREFILL["bits"][1]].t().contiguous()
+    for _ in range(3):
+        torch.matmul(X4, WT)
+    torch.cuda.synchronize()
+    lib_ms = []
+    for _ in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.matmul(X4, WT)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lib_ms.append(e0.elapsed_time(e1))
+    lib_tflops = 2.0 * PREFILL["M"] * PREFILL["N"] * PREFILL["K"] / (float(np.median(lib_ms)) * 1e-3) / 1e12
+    del WT
+
     def gbs(kind, bits, N, K, read_bits, write_bits):
         """(read + write) bytes of the group's launches over the group time"""
         total = sum(N * K * (read_bits(b) + write_bits(b)) / 8 for b in bits)
@@ -249,6 +267,11 @@ def main():
             "note": "algorithmic 2*M*N*K flops; b >= 10 issues twice the MFMA work (exact hi/lo "
                     "bf16 split), so its ceiling is half the peak",
             "per_launch_us": round(gemm_le9_ms * 1e3, 2),
+            "library_bf16_reference": {
+                "tflops": round(lib_tflops, 1),
+                "what": "torch.matmul bf16 x[2048,8192] @ W^T[8192,8192] (hipBLASLt, bf16 output) on "
+                        "the same GPU in the same run, untimed by the steps",
+            },
         },
         "groups_ms": {kind: round(group_ms[kind], 5) for kind in kinds},
         "throughput_gbs": {
