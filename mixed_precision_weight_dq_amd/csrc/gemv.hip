@@ -292,7 +292,7 @@ __device__ __forceinline__ void chunk_fma(const uint32_t (&w)[B], const uint32_t
     }
 }
 
-template <int B, int MT, int kRows, int kWaves>
+template <int B, int MT, int kRows, int kWaves, bool kAligned>
 __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
@@ -324,26 +324,54 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
     const int xc = tid * kXPerThread / kChunk;                 // chunk within the slice
     const int xp = (tid * kXPerThread) % kChunk;               // element offset within the chunk
 
+    // K a multiple of 32: every chunk lies inside its row, so codes and x come
+    // in with buffer loads of a fixed count (no per-lane branches, so the
+    // compiler can wait for exactly the loads it needs); past the end of a
+    // row (or for rows m >= M of x) the buffer bounds return zeros
+    BufRef xbuf[MT], wbuf[kRows];
+    if constexpr (kAligned) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            xbuf[m] = uniform_buf(x + (int64_t)(m < M ? m : 0) * K, m < M ? (uint32_t)(K * 2) : 0u);
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) wbuf[r] = uniform_buf(rowp[r], (uint32_t)(row_words * 4));
+    }
+    auto load_x = [&](int64_t s, uint4 (&v)[MT]) {
+        const int64_t k = (s * kSlice + xc) * kChunk + xp;
+        if constexpr (kAligned) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if constexpr (kXPerThread == 8) {
+                    const u32x4v_t d = buf_load_b128(xbuf[m], (uint32_t)(k * 2), 0u);
+                    v[m] = make_uint4(d.x, d.y, d.z, d.w);
+                } else {
+                    const u32x2v_t d = __builtin_amdgcn_raw_buffer_load_b64(
+                        make_rsrc(xbuf[m].base, xbuf[m].bytes), (uint32_t)(k * 2), 0u, 0);
+                    v[m] = make_uint4(d.x, d.y, 0u, 0u);
+                }
+            }
+        } else {
+            stage_x_load<MT, kXPerThread>(x, M, K, k, xvec, v);
+        }
+    };
+    auto load_w = [&](int64_t s, uint32_t (&w)[kRows][B]) {
+        const int64_t c = s * kSlice + lane;
+        if constexpr (kAligned) {
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) buf_load_words<B>(wbuf[r], (uint32_t)(c * B * 4), 0u, w[r]);
+        } else {
+            stage_w_load<B, kRows>(rowp, c, nchunks, row_words, w);
+        }
+    };
+
     float acc[kRows][MT];
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
-    uint32_t wcur[kRows][B], wnxt[kRows][B];
-    uint4 xnxt[MT];
-    stage_x_load<MT, kXPerThread>(x, M, K, (0 * kSlice + xc) * kChunk + xp, xvec, xnxt);
-    stage_x_store<MT, kXPerThread>(&xs[0][0][xc * kXPitch + xp], xnxt);
-    stage_w_load<B, kRows>(rowp, 0 * kSlice + lane, nchunks, row_words, wcur);
-
-    for (int64_t s = 0; s < nslices; ++s) {
-        const bool more = s + 1 < nslices;
-        if (more) {
-            stage_x_load<MT, kXPerThread>(x, M, K, ((s + 1) * kSlice + xc) * kChunk + xp, xvec, xnxt);
-            stage_w_load<B, kRows>(rowp, (s + 1) * kSlice + lane, nchunks, row_words, wnxt);
-        }
-        __syncthreads();
-        const int buf = (int)(s & 1);
+    // slice s: x from LDS buffer s & 1, codes from registers, accumulated into acc
+    auto compute = [&](int buf, int64_t s, const uint32_t (&w)[kRows][B]) {
         if (s * kSlice + lane < nchunks) {
             uint32_t xw[MT][16];
 #pragma unroll
@@ -361,17 +389,57 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
                 if constexpr (B <= 9)
-                    chunk_dot<B, MT>(wcur[r], xw, acc[r]);
+                    chunk_dot<B, MT>(w[r], xw, acc[r]);
                 else
-                    chunk_fma<B, MT>(wcur[r], xw, acc[r]);
+                    chunk_fma<B, MT>(w[r], xw, acc[r]);
             }
         }
-        if (more) {
-            stage_x_store<MT, kXPerThread>(&xs[buf ^ 1][0][xc * kXPitch + xp], xnxt);
+    };
+    uint4 xnxt[MT];
+    if constexpr (kAligned) {
+        // codes in two register sets by slice parity (unrolled by two, so each
+        // set keeps its registers and the waits count exactly); the loads of
+        // slice s+1 are issued unconditionally (past the last slice they read
+        // zeros) so their number is fixed
+        uint32_t w[2][kRows][B];
+        load_x(0, xnxt);
+        load_w(0, w[0]);
+        __builtin_amdgcn_sched_barrier(0);  // both in flight before x goes to LDS
+        stage_x_store<MT, kXPerThread>(&xs[0][0][xc * kXPitch + xp], xnxt);
+        auto step = [&](auto P, int64_t s) {
+            constexpr int p = decltype(P)::value;
+            load_x(s + 1, xnxt);
+            load_w(s + 1, w[p ^ 1]);
+            __syncthreads();
+            compute(p, s, w[p]);
+            stage_x_store<MT, kXPerThread>(&xs[p ^ 1][0][xc * kXPitch + xp], xnxt);
+        };
+        int64_t s = 0;
+        for (; s + 2 <= nslices; s += 2) {
+            step(std::integral_constant<int, 0>{}, s);
+            step(std::integral_constant<int, 1>{}, s + 1);
+        }
+        if (s < nslices) step(std::integral_constant<int, 0>{}, s);
+    } else {
+        uint32_t wcur[kRows][B], wnxt[kRows][B];
+        load_x(0, xnxt);
+        load_w(0, wcur);
+        stage_x_store<MT, kXPerThread>(&xs[0][0][xc * kXPitch + xp], xnxt);
+        for (int64_t s = 0; s < nslices; ++s) {
+            const bool more = s + 1 < nslices;
+            if (more) {
+                load_x(s + 1, xnxt);
+                load_w(s + 1, wnxt);
+            }
+            __syncthreads();
+            compute((int)(s & 1), s, wcur);
+            if (more) {
+                stage_x_store<MT, kXPerThread>(&xs[(s & 1) ^ 1][0][xc * kXPitch + xp], xnxt);
 #pragma unroll
-            for (int r = 0; r < kRows; ++r)
+                for (int r = 0; r < kRows; ++r)
 #pragma unroll
-                for (int i = 0; i < B; ++i) wcur[r][i] = wnxt[r][i];
+                    for (int i = 0; i < B; ++i) wcur[r][i] = wnxt[r][i];
+            }
         }
     }
 
@@ -583,8 +651,12 @@ hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
     const int64_t rw = packed_row_words(K, B);
     const int64_t rows_per_block = kWaves * kRows;
     const int64_t blocks = ceil_div(N, rows_per_block);
-    gemv_lds_kernel<B, MT, kRows, kWaves><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
-        x, (int)M, packed, scales, N, K, rw, y);
+    if (K % kChunk == 0)
+        gemv_lds_kernel<B, MT, kRows, kWaves, true><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
+    else
+        gemv_lds_kernel<B, MT, kRows, kWaves, false><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
     return hipGetLastError();
 }
 
