@@ -12,9 +12,7 @@
 //     loads of one row cover 64*B contiguous words); x is staged in LDS; codes
 //     become signed integers with one XOR per word plus a signed bit-field
 //     extract and meet x in bf16 pair dot products (fp32 FMAs for B >= 10);
-//   * 3 <= M <= 4 (gemv_kernel): the same per-lane decoding with x read per
-//     chunk from the caches;
-//   * 5 <= M <= 16 (gemv_mfma_kernel): codes expanded to exact bf16 operands
+//   * 3 <= M <= 16 (gemv_mfma_kernel): codes expanded to exact bf16 operands
 //     of v_mfma_f32_16x16x32_bf16, so the VALU cost per code no longer grows
 //     with M.
 #include "common.hpp"
@@ -24,96 +22,6 @@
 namespace dq {
 
 namespace {
-
-constexpr int kGemvThreads = 256;
-
-// x[m, 32c .. 32c+32) widened to fp32; zero at k >= K (the padding codes of a
-// row's last chunk are then multiplied by an exact zero).
-__device__ __forceinline__ void load_x_chunk(const uint16_t* __restrict__ xrow, int64_t K, int64_t c,
-                                             bool vec_ok, float* xv)
-{
-    const int64_t k0 = c * kChunk;
-    if (vec_ok && k0 + kChunk <= K) {
-        const uint4* p4 = reinterpret_cast<const uint4*>(xrow + k0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 d = p4[i];
-            const uint32_t u[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xv[i * 8 + e * 2 + 0] = __uint_as_float(u[e] << 16);
-                xv[i * 8 + e * 2 + 1] = __uint_as_float(u[e] & 0xffff0000u);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j)
-            xv[j] = (k0 + j < K) ? bf16_bits_to_float(xrow[k0 + j]) : 0.0f;
-    }
-}
-
-template <int B, int MT, int kRows>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
-    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
-    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * (kGemvThreads / kWave) + wave) * kRows;
-    if (n0 >= N) return;
-    const int64_t nchunks = ceil_div(K, kChunk);
-    const bool vec_ok = (K & 7) == 0;
-
-    float acc[kRows][MT];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-
-    for (int64_t c = lane; c < nchunks; c += kWave) {
-        float qf[kRows][kChunk];
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            uint32_t wd[B];
-            const int64_t n = n0 + r < N ? n0 + r : N - 1;
-            load_chunk_words<B>(packed + n * row_words, c, row_words, wd);
-#pragma unroll
-            for (int i = 0; i < B; ++i) wd[i] ^= code_msb_mask<B>(i);
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) qf[r][j] = (float)chunk_code_signed<B>(wd, j);
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < M) {
-                float xv[kChunk];
-                load_x_chunk(x + (int64_t)m * K, K, c, vec_ok, xv);
-#pragma unroll
-                for (int r = 0; r < kRows; ++r)
-#pragma unroll
-                    for (int j = 0; j < kChunk; ++j) acc[r][m] = fmaf(xv[j], qf[r][j], acc[r][m]);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const int64_t n = n0 + r;
-            if (n < N) {
-                const float s = scales[n];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    if (m < M) y[(int64_t)m * N + n] = s * acc[r][m];
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // M <= 2: x is staged per K-slice of 64 chunks (2048 codes) in LDS by the whole
@@ -463,11 +371,11 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3 <= M <= 16 on the matrix cores (v_mfma_f32_16x16x32_bf16): with 16 rows of
-// x the VALU dot products would cost 8 instructions per code, so the codes
-// are expanded once into exact bf16 operands (2-3 instructions per code) and
-// the products run on the MFMA units, leaving the kernel bound by the bytes of
-// the packed weights again.
+// 3 <= M <= 16 on the matrix cores (v_mfma_f32_16x16x32_bf16): with up to 16
+// rows of x the VALU dot products would cost up to 8 instructions per code,
+// so the codes are expanded once into exact bf16 operands (2-3 instructions
+// per code) and the products run on the MFMA units, leaving the kernel bound
+// by the bytes of the packed weights again.
 //
 // A workgroup owns 16 kNT weight rows; its 4 waves take the 128-code K steps
 // w, w+4, w+8, ... (together they stream each row's consecutive 512-code
@@ -480,7 +388,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 // step is computed.
 constexpr int kGemvMfmaWaves = 4;
 
-template <int B, int kNT, int kDepth>
+template <int B, int kNT, int kDepth, bool kAligned>
 __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
@@ -510,11 +418,36 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const uint16_t* xr = x + (int64_t)(xrow ? c : 0) * K;
     const bool xvec = (K & 7) == 0;
 
+    // K a multiple of 32: fixed-count buffer loads (no per-lane branches, so
+    // the waits cover only the loads they need).  The codes of the workgroup's
+    // rows are one buffer (rows past N read zeros); x lanes past K or with
+    // rows c >= M get an offset past the end of x and read zeros, so the
+    // padding codes past K meet exact zeros.
+    const int64_t nrows = N - n0 < 16 * kNT ? N - n0 : 16 * kNT;
+    BufRef wb{}, xb{};
+    if constexpr (kAligned) {
+        wb = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
+        xb = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+    }
+    constexpr uint32_t kOutside = 0xfffff000u;
+
     uint32_t w[kStages][kNT][B];
     uint4 xa[kStages][4];
     auto load = [&](auto P, int64_t ks) {
         constexpr int p = decltype(P)::value;
         const int64_t ch = 4 * ks + g;
+        if constexpr (kAligned) {
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+                buf_load_words<B>(wb, (uint32_t)((16 * j + c) * row_words * 4 + ch * B * 4), 0u, w[p][j]);
+            const uint32_t xo = (xrow && ch < nchunks) ? (uint32_t)((c * K + ch * kChunk) * 2) : kOutside;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4v_t d = buf_load_b128(xb, xo + 16 * i, 0u);
+                xa[p][i] = make_uint4(d.x, d.y, d.z, d.w);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             if (ks < nsteps && ch < nchunks) {
@@ -613,23 +546,33 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     }
 }
 
-#ifndef DQ_GEMV_MFMA_NT
-#define DQ_GEMV_MFMA_NT 1
-#endif
 #ifndef DQ_GEMV_MFMA_DEPTH
 #define DQ_GEMV_MFMA_DEPTH 1
 #endif
 
+template <int B, int kNT>
+hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* packed,
+                               const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+{
+    const int64_t rw = packed_row_words(K, B);
+    const dim3 grid((unsigned)ceil_div(N, 16 * kNT)), block(kGemvMfmaWaves * kWave);
+    if (K % kChunk == 0)
+        gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, true><<<grid, block, 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
+    else
+        gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, false><<<grid, block, 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
+    return hipGetLastError();
+}
+
+// 32 rows per workgroup (x fragments shared by two row tiles) above 2^24
+// weights, where there are workgroups enough for every CU; 16 rows below
 template <int B>
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
 {
-    constexpr int kNT = DQ_GEMV_MFMA_NT;
-    const int64_t rw = packed_row_words(K, B);
-    gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH>
-        <<<dim3((unsigned)ceil_div(N, 16 * kNT)), dim3(kGemvMfmaWaves * kWave), 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
-    return hipGetLastError();
+    if (N * K > (1LL << 24)) return launch_gemv_mfma_nt<B, 2>(x, M, packed, scales, N, K, y, stream);
+    return launch_gemv_mfma_nt<B, 1>(x, M, packed, scales, N, K, y, stream);
 }
 
 #ifndef DQ_GEMV_ROWS_NARROW
@@ -660,26 +603,12 @@ hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
     return hipGetLastError();
 }
 
-template <int B, int MT>
-hipError_t launch_gemv_bm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                          int64_t N, int64_t K, float* y, hipStream_t stream)
-{
-    constexpr int kRows = 2;
-    const int64_t rw = packed_row_words(K, B);
-    const int64_t rows_per_block = (kGemvThreads / kWave) * kRows;
-    const int64_t blocks = ceil_div(N, rows_per_block);
-    gemv_kernel<B, MT, kRows><<<dim3((unsigned)blocks), dim3(kGemvThreads), 0, stream>>>(
-        x, (int)M, packed, scales, N, K, rw, y);
-    return hipGetLastError();
-}
-
 template <int B>
 hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                          int64_t N, int64_t K, float* y, hipStream_t stream)
 {
     if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, stream);
     if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, stream);
-    if (M <= 4) return launch_gemv_bm<B, 4>(x, M, packed, scales, N, K, y, stream);
     return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, stream);
 }
 
