@@ -101,6 +101,25 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
     }
 }
 
+// Stores B consecutive words with as few instructions as possible (the
+// counterpart of load_words).
+template <int B>
+__device__ __forceinline__ void store_words(uint32_t* __restrict__ p, const uint32_t* w)
+{
+#pragma unroll
+    for (int i = 0; i + 4 <= B; i += 4)
+        *reinterpret_cast<u32x4_a4*>(p + i) = (u32x4_a4){w[i], w[i + 1], w[i + 2], w[i + 3]};
+    constexpr int r = B & 3;
+    constexpr int o = B - r;
+    if (r == 3) {
+        *reinterpret_cast<u32x3_a4*>(p + o) = (u32x3_a4){w[o], w[o + 1], w[o + 2]};
+    } else if (r == 2) {
+        *reinterpret_cast<u32x2_a4*>(p + o) = (u32x2_a4){w[o], w[o + 1]};
+    } else if (r == 1) {
+        p[o] = w[o];
+    }
+}
+
 // Loads the B words of chunk c of a packed row.  Words at or beyond row_words
 // (possible only in a row's last chunk) read as zero.
 template <int B>

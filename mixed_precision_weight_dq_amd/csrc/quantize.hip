@@ -21,14 +21,14 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
-template <bool BF16>
+template <bool BF16, bool kAligned>
 __device__ __forceinline__ void load_row_chunk(const void* __restrict__ w, int64_t row_off, int64_t K,
                                                int64_t c, bool vec_ok, float* v)
 {
     const int64_t k0 = c * kChunk;
     if (BF16) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + row_off + k0;
-        if (vec_ok && k0 + kChunk <= K) {
+        if (kAligned || (vec_ok && k0 + kChunk <= K)) {
             const uint4* p4 = reinterpret_cast<const uint4*>(p);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -47,7 +47,7 @@ __device__ __forceinline__ void load_row_chunk(const void* __restrict__ w, int64
         }
     } else {
         const float* p = reinterpret_cast<const float*>(w) + row_off + k0;
-        if (vec_ok && k0 + kChunk <= K) {
+        if (kAligned || (vec_ok && k0 + kChunk <= K)) {
             const float4* p4 = reinterpret_cast<const float4*>(p);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -107,8 +107,7 @@ __device__ __forceinline__ void store_chunk(uint32_t* __restrict__ prow, int64_t
 {
     const int64_t base = c * B;
     if (base + B <= row_words) {
-#pragma unroll
-        for (int i = 0; i < B; ++i) prow[base + i] = out[i];
+        store_words<B>(prow + base, out);
     } else {
 #pragma unroll
         for (int i = 0; i < B; ++i)
@@ -117,9 +116,10 @@ __device__ __forceinline__ void store_chunk(uint32_t* __restrict__ prow, int64_t
 }
 
 // One workgroup of 64..256 threads per row (enough for one chunk per thread
-// when K <= 8192).  Each thread keeps its first chunk in registers between the
+// when K <= 8192).  kAligned (K a multiple of 32): every chunk is whole, so
+// loads take the 16-byte vector path without per-lane bounds checks.  Each thread keeps its first chunk in registers between the
 // max pass and the quantize pass; further chunks (long rows) are read again.
-template <int B, bool BF16>
+template <int B, bool BF16, bool kAligned>
 __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t K, int64_t row_words, uint32_t* __restrict__ packed,
     float* __restrict__ scales)
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     float v0[kChunk];
     uint32_t amax = 0;
     if (tid < nchunks) {
-        load_row_chunk<BF16>(w, row_off, K, tid, vec_ok, v0);
+        load_row_chunk<BF16, kAligned>(w, row_off, K, tid, vec_ok, v0);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const uint32_t m = __float_as_uint(v0[j]) & 0x7fffffffu;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     }
     for (int64_t c = tid + threads; c < nchunks; c += threads) {
         float v[kChunk];
-        load_row_chunk<BF16>(w, row_off, K, c, vec_ok, v);
+        load_row_chunk<BF16, kAligned>(w, row_off, K, c, vec_ok, v);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const uint32_t m = __float_as_uint(v[j]) & 0x7fffffffu;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     }
     for (int64_t c = tid + threads; c < nchunks; c += threads) {
         float v[kChunk];
-        load_row_chunk<BF16>(w, row_off, K, c, vec_ok, v);
+        load_row_chunk<BF16, kAligned>(w, row_off, K, c, vec_ok, v);
         uint32_t out[B];
         quantize_chunk<B>(v, s, r, margin, zero_codes, c * kChunk, K, out);
         store_chunk<B>(prow, c, row_words, out);
@@ -260,12 +260,16 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
     const int64_t nchunks = ceil_div(K, kChunk);
     const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
                                                        : ceil_div(nchunks, kWave) * kWave);
-    if (bf16)
-        quantize_pack_kernel<B, true><<<dim3((unsigned)N), dim3(threads), 0, stream>>>(
-            w, K, rw, packed, scales);
+    const dim3 grid((unsigned)N), block(threads);
+    const bool aligned = K % kChunk == 0;
+    if (bf16 && aligned)
+        quantize_pack_kernel<B, true, true><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+    else if (bf16)
+        quantize_pack_kernel<B, true, false><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+    else if (aligned)
+        quantize_pack_kernel<B, false, true><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
     else
-        quantize_pack_kernel<B, false><<<dim3((unsigned)N), dim3(threads), 0, stream>>>(
-            w, K, rw, packed, scales);
+        quantize_pack_kernel<B, false, false><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
     return hipGetLastError();
 }
 

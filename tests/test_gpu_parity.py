@@ -79,7 +79,7 @@ def test_quantize_pack_bitexact_f32(bits):
 
 @pytest.mark.parametrize("bits", range(2, 16))
 def test_quantize_special_rows(bits):
-    for K in (1, 7, 33, 300):
+    for K in (1, 7, 33, 64, 300, 512):
         rows = special_rows(K, bits)
         assert_quantize_parity(rows, bits)
         bf = workload.bf16_from_f32(rows)
