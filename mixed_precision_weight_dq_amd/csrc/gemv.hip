@@ -585,6 +585,131 @@ hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed
 #define DQ_GEMV_WAVES 8
 #endif
 
+// M <= 2, K a multiple of 32 and x small enough to sit in LDS whole
+// (MT * K / 32 chunk slots of 80 B): x is staged once per workgroup (kR
+// 16-byte pieces per thread, a fixed count; threads past the last piece
+// repeat it), so the slice loop has no barriers, and each wave keeps the codes
+// of up to three slices in flight (register stages by slice % 3, unrolled by
+// three).  Loads: x first, then the codes of slices 0 and 1, then x to LDS
+// (waiting only for x), then the slice loop.
+constexpr int kXResMax = 48 * 1024;
+
+template <int B, int MT, int kWaves, int kR>
+__global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+    constexpr int kThreads = kWaves * kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t nchunks = K / kChunk;
+    const int64_t nslices = ceil_div(nchunks, kSlice);
+    const BufRef wbuf = uniform_buf(packed + (n < N ? n : N - 1) * row_words, (uint32_t)(row_words * 4));
+    const BufRef xall = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+
+    // x piece p (8 elements) = piece p % 4 of chunk slot p / 4 (slot = m * nchunks + chunk)
+    const int pieces = (int)(MT * nchunks * 4);
+    uint4 xv[kR];
+    int xdst[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int p = min(tid + r * kThreads, pieces - 1);
+        const int slot = p >> 2;
+        xdst[r] = slot * kXPitch + (p & 3) * 8;
+        // slot m * nchunks + c holds x[m][32 c ..]: its elements start at element
+        // 32 * slot of the M x K row-major x (rows m >= M lie past the buffer: zeros)
+        const u32x4v_t d = buf_load_b128(xall, (uint32_t)(slot * kChunk * 2 + (p & 3) * 16), 0u);
+        xv[r] = make_uint4(d.x, d.y, d.z, d.w);
+    }
+    uint32_t w[3][B];
+    auto load_w = [&](auto S, int64_t sl) {  // past the last slice: zeros
+        buf_load_words<B>(wbuf, (uint32_t)((sl * kSlice + lane) * B * 4), 0u, w[decltype(S)::value]);
+    };
+    load_w(std::integral_constant<int, 0>{}, 0);
+    load_w(std::integral_constant<int, 1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) *reinterpret_cast<uint4*>(xs_dyn + xdst[r]) = xv[r];
+    __syncthreads();
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    auto step = [&](auto S, int64_t sl) {
+        constexpr int st = decltype(S)::value;
+        load_w(std::integral_constant<int, (st + 2) % 3>{}, sl + 2);
+        const int64_t c = sl * kSlice + lane;
+        if (c < nchunks) {
+            uint32_t xw[MT][16];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint4* src = reinterpret_cast<const uint4*>(xs_dyn + (m * nchunks + c) * kXPitch);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 d = src[i];
+                    xw[m][4 * i + 0] = d.x;
+                    xw[m][4 * i + 1] = d.y;
+                    xw[m][4 * i + 2] = d.z;
+                    xw[m][4 * i + 3] = d.w;
+                }
+            }
+            if constexpr (B <= 9)
+                chunk_dot<B, MT>(w[st], xw, acc);
+            else
+                chunk_fma<B, MT>(w[st], xw, acc);
+        }
+    };
+    int64_t sl = 0;
+    for (; sl + 3 <= nslices; sl += 3) {
+        step(std::integral_constant<int, 0>{}, sl);
+        step(std::integral_constant<int, 1>{}, sl + 1);
+        step(std::integral_constant<int, 2>{}, sl + 2);
+    }
+    if (sl < nslices) step(std::integral_constant<int, 0>{}, sl);
+    if (sl + 1 < nslices) step(std::integral_constant<int, 1>{}, sl + 1);
+
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = wave_sum(acc[m]);
+    if (lane == 0 && n < N) {
+        constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
+        const float s = scales[n];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < M) y[(int64_t)m * N + n] = s * (acc[m] * kUnscale);
+    }
+}
+
+#ifndef DQ_GEMV_XRES_WAVES
+#define DQ_GEMV_XRES_WAVES 4
+#endif
+
+template <int B, int MT>
+hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed,
+                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+{
+    constexpr int kWaves = DQ_GEMV_XRES_WAVES;
+    constexpr int kThreads = kWaves * kWave;
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t nchunks = K / kChunk;
+    const size_t lds = (size_t)MT * nchunks * kXPitch * 2;
+    const int64_t pieces = MT * nchunks * 4;
+    const dim3 grid((unsigned)ceil_div(N, kWaves)), block(kThreads);
+#define DQ_XRES(R) gemv_xres_kernel<B, MT, kWaves, R><<<grid, block, lds, stream>>>(x, (int)M, packed, scales, N, K, rw, y)
+    // pieces per thread: every piece of x must be covered
+    static_assert(10 * kThreads >= kXResMax / (kXPitch * 2) * 4, "x staging covers the largest x");
+    if (pieces <= kThreads) DQ_XRES(1);
+    else if (pieces <= 2 * kThreads) DQ_XRES(2);
+    else if (pieces <= 3 * kThreads) DQ_XRES(3);
+    else if (pieces <= 5 * kThreads) DQ_XRES(5);
+    else DQ_XRES(10);
+#undef DQ_XRES
+    return hipGetLastError();
+}
+
 template <int B, int MT>
 hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
@@ -607,6 +732,15 @@ template <int B>
 hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                          int64_t N, int64_t K, float* y, hipStream_t stream)
 {
+#ifndef DQ_GEMV_NO_XRES
+    // x resident in LDS when it fits, up to 2^27 weights (beyond, the sliced
+    // kernel's eight waves per workgroup stream slightly faster)
+    if (M <= 2 && K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax &&
+        N * K <= (1LL << 27)) {
+        if (M <= 1) return launch_gemv_xres<B, 1>(x, M, packed, scales, N, K, y, stream);
+        return launch_gemv_xres<B, 2>(x, M, packed, scales, N, K, y, stream);
+    }
+#endif
     if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, stream);
     if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, stream);
     return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, stream);

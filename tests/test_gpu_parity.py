@@ -128,7 +128,7 @@ def assert_matmul_parity(kind: str, M: int, N: int, K: int, bits: int, seed: int
             kind, M, N, K, bits, m, n, y[m, n], y_ref[m, n], bound[m, n], int((~ok).sum())))
 
 
-GEMV_SHAPES = [(1, 1), (37, 1000), (300, 4096 + 37), (8, 17408)]
+GEMV_SHAPES = [(1, 1), (37, 1000), (300, 4096 + 37), (8, 17408), (40, 6144), (70, 2048)]
 
 
 @pytest.mark.parametrize("bits", range(2, 16))
