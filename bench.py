@@ -60,7 +60,10 @@ def kernel_source_digest() -> str:
     csrc = os.path.join(ROOT, "mixed_precision_weight_dq_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f in ("gemv.hip", "common.hpp"):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            # code only: whole-line comments do not change the kernel
+            for line in open(os.path.join(csrc, f), "rb"):
+                if not line.lstrip().startswith(b"//"):
+                    h.update(line)
     return h.hexdigest()[:16]
 
 

@@ -7,14 +7,16 @@
 // Quantization tutorial's closing remark on prefill vs decode puts it).
 //
 // Three kernels by M (the row scale always multiplies the reduced sum once):
-//   * M <= 2 (gemv_lds_kernel): a wave owns a row; lane l walks the chunks
+//   * M <= 2 (gemv_xres_kernel when K is a multiple of 32 and x fits in LDS
+//     whole, else gemv_lds_kernel): a wave owns a row; lane l walks the chunks
 //     l, l+64, ... of it (a chunk = 32 codes = B whole words, so a wave's
-//     loads of one row cover 64*B contiguous words); x is staged in LDS; codes
+//     loads of one row cover 64*B contiguous words); x sits in LDS; codes
 //     become signed integers with one XOR per word plus a signed bit-field
 //     extract and meet x in bf16 pair dot products (fp32 FMAs for B >= 10);
-//   * 3 <= M <= 16 (gemv_mfma_kernel): codes expanded to exact bf16 operands
-//     of v_mfma_f32_16x16x32_bf16, so the VALU cost per code no longer grows
-//     with M.
+//   * 3 <= M <= 16 (gemv_mfma_xlds_kernel when K is a multiple of 32, x
+//     copied through LDS; else gemv_mfma_kernel): codes expanded to exact
+//     bf16 operands of v_mfma_f32_16x16x32_bf16, so the VALU cost per code no
+//     longer grows with M.
 #include "common.hpp"
 #include "launch.hpp"
 #include "gemm_tiles.hpp"
@@ -385,10 +387,14 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 // 8g .. 8g+7 of the 16x16x32 shape); the A operand of lane l is x[c][32 (4 ks
 // + g) + 8 t .. + 8], so both sides use the same order of k.  Rows m >= M of x
 // are zero.  The codes and x of the next kDepth steps are loaded before this
-// step is computed.
-constexpr int kGemvMfmaWaves = 4;
+// step is computed.  This kernel serves K not a multiple of 32 (per-lane
+// guarded loads); gemv_mfma_xlds_kernel below serves the rest.
+#ifndef DQ_GEMV_MFMA_WAVES
+#define DQ_GEMV_MFMA_WAVES 4
+#endif
+constexpr int kGemvMfmaWaves = DQ_GEMV_MFMA_WAVES;
 
-template <int B, int kNT, int kDepth, bool kAligned>
+template <int B, int kNT, int kDepth>
 __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
@@ -398,6 +404,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     typedef float f32x4m_t __attribute__((ext_vector_type(4)));
     constexpr bool kSplit = B >= 10;
     constexpr int kStages = kDepth + 1;
+    static_assert(kDepth >= 1 && kDepth <= 3, "one to three steps ahead");
     __shared__ float red[kGemvMfmaWaves - 1][kNT][4][kWave];
 
     const int tid = threadIdx.x;
@@ -418,36 +425,11 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const uint16_t* xr = x + (int64_t)(xrow ? c : 0) * K;
     const bool xvec = (K & 7) == 0;
 
-    // K a multiple of 32: fixed-count buffer loads (no per-lane branches, so
-    // the waits cover only the loads they need).  The codes of the workgroup's
-    // rows are one buffer (rows past N read zeros); x lanes past K or with
-    // rows c >= M get an offset past the end of x and read zeros, so the
-    // padding codes past K meet exact zeros.
-    const int64_t nrows = N - n0 < 16 * kNT ? N - n0 : 16 * kNT;
-    BufRef wb{}, xb{};
-    if constexpr (kAligned) {
-        wb = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
-        xb = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
-    }
-    constexpr uint32_t kOutside = 0xfffff000u;
-
     uint32_t w[kStages][kNT][B];
     uint4 xa[kStages][4];
     auto load = [&](auto P, int64_t ks) {
         constexpr int p = decltype(P)::value;
         const int64_t ch = 4 * ks + g;
-        if constexpr (kAligned) {
-#pragma unroll
-            for (int j = 0; j < kNT; ++j)
-                buf_load_words<B>(wb, (uint32_t)((16 * j + c) * row_words * 4 + ch * B * 4), 0u, w[p][j]);
-            const uint32_t xo = (xrow && ch < nchunks) ? (uint32_t)((c * K + ch * kChunk) * 2) : kOutside;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4v_t d = buf_load_b128(xb, xo + 16 * i, 0u);
-                xa[p][i] = make_uint4(d.x, d.y, d.z, d.w);
-            }
-            return;
-        }
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             if (ks < nsteps && ch < nchunks) {
@@ -494,30 +476,30 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
             }
         }
     };
+    // Stage i of the register ring holds step ks + i kW.  Each step's loads
+    // are pinned ahead of the computation of the step kDepth before it, so
+    // the wait for a stage leaves the later stages' loads in flight.
     constexpr int64_t kW = kGemvMfmaWaves;
     int64_t ks = wave;
     load(std::integral_constant<int, 0>{}, ks);
     if constexpr (kDepth > 1) load(std::integral_constant<int, 1>{}, ks + kW);
-    if constexpr (kDepth == 1) {
-        for (; ks + kW < nsteps; ks += 2 * kW) {
-            load(std::integral_constant<int, 1>{}, ks + kW);
-            compute(std::integral_constant<int, 0>{});
-            load(std::integral_constant<int, 0>{}, ks + 2 * kW);
-            compute(std::integral_constant<int, 1>{});
-        }
-        if (ks < nsteps) compute(std::integral_constant<int, 0>{});
-    } else {
-        for (; ks + 2 * kW < nsteps; ks += 3 * kW) {
-            load(std::integral_constant<int, 2>{}, ks + 2 * kW);
-            compute(std::integral_constant<int, 0>{});
-            load(std::integral_constant<int, 0>{}, ks + 3 * kW);
-            compute(std::integral_constant<int, 1>{});
-            load(std::integral_constant<int, 1>{}, ks + 4 * kW);
-            compute(std::integral_constant<int, 2>{});
-        }
-        if (ks < nsteps) compute(std::integral_constant<int, 0>{});
-        if (ks + kW < nsteps) compute(std::integral_constant<int, 1>{});
+    if constexpr (kDepth > 2) load(std::integral_constant<int, 2>{}, ks + 2 * kW);
+    __builtin_amdgcn_sched_barrier(0);
+    auto stage = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        load(std::integral_constant<int, (i + kDepth) % kStages>{}, ks + (i + kDepth) * kW);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(I);
+    };
+    for (; ks + kDepth * kW < nsteps; ks += kStages * kW) {
+        stage(std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 1>{});
+        if constexpr (kStages > 2) stage(std::integral_constant<int, 2>{});
+        if constexpr (kStages > 3) stage(std::integral_constant<int, 3>{});
     }
+    if (ks < nsteps) compute(std::integral_constant<int, 0>{});
+    if constexpr (kDepth > 1) if (ks + kW < nsteps) compute(std::integral_constant<int, 1>{});
+    if constexpr (kDepth > 2) if (ks + 2 * kW < nsteps) compute(std::integral_constant<int, 2>{});
 
     // lane (g, c) holds rows 4 g + r of column c; waves 1..3 hand theirs to wave 0
     if (wave > 0) {
@@ -546,8 +528,180 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 3 <= M <= 16 and K a multiple of 32: gemv_mfma_kernel with x taken through
+// LDS.  Loaded into registers, x costs as much as the code stream: each lane
+// needs 64 bytes of one row, so every 16-byte load spreads its 64 lanes over
+// 64 cache lines, and lanes of rows past M load too.  Here each wave copies
+// the x of its own steps, rows below kMR only (4 rows of 256 bytes per
+// instruction, each row's 16-byte pieces in one run), straight into a ring of
+// LDS stages of its own (buffer_load ... lds) and reads the A operands back
+// with ds_read_b128.  Piece p of row i sits at slot 16 i + (p ^ i), so the 16
+// lanes of a read that take the same piece of 16 rows hit distinct banks.
+// The ring is private to the wave, so the loop has no barriers; an explicit
+// vmcnt wait before each step covers the LDS copies, which the compiler does
+// not track.  x pieces past K (the last step of a K not a multiple of 128)
+// and rows past M read an offset outside the x buffer, which loads zeros.
+template <int B>
+constexpr int words_loads() { return B / 4 + (B % 4 != 0 ? 1 : 0); }
+
+template <int B, int kNT, int kDepth, int kMR>
+__global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y)
+{
+    typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
+    typedef float f32x4m_t __attribute__((ext_vector_type(4)));
+    constexpr bool kSplit = B >= 10;
+    constexpr int kStages = kDepth + 1;
+    constexpr int kXCopies = kMR / 4;
+    constexpr int kPerStage = kNT * words_loads<B>() + kXCopies;
+    constexpr int kSlots = kMR * 16;  // 16-byte x pieces of one step
+    static_assert(kDepth >= 1 && kDepth <= 3, "one to three steps ahead");
+    static_assert(kMR == 8 || kMR == 16, "x rows staged: 8 or 16");
+    static_assert(kDepth * kPerStage < 64, "vmcnt holds at most 63");
+    // one LDS object per stage, so each copy and read names its stage
+    __shared__ __attribute__((aligned(16))) uint4 xs0[kGemvMfmaWaves][kSlots];
+    __shared__ __attribute__((aligned(16))) uint4 xs1[kGemvMfmaWaves][kSlots];
+    __shared__ __attribute__((aligned(16))) uint4 xs2[kStages > 2 ? kGemvMfmaWaves : 1][kStages > 2 ? kSlots : 1];
+    __shared__ __attribute__((aligned(16))) uint4 xs3[kStages > 3 ? kGemvMfmaWaves : 1][kStages > 3 ? kSlots : 1];
+    __shared__ float red[kGemvMfmaWaves - 1][kNT][4][kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    auto ring = [&](auto S) -> uint4* {
+        constexpr int st = decltype(S)::value;
+        if constexpr (st == 0) return xs0[wave];
+        else if constexpr (st == 1) return xs1[wave];
+        else if constexpr (st == 2) return xs2[kStages > 2 ? wave : 0];
+        else return xs3[kStages > 3 ? wave : 0];
+    };
+
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * kNT;
+    const int64_t nchunks = K / kChunk;
+    const int64_t nsteps = ceil_div(nchunks, 4);
+    const int64_t nrows = N - n0 < 16 * kNT ? N - n0 : 16 * kNT;
+    const BufRef wb = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
+    const BufRef xb = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+    constexpr uint32_t kOutside = 0xfffff000u;
+
+    // copy instruction q: lane l fills slot 64 q + l = row r, position l % 16,
+    // which holds piece p = (l % 16) ^ r of that row (chunk 4 ks + p / 4)
+    uint32_t xbase[kXCopies];
+    int xchunk[kXCopies];
+#pragma unroll
+    for (int q = 0; q < kXCopies; ++q) {
+        const int r = 4 * q + (lane >> 4);
+        const int pc = (lane & 15) ^ r;
+        xbase[q] = r < M ? (uint32_t)(r * K * 2 + 16 * pc) : kOutside;
+        xchunk[q] = pc >> 2;
+    }
+    // A operand of substep t: row c (rows past kMR repeat rows below it; their
+    // sums land in output rows that are never stored), piece 4 g + t
+    const int ar = c & (kMR - 1);
+    int aslot[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aslot[t] = 16 * ar + ((4 * g + t) ^ ar);
+
+    uint32_t w[kStages][kNT][B];
+    auto load = [&](auto P, int64_t ks) {
+        constexpr int p = decltype(P)::value;
+        const int64_t ch = 4 * ks + g;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+            buf_load_words<B>(wb, (uint32_t)((16 * j + c) * row_words * 4 + ch * B * 4), 0u, w[p][j]);
+        uint4* dst = ring(P);
+#pragma unroll
+        for (int q = 0; q < kXCopies; ++q) {
+            const bool in = xbase[q] != kOutside && 4 * ks + xchunk[q] < nchunks;
+            buf_load_lds16(xb, dst + 64 * q, in ? xbase[q] + (uint32_t)(ks * 256) : kOutside, 0u);
+        }
+    };
+    f32x4m_t acc[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
+    // vmcnt(n) with expcnt and lgkmcnt left at their maxima
+    auto compute = [&](auto P, auto Wait) {
+        constexpr int p = decltype(P)::value;
+        constexpr int n = decltype(Wait)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+        const uint4* src = ring(P);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8m_t a = __builtin_bit_cast(bf16x8m_t, src[aslot[t]]);
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                bf16x8_t bh, bl;
+                expand8<B>(w[p][j], t, bh, bl);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
+                if constexpr (kSplit) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
+            }
+        }
+    };
+
+    // Stage i of the ring holds step ks + i kW; each step's loads are issued
+    // before the computation of the step kDepth before it.
+    constexpr int64_t kW = kGemvMfmaWaves;
+    int64_t ks = wave;
+    load(std::integral_constant<int, 0>{}, ks);
+    if constexpr (kDepth > 1) load(std::integral_constant<int, 1>{}, ks + kW);
+    if constexpr (kDepth > 2) load(std::integral_constant<int, 2>{}, ks + 2 * kW);
+    __builtin_amdgcn_sched_barrier(0);
+    auto stage = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        load(std::integral_constant<int, (i + kDepth) % kStages>{}, ks + (i + kDepth) * kW);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(I, std::integral_constant<int, kDepth * kPerStage>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; ks + kDepth * kW < nsteps; ks += kStages * kW) {
+        stage(std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 1>{});
+        if constexpr (kStages > 2) stage(std::integral_constant<int, 2>{});
+        if constexpr (kStages > 3) stage(std::integral_constant<int, 3>{});
+    }
+    // the last loads in flight are those of stages 0 .. kDepth-1, in order
+    if (ks < nsteps) compute(std::integral_constant<int, 0>{}, std::integral_constant<int, (kDepth - 1) * kPerStage>{});
+    if constexpr (kDepth > 1)
+        if (ks + kW < nsteps) compute(std::integral_constant<int, 1>{}, std::integral_constant<int, (kDepth - 2) * kPerStage>{});
+    if constexpr (kDepth > 2)
+        if (ks + 2 * kW < nsteps) compute(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
+    // copies past the last step may still be in flight: drain them before
+    // the workgroup's LDS can be handed to another workgroup
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][j][r][lane] = acc[j][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr float kUnscale = 1.0f / expand8_scale<B>();
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            const int64_t n = n0 + 16 * j + c;
+            if (n >= N) continue;
+            const float s = scales[n];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = acc[j][r];
+#pragma unroll
+                for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
+                const int m = 4 * g + r;
+                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
+            }
+        }
+    }
+}
+
 #ifndef DQ_GEMV_MFMA_DEPTH
-#define DQ_GEMV_MFMA_DEPTH 1
+#define DQ_GEMV_MFMA_DEPTH 2
 #endif
 
 template <int B, int kNT>
@@ -556,11 +710,14 @@ hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* pac
 {
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 16 * kNT)), block(kGemvMfmaWaves * kWave);
-    if (K % kChunk == 0)
-        gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, true><<<grid, block, 0, stream>>>(
+    if (K % kChunk == 0 && M <= 8)
+        gemv_mfma_xlds_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, 8><<<grid, block, 0, stream>>>(
+            x, (int)M, packed, scales, N, K, rw, y);
+    else if (K % kChunk == 0)
+        gemv_mfma_xlds_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, 16><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y);
     else
-        gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, false><<<grid, block, 0, stream>>>(
+        gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y);
     return hipGetLastError();
 }
@@ -571,7 +728,10 @@ template <int B>
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
 {
-    if (N * K > (1LL << 24)) return launch_gemv_mfma_nt<B, 2>(x, M, packed, scales, N, K, y, stream);
+#ifndef DQ_GEMV_MFMA_NT2_MIN
+#define DQ_GEMV_MFMA_NT2_MIN (1LL << 24)
+#endif
+    if (N * K > DQ_GEMV_MFMA_NT2_MIN) return launch_gemv_mfma_nt<B, 2>(x, M, packed, scales, N, K, y, stream);
     return launch_gemv_mfma_nt<B, 1>(x, M, packed, scales, N, K, y, stream);
 }
 
