@@ -123,6 +123,56 @@ def stack_context(torch, dq, workload, dev, stream):
     return out
 
 
+def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: int):
+    """Context for the GEMV figure, outside the timed steps: the five decode
+    GEMV launches against a plain streaming read (dq_stream_read) of the same
+    five packed buffers, each group timed after the same cache-flushing GEMM;
+    plus the read rate of a 1 GiB buffer.  The read's share count is the best
+    of three."""
+    nbytes = sum(b.numel() * b.element_size() for b in read_bufs)
+
+    def timed(group):
+        ts = []
+        for _ in range(reps):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            group()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    parts = {}
+    for per in (256, 512, 1024):
+        outs = [torch.empty((max(1, min(65536, b.numel() * b.element_size() // 16 // per)),),
+                            dtype=torch.int32, device=dev) for b in read_bufs]
+        parts[per] = (outs, timed(lambda: [dq.stream_read(b, o.shape[0], o) for b, o in zip(read_bufs, outs)]))
+    per, (outs, read_ms) = min(parts.items(), key=lambda kv: kv[1][1])
+    gemv_ms = timed(gemv_group)
+    big = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
+    big_out = torch.empty((65536,), dtype=torch.int32, device=dev)
+    dq.stream_read(big, 65536, big_out)
+    torch.cuda.synchronize()
+    big_ms = timed(lambda: dq.stream_read(big, 65536, big_out))
+    del big
+    n = len(read_bufs)
+    read_gbs = nbytes / (read_ms * 1e-3) / 1e9
+    gemv_gbs = nbytes / (gemv_ms * 1e-3) / 1e9
+    return {
+        "what": "plain streaming read (dq_stream_read) of the five packed 4096x4096 buffers, back "
+                "to back, vs the five GEMV launches on them; each group after the same b=6 prefill "
+                "GEMM, median of %d; bytes = packed buffers; context, not the value" % reps,
+        "read_gbs": round(read_gbs, 1),
+        "read_per_launch_us": round(read_ms / n * 1e3, 3),
+        "read_shares": [o.shape[0] for o in outs],
+        "gemv_gbs": round(gemv_gbs, 1),
+        "gemv_per_launch_us": round(gemv_ms / n * 1e3, 3),
+        "gemv_frac_of_read": round(gemv_gbs / read_gbs, 4),
+        "read_1gib_gbs": round((1 << 30) / (big_ms * 1e-3) / 1e9, 1),
+    }
+
+
 def cpu_baseline(decode_w, x1, target_s: float):
     """The oracle's fp64 GEMV (unpack bit by bit + dot product) over the decode
     matrices, repeated until about target_s seconds of CPU time."""
@@ -339,6 +389,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = src.numel() * 4
+    b6 = PREFILL["bits"][1]
+    out["roofline"]["attainable_read"] = attainable_read(
+        torch, dq, dev, stream,
+        lambda: [dq.gemv(X1, P2[b], S2[b], DECODE["K"], b, Y1[b]) for b in W2],
+        [P2[b] for b in W2],
+        lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
     if not args.no_stack:
         del P4, W4, X4, Y4, Q2
         torch.cuda.empty_cache()

@@ -109,6 +109,19 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
 dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                   int64_t N, int64_t K, int32_t bits, float* y, void* stream);
 
+/* Not a step of the method: a plain streaming read of `bytes` bytes, the
+ * yardstick for the bandwidth-bound entry points above (the rate a kernel
+ * that only reads the same bytes reaches at the same size).  `nparts`
+ * workgroups each read a contiguous share with 16-byte loads and write the
+ * XOR of its 32-bit words to partial[i], so the XOR of partial[0 .. nparts)
+ * is the XOR of every word of the buffer (a share may be empty: then 0).
+ *   buf      in   device, bytes >= 16 and a multiple of 16, 16-byte aligned
+ *   partial  out  device, [nparts] uint32, 4-byte aligned
+ *   1 <= nparts <= DQ_STREAM_MAX_PARTS (else DQ_ERR_SHAPE, as is a bad size) */
+#define DQ_STREAM_MAX_PARTS 65536
+dq_status dq_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* dq_status_string(dq_status status);
 

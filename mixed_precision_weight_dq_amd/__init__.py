@@ -5,12 +5,16 @@ Two layers, both argument marshalling only (every step runs in the HIP
 kernels behind the C ABI declared in ``include/dq.h``):
 
 * ``dq_packed_row_bytes``, ``dq_quantize_pack``, ``dq_unpack``, ``dq_gemv``,
-  ``dq_gemm`` -- the C entry points under their own names, taking integer
-  device addresses and sizes; they return the ``dq_status`` code.
-* ``quantize_pack``, ``unpack``, ``gemv``, ``gemm`` -- the same calls on torch
-  tensors (torch provides device memory and the current stream); they check
-  device, dtype and contiguity, allocate outputs with torch and raise
-  ``DQError`` on a non-zero status.
+  ``dq_gemm``, ``dq_stream_read`` -- the C entry points under their own names,
+  taking integer device addresses and sizes; they return the ``dq_status``
+  code.
+* ``quantize_pack``, ``unpack``, ``gemv``, ``gemm``, ``stream_read`` -- the same
+  calls on torch tensors (torch provides device memory and the current
+  stream); they check device, dtype and contiguity, allocate outputs with
+  torch and raise ``DQError`` on a non-zero status.
+
+``dq_stream_read`` is not a step of the method: a plain streaming read that
+measures what a kernel bound by HBM reaches at a given size.
 
 There is no fallback: if the library is missing or the device is not a GPU,
 the calls fail.
@@ -22,8 +26,8 @@ import os
 
 __all__ = [
     "DQError", "DQ_F32", "DQ_BF16", "library_path", "dq_packed_row_bytes", "dq_quantize_pack",
-    "dq_unpack", "dq_gemv", "dq_gemm", "dq_status_string", "dq_last_error", "packed_row_bytes",
-    "quantize_pack", "unpack", "gemv", "gemm", "load",
+    "dq_unpack", "dq_gemv", "dq_gemm", "dq_stream_read", "dq_status_string", "dq_last_error",
+    "packed_row_bytes", "quantize_pack", "unpack", "gemv", "gemm", "stream_read", "load",
 ]
 
 DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP = range(7)
@@ -64,6 +68,8 @@ def load():
     lib.dq_gemv.restype = st
     lib.dq_gemm.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp]
     lib.dq_gemm.restype = st
+    lib.dq_stream_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.dq_stream_read.restype = st
     lib.dq_status_string.argtypes = [st]
     lib.dq_status_string.restype = ctypes.c_char_p
     lib.dq_last_error.argtypes = []
@@ -96,6 +102,10 @@ def dq_gemv(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int,
 def dq_gemm(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, y: int,
             stream: int = 0) -> int:
     return int(load().dq_gemm(x, M, packed, scales, N, K, bits, y, stream))
+
+
+def dq_stream_read(buf: int, nbytes: int, partial: int, nparts: int, stream: int = 0) -> int:
+    return int(load().dq_stream_read(buf, nbytes, partial, nparts, stream))
 
 
 def dq_status_string(status: int) -> str:
@@ -207,3 +217,21 @@ def gemv(x, packed, scales, K: int, bits: int, y=None):
 def gemm(x, packed, scales, K: int, bits: int, y=None):
     """y[M, N] = x . dequant(W)^T on the bf16 matrix cores (any M >= 1)."""
     return _matmul(dq_gemm, "dq_gemm", x, packed, scales, K, bits, y)
+
+
+def stream_read(buf, nparts: int, partial=None):
+    """Plain streaming read of a contiguous GPU tensor (any dtype, a multiple of
+    16 bytes): the yardstick for the bandwidth-bound calls, not a step of the
+    method.  Returns int32 [nparts] whose XOR is the XOR of every 32-bit word."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if partial is None:
+        partial = torch.empty((nparts,), dtype=torch.int32, device=buf.device)
+    _need(partial, "partial", (torch.int32,), 1)
+    if partial.shape[0] != nparts:
+        raise ValueError("partial must hold nparts words")
+    nbytes = buf.numel() * buf.element_size()
+    _check(dq_stream_read(buf.data_ptr(), nbytes, partial.data_ptr(), nparts, _stream(buf)),
+           "dq_stream_read")
+    return partial

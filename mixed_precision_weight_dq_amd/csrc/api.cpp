@@ -91,6 +91,17 @@ dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
         dq::launch_gemm(x, M, packed, scales, N, K, bits, y, static_cast<hipStream_t>(stream)));
 }
 
+dq_status dq_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
+                         void* stream)
+{
+    if (!buf || !partial) return DQ_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0 || nparts < 1 || nparts > DQ_STREAM_MAX_PARTS)
+        return DQ_ERR_SHAPE;
+    if (!aligned(buf, 16) || !aligned(partial, 4)) return DQ_ERR_ALIGN;
+    return hip_status(
+        dq::launch_stream_read(buf, bytes, partial, nparts, static_cast<hipStream_t>(stream)));
+}
+
 const char* dq_status_string(dq_status status)
 {
     switch (status) {

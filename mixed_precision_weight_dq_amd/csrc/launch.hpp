@@ -16,6 +16,8 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, con
                        int64_t N, int64_t K, int bits, float* y, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
+                              hipStream_t stream);
 
 inline int64_t packed_row_words(int64_t K, int bits)
 {

@@ -115,6 +115,17 @@ def test_alignment_rejected():
         assert fn(A, 1, A, A, 4, 64, 6, A + 2) == dq.DQ_ERR_ALIGN
 
 
+def test_stream_read_arguments_rejected():
+    assert dq.dq_stream_read(0, 64, A, 1) == dq.DQ_ERR_NULL
+    assert dq.dq_stream_read(A, 64, 0, 1) == dq.DQ_ERR_NULL
+    for nbytes in (0, 8, 24, -16):
+        assert dq.dq_stream_read(A, nbytes, A, 1) == dq.DQ_ERR_SHAPE
+    for nparts in (0, -1, 65537):
+        assert dq.dq_stream_read(A, 64, A, nparts) == dq.DQ_ERR_SHAPE
+    assert dq.dq_stream_read(A + 8, 64, A, 1) == dq.DQ_ERR_ALIGN
+    assert dq.dq_stream_read(A, 64, A + 2, 1) == dq.DQ_ERR_ALIGN
+
+
 def test_tensor_wrappers_refuse_cpu_tensors():
     torch = pytest.importorskip("torch")
     w = torch.zeros((4, 64), dtype=torch.float32)

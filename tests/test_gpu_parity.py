@@ -207,3 +207,25 @@ def test_quantize_then_matmul_end_to_end():
     y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
     assert within_tolerance(yv.cpu().numpy(), y_ref, bound).all()
     assert within_tolerance(ym.cpu().numpy(), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("nbytes,nparts", [(16, 1), (16, 3), (4096 + 16, 7), ((1 << 20) + 48, 2048),
+                                           (12 * (1 << 20), 2048)])
+def test_stream_read_reads_every_word(nbytes, nparts):
+    """The streaming-read yardstick: share p of the 16-byte pieces is
+    [n16 p / nparts, n16 (p + 1) / nparts) and its XOR lands in partial[p]."""
+    rng = np.random.default_rng(nbytes + nparts)
+    words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+    report("stream_read bytes=%d nparts=%d" % (nbytes, nparts))
+    buf = torch().from_numpy(words.view(np.int32)).cuda()
+    part = dq.stream_read(buf, nparts)
+    torch().cuda.synchronize()
+    got = part.cpu().numpy().view(np.uint32)
+    n16 = nbytes // 16
+    pieces = words.reshape(n16, 4)
+    want = np.zeros(nparts, dtype=np.uint32)
+    for p in range(nparts):
+        lo, hi = n16 * p // nparts, n16 * (p + 1) // nparts
+        if hi > lo:
+            want[p] = np.bitwise_xor.reduce(pieces[lo:hi].ravel())
+    assert np.array_equal(got, want)
