@@ -604,21 +604,25 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     // epilogue: lane (c, h) holds column c of each 32 x 32 tile, rows
     // 8 (r / 4) + 4 h + r % 4 of accumulator register r.  Whole tiles store
     // without bounds checks, as streaming (nontemporal) stores: y is written
-    // once and not read back by this kernel.
+    // once and not read back by this kernel.  They are buffer stores whose row
+    // offset is a scalar (the same for every lane), so no per-store address
+    // arithmetic runs on the vector units; the tile's 256 rows of y must span
+    // less than 4 GiB (N < 2^22), else the checked stores below serve.
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
-    if (m0 + T::BM <= M && n0 + T::BN <= N) {
+    if (m0 + T::BM <= M && n0 + T::BN <= N && (int64_t)T::BM * N * 4 <= 0xffffffffLL) {
+        const BufRef yb = uniform_buf(y + m0 * N, (uint32_t)(T::BM * N * 4));
+        const uint32_t row4 = (uint32_t)(N * 4);
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
             const float s = scales[n];
+            const uint32_t voff = (uint32_t)(4 * h) * row4 + (uint32_t)n * 4;
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) {
-                float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
+            for (int i = 0; i < kMT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    __builtin_nontemporal_store(s * (acc[i][j][r] * kUnscale),
-                                                yp + (8 * (r >> 2) + (r & 3)) * N);
-            }
+                    buf_store_f32_nt(yb, s * (acc[i][j][r] * kUnscale), voff,
+                                     (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * row4);
         }
         return;
     }

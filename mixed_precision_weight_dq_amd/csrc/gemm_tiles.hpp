@@ -140,6 +140,14 @@ __device__ __forceinline__ u32x4v_t buf_load_b128(BufRef buf, uint32_t voff, uin
     return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(buf.base, buf.bytes), voff, soff, 0);
 }
 
+// One fp32 per lane to byte offset voff + soff of a buffer, as a streaming
+// (nontemporal) store.
+__device__ __forceinline__ void buf_store_f32_nt(BufRef buf, float v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), make_rsrc(buf.base, buf.bytes),
+                                          voff, soff, 2 /* nt */);
+}
+
 // 16 bytes per lane from byte offset voff + soff of a buffer straight into LDS
 // at lds + 16 * lane (buffer_load_dwordx4 ... lds).
 __device__ __forceinline__ void buf_load_lds16(BufRef buf, void* lds, uint32_t voff, uint32_t soff)
