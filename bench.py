@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stack", action="store_true",
                    help="skip the context measurement over the 448-matrix layer stack")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step: every bit width 2..15 on the 28672x8192 matrix "
+                        "(quantize + pack, GEMV at M=1 and 16, GEMM at M=256), one JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed steps, copy 256 MiB device to device once (a plain copy "
                         "of known size for scaling hardware byte counters)")
@@ -197,6 +200,62 @@ def cpu_baseline(decode_w, x1, target_s: float):
                       "%d passes, %.1f s" % (reps, el)}
 
 
+def sweep(torch, dq, workload, dev, stream, reps: int):
+    """Workload 5 at every width: W[28672, 8192] Student-t(5) (std 0.02), x N(0, 1).
+    Each launch is timed alone with HIP events right after a cache-flushing bf16
+    GEMM (so its operands come from HBM), median of `reps`; per-launch times
+    include the launch overhead of one kernel."""
+    wl = workload.WORKLOADS[5]
+    N, K = wl.N, wl.K
+    W = torch.from_numpy(workload.workload_weights(wl, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+    x16 = torch.from_numpy(workload.activations(5, 0, 256, K).view(np.int16)).view(torch.bfloat16).to(dev)
+    ga = torch.randn((4096, 8192), device=dev).to(torch.bfloat16)
+    gb = torch.randn((8192, 4096), device=dev).to(torch.bfloat16)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            torch.matmul(ga, gb)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    rows = []
+    for b in range(2, 16):
+        rb = dq.packed_row_bytes(K, b)
+        P = torch.empty((N, rb // 4), dtype=torch.int32, device=dev)
+        S = torch.empty((N,), dtype=torch.float32, device=dev)
+        dq.quantize_pack(W, b, P, S)
+        y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        y16 = torch.empty((16, N), dtype=torch.float32, device=dev)
+        y256 = torch.empty((256, N), dtype=torch.float32, device=dev)
+        x1, xs = x16[:1], x16[:16]
+        tq = timed(lambda: dq.quantize_pack(W, b, P, S))
+        t1 = timed(lambda: dq.gemv(x1, P, S, K, b, y1))
+        t16 = timed(lambda: dq.gemv(xs, P, S, K, b, y16))
+        tg = timed(lambda: dq.gemm(x16, P, S, K, b, y256))
+        packed = N * K * b / 8
+        rows.append({
+            "bits": b, "packed_mb": round(packed / 1e6, 1),
+            "quantize_us": round(tq, 1), "quantize_gbs": round((N * K * 2 + N * rb) / tq / 1e3, 1),
+            "gemv_m1_us": round(t1, 1), "gemv_m1_gbs": round(packed / t1 / 1e3, 1),
+            "gemv_m16_us": round(t16, 1), "gemv_m16_gbs": round(packed / t16 / 1e3, 1),
+            "gemm_m256_us": round(tg, 1), "gemm_m256_tflops": round(2.0 * 256 * N * K / tg / 1e6, 1),
+        })
+        del P, S, y1, y16, y256
+    return {
+        "sweep": "workload 5: W 28672x8192 bf16 Student-t(5) std 0.02, x N(0,1); every bit width",
+        "timing": "one launch after a cache-flushing bf16 GEMM, HIP events, median of %d; "
+                  "includes one launch overhead" % reps,
+        "peaks": {"hbm_gbs": HBM_PEAK_GBS, "bf16_tflops": MFMA_BF16_PEAK_TFLOPS},
+        "rows": rows,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -212,6 +271,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.sweep:
+        print(json.dumps(sweep(torch, dq, workload, dev, stream, reps=max(5, args.steps // 4))))
+        return
 
     def bf16(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -679,6 +679,14 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
         const int64_t wide = ceil_div(M, 256) * ceil_div(N, WideTile<kWideNT>::BN);
         if (M >= 256 && wide >= 256 && wide * 5 >= ceil_div(wide, 256) * 256 * 4)
             return launch_gemm_wide<B, kWideNT, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, stream);
+        // 256 x 128 tiles when the wider ones are too few (e.g. M = 256 with N
+        // in the tens of thousands): taken when they fill the CUs in at most
+        // two rounds, at least 85 % busy; one row tile then reads each code
+        // once where the 128-row tiles read it twice
+        const int64_t wide1 = ceil_div(M, 256) * ceil_div(N, WideTile<1>::BN);
+        const int64_t rounds1 = ceil_div(wide1, 256);
+        if (M >= 256 && rounds1 <= 2 && wide1 * 20 >= rounds1 * 256 * 17)
+            return launch_gemm_wide<B, 1, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, stream);
         // 128 x 256 tiles (codes up to 8 bits: wider ones need more registers
         // than two workgroups per CU leave), when they fill the 256 CUs twice
         // over; else 128 x 128

@@ -237,6 +237,9 @@ WIDE_CASES = [
     (2000, 8100, 64 * 7),
     (2000, 8100, 64 * 8),
     (1300, 10700, 64 * 9),
+    # 2 x 235 tiles of 256 x 128 (too few 256 x 256 tiles for the CUs): the
+    # narrow wide tiling for every width
+    (300, 30000, 64 * 7),
 ]
 
 
