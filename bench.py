@@ -6,9 +6,13 @@ One step = one pass of the whole path over the synthetic workload:
   2. unpack them back to int32 codes;
   3. quantize + pack the four 8192x8192 prefill matrices (b = 5, 6, 8, 12);
   4. GEMM x[2048, 8192] . W^T for each prefill matrix;
-  5. GEMV x[1, 4096] . W^T for each decode matrix.
-The GEMVs run last, after ~1.5 GB of other traffic, so their packed weights
-are read from HBM rather than from the 256 MB last-level cache.
+  5. decode: for each of 8 tokens, GEMV x_t[1, 4096] . W^T for each decode
+     matrix; token t reads its own copy of the five packed matrices (copy 0 is
+     the one step 1 writes; copies 1..7 hold the same bits, written before
+     timing), 503 MB in all, so no launch finds its weights in the 256 MB
+     last-level cache.
+The 40 GEMV launches form one timed group: one pair of HIP events costs about
+4.5 us, which spread over only five launches would add ~0.9 us to each.
 
 Reported ``value`` is the metric's first half: packed-weight GB/s of the M=1
 GEMV (sum of packed bytes over the sum of the GEMV kernel times, measured with
@@ -34,7 +38,9 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 
-DECODE = dict(N=4096, K=4096, bits=(4, 5, 6, 7, 8), M=1)
+# decode: the five matrices for `tokens` decode tokens, token t reading copy t
+# of the packed matrices (copies x 63 MB > the 256 MB last-level cache)
+DECODE = dict(N=4096, K=4096, bits=(4, 5, 6, 7, 8), M=1, tokens=8)
 PREFILL = dict(N=8192, K=8192, bits=(5, 6, 8, 12), M=2048)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_traffic.json")
 
@@ -127,12 +133,13 @@ def stack_context(torch, dq, workload, dev, stream):
 
 
 def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: int):
-    """Context for the GEMV figure, outside the timed steps: the five decode
-    GEMV launches against a plain streaming read (dq_stream_read) of the same
-    five packed buffers, each group timed after the same cache-flushing GEMM;
-    plus the read rate of a 1 GiB buffer.  The read's share count is the best
-    of three."""
+    """Context for the GEMV figure, outside the timed steps: the decode GEMV
+    launches of a step against a plain streaming read (dq_stream_read) of the
+    same packed buffers in the same order, each group timed after the same
+    cache-flushing GEMM; plus the read rate of a 1 GiB buffer.  The read's
+    share count is the best of three."""
     nbytes = sum(b.numel() * b.element_size() for b in read_bufs)
+    n = len(read_bufs)
 
     def timed(group):
         ts = []
@@ -159,16 +166,16 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     torch.cuda.synchronize()
     big_ms = timed(lambda: dq.stream_read(big, 65536, big_out))
     del big
-    n = len(read_bufs)
     read_gbs = nbytes / (read_ms * 1e-3) / 1e9
     gemv_gbs = nbytes / (gemv_ms * 1e-3) / 1e9
     return {
-        "what": "plain streaming read (dq_stream_read) of the five packed 4096x4096 buffers, back "
-                "to back, vs the five GEMV launches on them; each group after the same b=6 prefill "
-                "GEMM, median of %d; bytes = packed buffers; context, not the value" % reps,
+        "what": "plain streaming read (dq_stream_read) of the step's %d packed 4096x4096 buffers "
+                "(8 tokens x b=4..8, one copy per token), back to back, vs the %d GEMV launches on "
+                "them; each group after the same b=6 prefill GEMM, median of %d; bytes = packed "
+                "buffers; context, not the value" % (n, n, reps),
         "read_gbs": round(read_gbs, 1),
         "read_per_launch_us": round(read_ms / n * 1e3, 3),
-        "read_shares": [o.shape[0] for o in outs],
+        "read_shares": sorted({o.shape[0] for o in outs}),
         "gemv_gbs": round(gemv_gbs, 1),
         "gemv_per_launch_us": round(gemv_ms / n * 1e3, 3),
         "gemv_frac_of_read": round(gemv_gbs / read_gbs, 4),
@@ -284,6 +291,8 @@ def main():
     x1_np = workload.activations(2, 0, DECODE["M"], DECODE["K"])
     W2 = {b: bf16(w) for b, w in decode_np.items()}
     X1 = bf16(x1_np)
+    X1t = [X1] + [bf16(workload.activations(2, t, DECODE["M"], DECODE["K"]))
+                  for t in range(1, DECODE["tokens"])]
     W4 = {b: bf16(workload.workload_weights(wl4, i)) for i, b in enumerate(PREFILL["bits"])}
     X4 = bf16(workload.activations(4, 0, PREFILL["M"], PREFILL["K"]))
 
@@ -294,6 +303,9 @@ def main():
     S2 = {b: torch.empty((DECODE["N"],), dtype=torch.float32, device=dev) for b in W2}
     Q2 = {b: torch.empty((DECODE["N"], DECODE["K"]), dtype=torch.int32, device=dev) for b in W2}
     Y1 = {b: torch.empty((1, DECODE["N"]), dtype=torch.float32, device=dev) for b in W2}
+    for b in W2:
+        dq.quantize_pack(W2[b], b, P2[b], S2[b])
+    P2t = [P2] + [{b: P2[b].clone() for b in W2} for _ in range(1, DECODE["tokens"])]
     P4 = {b: torch.empty((PREFILL["N"], rw(PREFILL["K"], b)), dtype=torch.int32, device=dev) for b in W4}
     S4 = {b: torch.empty((PREFILL["N"],), dtype=torch.float32, device=dev) for b in W4}
     Y4 = torch.empty((PREFILL["M"], PREFILL["N"]), dtype=torch.float32, device=dev)
@@ -309,8 +321,10 @@ def main():
         ops.append(("quantize_pack_8192", b, lambda b=b: dq.quantize_pack(W4[b], b, P4[b], S4[b])))
     for b in W4:  # one event group per GEMM (each runs for hundreds of microseconds)
         ops.append(("gemm_2048_b%d" % b, b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
-    for b in W2:
-        ops.append(("gemv_m1", b, lambda b=b: dq.gemv(X1, P2[b], S2[b], DECODE["K"], b, Y1[b])))
+    decode = [(X1t[t], P2t[t][b], S2[b], b, Y1[b]) for t in range(DECODE["tokens"]) for b in W2]
+    for xt, pt, st, b, yt in decode:
+        ops.append(("gemv_m1", b, lambda xt=xt, pt=pt, st=st, b=b, yt=yt:
+                    dq.gemv(xt, pt, st, DECODE["K"], b, yt)))
 
     # one HIP event at every group boundary (events between every launch would
     # add their own dispatch gaps to the tiny GEMV launches)
@@ -350,9 +364,9 @@ def main():
 
     Nd, Kd = DECODE["N"], DECODE["K"]
     Np, Kp, Mp = PREFILL["N"], PREFILL["K"], PREFILL["M"]
-    gemv_bytes = {b: Nd * Kd * b // 8 for b in DECODE["bits"]}
+    gemv_bytes = DECODE["tokens"] * sum(Nd * Kd * b // 8 for b in DECODE["bits"])
     gemv_ms = group_ms["gemv_m1"]
-    value = sum(gemv_bytes.values()) / (gemv_ms * 1e-3) / 1e9
+    value = gemv_bytes / (gemv_ms * 1e-3) / 1e9
     gemm_flop = 2.0 * Mp * Np * Kp
     gemm_ms = {b: group_ms["gemm_2048_b%d" % b] for b in PREFILL["bits"]}
     gemm_tflops = {b: gemm_flop / (t * 1e-3) / 1e12 for b, t in gemm_ms.items()}
@@ -399,16 +413,18 @@ def main():
         "config": {
             "workload": "decode GEMV 4096x4096 b=4..8 M=1 (value) + prefill GEMM "
                         "M=2048 N=K=8192 b=5,6,8,12 (roofline_gemm)",
-            "gemv": {"N": Nd, "K": Kd, "M": 1, "bits": list(DECODE["bits"])},
+            "gemv": {"N": Nd, "K": Kd, "M": 1, "bits": list(DECODE["bits"]),
+                     "tokens": DECODE["tokens"], "weight_copies": DECODE["tokens"]},
             "gemm": {"N": Np, "K": Kp, "M": Mp, "bits": list(PREFILL["bits"]),
                      "mfma_dtype": "bf16", "accumulate": "f32"},
             "step": "quantize+pack(5 decode) -> unpack(5) -> quantize+pack(4 prefill) -> "
-                    "gemm(4) -> gemv(5)",
+                    "gemm(4) -> decode 8 tokens x gemv(5), token t on copy t of the packed weights",
             "timing": "HIP events at group boundaries on the launch stream; per-launch "
                       "figures are group time / launches (inter-launch gaps included)",
         },
         "roofline": {
-            "kernel": "dq_gemv M=1 N=K=4096 (five launches, b=4..8, back to back)",
+            "kernel": "dq_gemv M=1 N=K=4096 (40 launches back to back: 8 tokens x b=4..8, "
+                      "each on its own copy of the weights)",
             "bound": "hbm",
             "achieved": round(value, 2),
             "peak": HBM_PEAK_GBS,
@@ -454,8 +470,8 @@ def main():
     b6 = PREFILL["bits"][1]
     out["roofline"]["attainable_read"] = attainable_read(
         torch, dq, dev, stream,
-        lambda: [dq.gemv(X1, P2[b], S2[b], DECODE["K"], b, Y1[b]) for b in W2],
-        [P2[b] for b in W2],
+        lambda: [dq.gemv(xt, pt, st, DECODE["K"], b, yt) for xt, pt, st, b, yt in decode],
+        [pt for _, pt, _, _, _ in decode],
         lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
     if not args.no_stack:
         del P4, W4, X4, Y4, Q2
