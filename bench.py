@@ -207,6 +207,17 @@ def cpu_baseline(decode_w, x1, target_s: float):
                       "%d passes, %.1f s" % (reps, el)}
 
 
+def device_info(torch, dev) -> dict:
+    """What the run ran on (the peaks above are MI355X's published figures)."""
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "compute_units": p.multi_processor_count,
+            "memory_gb": round(p.total_memory / 1e9, 1)}
+    arch = getattr(p, "gcnArchName", None)
+    if arch:
+        info["arch"] = arch
+    return info
+
+
 def sweep(torch, dq, workload, dev, stream, reps: int):
     """Workload 5 at every width: W[28672, 8192] Student-t(5) (std 0.02), x N(0, 1).
     Each launch is timed alone with HIP events right after a cache-flushing bf16
@@ -259,6 +270,7 @@ def sweep(torch, dq, workload, dev, stream, reps: int):
         "timing": "one launch after a cache-flushing bf16 GEMM, HIP events, median of %d; "
                   "includes one launch overhead" % reps,
         "peaks": {"hbm_gbs": HBM_PEAK_GBS, "bf16_tflops": MFMA_BF16_PEAK_TFLOPS},
+        "device": device_info(torch, dev),
         "rows": rows,
     }
 
@@ -459,6 +471,7 @@ def main():
                                       lambda b: 16, lambda b: b),
         },
         "cpu_baseline": None,
+        "device": device_info(torch, dev),
     }
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
