@@ -229,3 +229,32 @@ def test_stream_read_reads_every_word(nbytes, nparts):
         if hi > lo:
             want[p] = np.bitwise_xor.reduce(pieces[lo:hi].ravel())
     assert np.array_equal(got, want)
+
+
+def test_random_shapes_whole_path():
+    """Seeded random shapes, widths, dtypes and M through the whole GPU path
+    (quantize + pack on the GPU, then GEMV or GEMM on its output), each checked
+    in full against the oracle: bit-exact packed words and scales, products
+    within 1e-4 * sum |x * w_hat|."""
+    rng = np.random.default_rng(20261203)
+    for case in range(40):
+        bits = int(rng.integers(2, 16))
+        N = int(rng.integers(1, 700))
+        K = int(rng.choice([int(rng.integers(1, 3000)), 32 * int(rng.integers(1, 90)),
+                            64 * int(rng.integers(1, 45))]))
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        kind = "gemv" if case % 2 == 0 else "gemm"
+        M = int(rng.integers(1, 17)) if kind == "gemv" else int(rng.integers(1, 300))
+        outliers = 0.001 if rng.random() < 0.3 else 0.0
+        w = workload.weights(30, case, N, K, dtype=dtype, outlier_frac=outliers)
+        x = workload.activations(30, case, M, K)
+        report("random case %d: %s M=%d N=%d K=%d b=%d %s" % (case, kind, M, N, K, bits, dtype))
+        P, S = dq.quantize_pack(weights_gpu(w), bits)
+        y = (dq.gemv if kind == "gemv" else dq.gemm)(bf16_gpu(x), P, S, K, bits)
+        torch().cuda.synchronize()
+        o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+        assert np.array_equal(u32(P), o_packed), "case %d: packed words differ" % case
+        assert np.array_equal(f32_bits(S), o_scales.view(np.uint32)), "case %d: scales differ" % case
+        y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
+        ok = within_tolerance(y.cpu().numpy(), y_ref, bound)
+        assert ok.all(), "case %d: %d outputs out of tolerance" % (case, int((~ok).sum()))
