@@ -201,10 +201,17 @@ def cpu_baseline(decode_w, x1, target_s: float):
         el = time.perf_counter() - t0
         if el >= target_s:
             break
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": "fp64 GEMV M=1 over the five 4096x4096 decode matrices (b=4..8), "
-                      "%d passes, %.1f s" % (reps, el)}
+                      "%d passes, %.1f s" % (reps, el),
+            "cpu": cpu}
 
 
 def device_info(torch, dev) -> dict:
