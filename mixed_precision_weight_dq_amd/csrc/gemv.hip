@@ -13,10 +13,10 @@
 //     loads of one row cover 64*B contiguous words); x sits in LDS; codes
 //     become signed integers with one XOR per word plus a signed bit-field
 //     extract and meet x in bf16 pair dot products (fp32 FMAs for B >= 10);
-//   * 3 <= M <= 16 (gemv_mfma_xlds_kernel when K is a multiple of 32, x
-//     copied through LDS; else gemv_mfma_kernel): codes expanded to exact
-//     bf16 operands of v_mfma_f32_16x16x32_bf16, so the VALU cost per code no
-//     longer grows with M.
+//   * 3 <= M <= 16 (gemv_mfma_xlds_kernel when K is a multiple of 32, codes
+//     and x copied through LDS; else gemv_mfma_kernel): codes expanded to
+//     exact bf16 operands of v_mfma_f32_16x16x32_bf16, so the VALU cost per
+//     code no longer grows with M.
 #include "common.hpp"
 #include "launch.hpp"
 #include "gemm_tiles.hpp"
@@ -529,19 +529,24 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3 <= M <= 16 and K a multiple of 32: gemv_mfma_kernel with x taken through
-// LDS.  Loaded into registers, x costs as much as the code stream: each lane
-// needs 64 bytes of one row, so every 16-byte load spreads its 64 lanes over
-// 64 cache lines, and lanes of rows past M load too.  Here each wave copies
-// the x of its own steps, rows below kMR only (4 rows of 256 bytes per
-// instruction, each row's 16-byte pieces in one run), straight into a ring of
-// LDS stages of its own (buffer_load ... lds) and reads the A operands back
-// with ds_read_b128.  Piece p of row i sits at slot 16 i + (p ^ i), so the 16
-// lanes of a read that take the same piece of 16 rows hit distinct banks.
-// The ring is private to the wave, so the loop has no barriers; an explicit
-// vmcnt wait before each step covers the LDS copies, which the compiler does
-// not track.  x pieces past K (the last step of a K not a multiple of 128)
-// and rows past M read an offset outside the x buffer, which loads zeros.
+// 3 <= M <= 16 and K a multiple of 32: gemv_mfma_kernel with the codes and x
+// taken through LDS.  Loaded into registers in the MFMA lane layout, each
+// load instruction spreads its lanes over 16 rows (lane 16 g + c: row c,
+// chunk g) and x costs as much as the code stream (each lane needs 64 bytes
+// of one row, so a 16-byte load touches 64 cache lines, and lanes of rows
+// past M load too).  Here each wave copies the codes and x of its own steps
+// straight into a ring of LDS stages of its own (buffer_load ... lds): the
+// codes row by row (a step is 4 chunks = 16 B bytes of each of the 16 kNT
+// rows, so row r fills slots r B .. r B + B - 1), x for rows below kMR only
+// (4 rows of 256 bytes per instruction).  Lanes then read their chunk's B
+// words and the A operands (ds_read_b128) back.  x piece p of row i sits at
+// slot 16 i + (p ^ i), so the 16 lanes of a read that take the same piece of
+// 16 rows hit distinct banks.  The ring is private to the wave, so the loop
+// has no barriers; an explicit vmcnt wait before each step covers the LDS
+// copies, which the compiler does not track.  x pieces past K (the last step
+// of a K not a multiple of 128) and rows past M read an offset outside the x
+// buffer, which loads zeros; codes past a row's end meet those zeros, and
+// rows past N read zeros.
 template <int B>
 constexpr int words_loads() { return B / 4 + (B % 4 != 0 ? 1 : 0); }
 
@@ -556,9 +561,11 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     constexpr bool kSplit = B >= 10;
     constexpr int kStages = kDepth + 1;
     constexpr int kXCopies = kMR / 4;
-    constexpr int kPerStage = kNT * words_loads<B>() + kXCopies;
+    constexpr int kCodeSlots = (16 * kNT * B + 63) / 64 * 64;  // 16-byte code pieces of one step
+    constexpr int kCodeCopies = kCodeSlots / 64;
+    constexpr int kPerStage = kCodeCopies + kXCopies;
     constexpr int kSlots = kMR * 16;  // 16-byte x pieces of one step
-    static_assert(kDepth >= 1 && kDepth <= 3, "one to three steps ahead");
+    static_assert(kDepth >= 1 && kDepth <= 2, "one or two steps ahead");
     static_assert(kMR == 8 || kMR == 16, "x rows staged: 8 or 16");
     static_assert(kDepth * kPerStage < 64, "vmcnt holds at most 63");
     // one LDS object per stage, so each copy and read names its stage
@@ -567,12 +574,21 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     __shared__ __attribute__((aligned(16))) uint4 xs2[kStages > 2 ? kGemvMfmaWaves : 1][kStages > 2 ? kSlots : 1];
     __shared__ __attribute__((aligned(16))) uint4 xs3[kStages > 3 ? kGemvMfmaWaves : 1][kStages > 3 ? kSlots : 1];
     __shared__ float red[kGemvMfmaWaves - 1][kNT][4][kWave];
+    __shared__ __attribute__((aligned(16))) uint4 cs0[kGemvMfmaWaves][kCodeSlots];
+    __shared__ __attribute__((aligned(16))) uint4 cs1[kGemvMfmaWaves][kCodeSlots];
+    __shared__ __attribute__((aligned(16))) uint4 cs2[kStages > 2 ? kGemvMfmaWaves : 1][kStages > 2 ? kCodeSlots : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = lane & 15;
     const int g = lane >> 4;
+    auto cring = [&](auto S) -> uint4* {
+        constexpr int st = decltype(S)::value;
+        if constexpr (st == 0) return cs0[wave];
+        else if constexpr (st == 1) return cs1[wave];
+        else return cs2[kStages > 2 ? wave : 0];
+    };
     auto ring = [&](auto S) -> uint4* {
         constexpr int st = decltype(S)::value;
         if constexpr (st == 0) return xs0[wave];
@@ -607,13 +623,20 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) aslot[t] = 16 * ar + ((4 * g + t) ^ ar);
 
-    uint32_t w[kStages][kNT][B];
-    auto load = [&](auto P, int64_t ks) {
-        constexpr int p = decltype(P)::value;
-        const int64_t ch = 4 * ks + g;
+    // codes: copy q fills slot s = 64 q + l with piece s % B of row s / B of
+    // the step (16-byte pieces; slots past the tile's rows get zeros)
+    uint32_t cbase[kCodeCopies];
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
-            buf_load_words<B>(wb, (uint32_t)((16 * j + c) * row_words * 4 + ch * B * 4), 0u, w[p][j]);
+    for (int q = 0; q < kCodeCopies; ++q) {
+        const int sl = 64 * q + lane;
+        const int r = sl / B, pc = sl % B;
+        cbase[q] = r < 16 * kNT ? (uint32_t)(r * row_words * 4 + pc * 16) : kOutside;
+    }
+    auto load = [&](auto P, int64_t ks) {
+        uint4* cdst = cring(P);
+#pragma unroll
+        for (int q = 0; q < kCodeCopies; ++q)
+            buf_load_lds16(wb, cdst + 64 * q, cbase[q] != kOutside ? cbase[q] + (uint32_t)(ks * 16 * B) : kOutside, 0u);
         uint4* dst = ring(P);
 #pragma unroll
         for (int q = 0; q < kXCopies; ++q) {
@@ -626,17 +649,23 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     for (int j = 0; j < kNT; ++j) acc[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
     // vmcnt(n) with expcnt and lgkmcnt left at their maxima
     auto compute = [&](auto P, auto Wait) {
-        constexpr int p = decltype(P)::value;
         constexpr int n = decltype(Wait)::value;
         __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
         const uint4* src = ring(P);
+        // this lane's chunk (chunk g of the step) of row c of each row tile
+        uint32_t wl[kNT][B];
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(cring(P));
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int i = 0; i < B; ++i) wl[j][i] = cw[(16 * j + c) * 4 * B + g * B + i];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const bf16x8m_t a = __builtin_bit_cast(bf16x8m_t, src[aslot[t]]);
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 bf16x8_t bh, bl;
-                expand8<B>(w[p][j], t, bh, bl);
+                expand8<B>(wl[j], t, bh, bl);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
                 if constexpr (kSplit) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
             }
@@ -711,10 +740,10 @@ hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* pac
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 16 * kNT)), block(kGemvMfmaWaves * kWave);
     if (K % kChunk == 0 && M <= 8)
-        gemv_mfma_xlds_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, 8><<<grid, block, 0, stream>>>(
+        gemv_mfma_xlds_kernel<B, kNT, 2, 8><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y);
-    else if (K % kChunk == 0)
-        gemv_mfma_xlds_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH, 16><<<grid, block, 0, stream>>>(
+    else if (K % kChunk == 0)  // twice the x per stage: one step ahead, so two workgroups fit per CU
+        gemv_mfma_xlds_kernel<B, kNT, 1, 16><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y);
     else
         gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH><<<grid, block, 0, stream>>>(
