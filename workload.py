@@ -7,13 +7,17 @@ random draws, the fp32 -> bf16 input rounding and the workload shapes.
 Recipe (every draw is reproducible from its integers):
 * generator: numpy PCG64 seeded with SeedSequence([workload, matrix, role,
   block]); role 0 = weights, 1 = activations, 2 = outlier positions,
-  3 = bit-width shuffle; weights are drawn in blocks of 1024 rows;
+  3 = bit-width shuffle, 4 = Hessian traces; weights are drawn in blocks of
+  1024 rows;
 * weights: fp32 draws times the stated std (0.02), rounded to bf16 with
   round-half-to-even on the bit pattern (or kept fp32 where the workload says
   fp32); Student-t(5) draws are divided by sqrt(5/3) so the std is 0.02;
 * outliers: a fraction of positions drawn without replacement over the whole
   matrix, multiplied by 20 in fp32 before the bf16 rounding;
-* activations: bf16 N(0, 1) rounded the same way.
+* activations: bf16 N(0, 1) rounded the same way;
+* Hessian traces (the model-dependent half of a sensitivity, which needs a
+  trained model and calibration data): one log-normal draw per matrix,
+  exp(N(0, 1)), so sensitivities spread over about two decades.
 
 The shapes follow the pages' model sizes: the 27B-class layer (5120 hidden,
 17408 MLP, 64 layers, 448 matrices) of the DynaQuant page's results table and
@@ -26,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-ROLE_W, ROLE_X, ROLE_OUTLIER, ROLE_SHUFFLE = 0, 1, 2, 3
+ROLE_W, ROLE_X, ROLE_OUTLIER, ROLE_SHUFFLE, ROLE_HTRACE = 0, 1, 2, 3, 4
 ROW_BLOCK = 1024
 
 
@@ -104,6 +108,12 @@ def stack_bits(workload: int = 3) -> list[int]:
     bits = [6] * 283 + [5] * 98 + [7] * 40 + [8] * 27
     perm = _rng(workload, 0, ROLE_SHUFFLE, 0).permutation(len(bits))
     return [bits[i] for i in perm]
+
+
+def hessian_traces(workload: int, count: int) -> np.ndarray:
+    """Synthetic per-matrix Hessian traces: fp64 exp(N(0, 1)), one per matrix."""
+    g = _rng(workload, 0, ROLE_HTRACE, 0)
+    return np.exp(g.standard_normal(count))
 
 
 def stack_shapes() -> list[tuple[int, int]]:
