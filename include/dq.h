@@ -21,10 +21,21 @@
  *    (dequantize fused into the matrix product; int weights, fp32 scales, fp32
  *    output):  y[m,n] = s[n] * sum_k x[m,k] * q[n,k],  i.e. y = x . W_hat^T.
  *
+ *  - Bit allocation (the step before quantization): DynaQuant page,
+ *    "第一步：敏感度测量" (sensitivity = Hessian trace x mean(w^2)) and
+ *    "第二步：比特分配" (water-filling on a max-heap; hardware-native levels
+ *    {4, 8, 16} or every width 4 .. 16, where 16 keeps the BF16 weights).
+ *    mean(w^2) is measured on the GPU (dq_row_sumsq, or fused into the
+ *    quantize pass: dq_quantize_pack_sumsq); dq_sensitivity and
+ *    dq_allocate_bits run on the host.
+ *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers (memory of the current HIP
- *    device).  The caller allocates and owns every buffer; the library
- *    allocates nothing, keeps no state between calls and is re-entrant.
+ *    device), except for dq_sensitivity and dq_allocate_bits, which take HOST
+ *    pointers, enqueue nothing and return when done.  The caller allocates
+ *    and owns every buffer; the library allocates no device memory (the
+ *    allocator keeps O(n) host memory during the call), keeps no state
+ *    between calls and is re-entrant.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued asynchronously; nothing is synchronised.
  *  - Argument errors are detected on the host and returned BEFORE any HIP call;
@@ -40,7 +51,8 @@
  *  - Sizes: 1 <= N <= 2^31-1, 1 <= K <= DQ_MAX_K; dq_gemv: 1 <= M <= 16;
  *    dq_gemm: 1 <= M <= 2^31-1.
  *  - Alignment: W, packed and x must be 16-byte aligned (DQ_ERR_ALIGN);
- *    scales, q_out, w_out and y 4-byte aligned.
+ *    scales, q_out, w_out and y 4-byte aligned; row_sumsq and matrix_sumsq
+ *    8-byte aligned.
  */
 #ifndef DQ_H
 #define DQ_H
@@ -61,6 +73,8 @@ typedef int32_t dq_status;
 #define DQ_ERR_ALIGN 4 /* a pointer is not aligned as required               */
 #define DQ_ERR_DTYPE 5 /* w_dtype is neither DQ_F32 nor DQ_BF16              */
 #define DQ_ERR_HIP 6   /* a HIP launch or runtime call failed                */
+#define DQ_ERR_BUDGET 7 /* bit budget below every matrix at its lowest level */
+#define DQ_ERR_VALUE 8 /* a sensitivity, trace, sum or parameter count out of range */
 
 #define DQ_F32 0  /* W holds IEEE fp32 values                               */
 #define DQ_BF16 1 /* W holds bf16 bit patterns (uint16)                     */
@@ -69,6 +83,9 @@ typedef int32_t dq_status;
 #define DQ_MAX_BITS 15
 #define DQ_GEMV_MAX_M 16
 #define DQ_MAX_K (1LL << 22)
+#define DQ_TOP_BITS 16                 /* allocation level meaning "BF16 kept" */
+#define DQ_MAX_MATRICES (1LL << 24)    /* matrices per allocation              */
+#define DQ_MAX_PARAMS (1LL << 40)      /* parameters per matrix                */
 
 /* Bytes of one packed row: ceil(K*bits/8) rounded up to a multiple of 128.
  * Returns 0 when K or bits is out of range.  Host-only, no HIP call. */
@@ -83,6 +100,27 @@ size_t dq_packed_row_bytes(int64_t K, int32_t bits);
  * treated like an all-zero row: scale = fl32(1/qmax), q = 0. */
 dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
                            uint32_t* packed, float* scales, void* stream);
+
+/* The statistic a matrix's sensitivity needs (DynaQuant page, "第一步：敏感度
+ * 测量": mean(w^2) of the matrix), measured before any width is chosen: one
+ * read of W.
+ *   w             in   device, [N, K], dtype w_dtype (DQ_F32 or DQ_BF16)
+ *   row_sumsq     out  device, [N] fp64, sum_k W[n,k]^2 (8-byte aligned)
+ *   matrix_sumsq  out  device, [1] fp64, sum of row_sumsq; may be NULL
+ * Every square of an fp32 or bf16 value is exact in fp64; the sums are fp64
+ * in a fixed order (the same bits on every call), within (count - 1) * 2^-53
+ * of the exact sum relative to it.  A row with a NaN gives NaN, one with an
+ * infinity +inf.  mean(w^2) = matrix_sumsq / (N * K). */
+dq_status dq_row_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K, double* row_sumsq,
+                       double* matrix_sumsq, void* stream);
+
+/* dq_quantize_pack and dq_row_sumsq in one pass over W, for callers that
+ * quantize a matrix anyway and want the statistic of exactly what they store
+ * (say, to re-run the allocation after a change).  packed and scales are
+ * bit-identical to dq_quantize_pack's, the sums to dq_row_sumsq's. */
+dq_status dq_quantize_pack_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                 int32_t bits, uint32_t* packed, float* scales,
+                                 double* row_sumsq, double* matrix_sumsq, void* stream);
 
 /* Inverse of the packing.
  *   packed  in   device, [N, row_words] uint32
@@ -121,6 +159,41 @@ dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
 #define DQ_STREAM_MAX_PARTS 65536
 dq_status dq_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
                          void* stream);
+
+/* Sensitivity of each of n matrices (HOST pointers; DynaQuant page,
+ * "第一步：敏感度测量"):  out[i] = h_trace[i] * (sumsq[i] / params[i]), an fp64
+ * divide then an fp64 multiply.  h_trace and sumsq must be finite and >= 0,
+ * 1 <= params[i] <= DQ_MAX_PARAMS (else DQ_ERR_VALUE); 1 <= n <= DQ_MAX_MATRICES. */
+dq_status dq_sensitivity(const double* h_trace, const double* sumsq, const int64_t* params,
+                         int64_t n, double* out);
+
+/* Water-filling bit allocation over n matrices (HOST pointers; DynaQuant page,
+ * "第二步：比特分配").  Every matrix starts at levels[0]; a step raises one
+ * matrix to its next level; the step removing the most predicted loss per
+ * byte goes first (ties: the lower matrix index).  Predicted loss of matrix i
+ * at b bits: sensitivity[i] * 4^-b, and 0 at DQ_TOP_BITS (BF16 kept).  A step
+ * that does not fit in the budget is dropped for good and the others go on;
+ * a step that removes no loss is never taken.
+ *   sensitivity    in   [n] fp64, finite, >= 0
+ *   params         in   [n] parameters per matrix, 1 .. DQ_MAX_PARAMS
+ *   levels         in   [n_levels] strictly increasing widths in [2, 16]
+ *                       ({4, 8, 16} hardware-native, {4, ..., 16} full)
+ *   budget_bits        total bits sum_i params[i] * bits[i] allowed; < 0 = no
+ *                       limit (the whole frontier); below the floor
+ *                       sum_i params[i] * levels[0]: DQ_ERR_BUDGET
+ *   bits_out       out  [n] chosen width per matrix (the recipe)
+ *   step_matrix,
+ *   step_bits      out  [step_capacity] the steps taken, in order (matrix,
+ *                       new width); may be NULL when step_capacity == 0;
+ *                       only the first step_capacity are written
+ *   n_steps        out  number of steps taken (may exceed step_capacity); may be NULL
+ *   loss           out  predicted total loss sum_i L_i(bits_out[i]); may be NULL
+ * Priorities are fp64 in a fixed order of operations, so the result is the
+ * same bit for bit on every platform with IEEE doubles. */
+dq_status dq_allocate_bits(const double* sensitivity, const int64_t* params, int64_t n,
+                           const int32_t* levels, int32_t n_levels, int64_t budget_bits,
+                           int32_t* bits_out, int64_t* step_matrix, int32_t* step_bits,
+                           int64_t step_capacity, int64_t* n_steps, double* loss);
 
 /* Static text for a status code. */
 const char* dq_status_string(dq_status status);

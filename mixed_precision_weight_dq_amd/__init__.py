@@ -4,14 +4,17 @@ dequantized GEMV / GEMM on MI355X (gfx950).
 Two layers, both argument marshalling only (every step runs in the HIP
 kernels behind the C ABI declared in ``include/dq.h``):
 
-* ``dq_packed_row_bytes``, ``dq_quantize_pack``, ``dq_unpack``, ``dq_gemv``,
-  ``dq_gemm``, ``dq_stream_read`` -- the C entry points under their own names,
-  taking integer device addresses and sizes; they return the ``dq_status``
-  code.
-* ``quantize_pack``, ``unpack``, ``gemv``, ``gemm``, ``stream_read`` -- the same
-  calls on torch tensors (torch provides device memory and the current
-  stream); they check device, dtype and contiguity, allocate outputs with
-  torch and raise ``DQError`` on a non-zero status.
+* ``dq_packed_row_bytes``, ``dq_quantize_pack``, ``dq_row_sumsq``,
+  ``dq_quantize_pack_sumsq``, ``dq_unpack``, ``dq_gemv``, ``dq_gemm``, ``dq_stream_read``,
+  ``dq_sensitivity``, ``dq_allocate_bits`` -- the C entry points under their
+  own names, taking integer addresses (device memory, host memory for the last
+  two) and sizes; they return the ``dq_status`` code.
+* ``quantize_pack``, ``row_sumsq``, ``quantize_pack_sumsq``, ``unpack``, ``gemv``, ``gemm``,
+  ``stream_read`` -- the same calls on torch tensors (torch provides device
+  memory and the current stream); they check device, dtype and contiguity,
+  allocate outputs with torch and raise ``DQError`` on a non-zero status.
+* ``sensitivity``, ``allocate_bits`` -- the host-side allocation calls on
+  numpy arrays (the recipe: one bit width per matrix).
 
 ``dq_stream_read`` is not a step of the method: a plain streaming read that
 measures what a kernel bound by HBM reaches at a given size.
@@ -28,11 +31,16 @@ __all__ = [
     "DQError", "DQ_F32", "DQ_BF16", "library_path", "dq_packed_row_bytes", "dq_quantize_pack",
     "dq_unpack", "dq_gemv", "dq_gemm", "dq_stream_read", "dq_status_string", "dq_last_error",
     "packed_row_bytes", "quantize_pack", "unpack", "gemv", "gemm", "stream_read", "load",
+    "dq_row_sumsq", "row_sumsq", "dq_quantize_pack_sumsq", "dq_sensitivity", "dq_allocate_bits", "quantize_pack_sumsq",
+    "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS",
 ]
 
-DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP = range(7)
+(DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP,
+ DQ_ERR_BUDGET, DQ_ERR_VALUE) = range(9)
 DQ_F32, DQ_BF16 = 0, 1
 GEMV_MAX_M = 16
+NATIVE_LEVELS = (4, 8, 16)        # hardware-native allocation levels (16 = BF16 kept)
+FULL_LEVELS = tuple(range(4, 17))  # every width from 4 to 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdq.so")
@@ -70,6 +78,14 @@ def load():
     lib.dq_gemm.restype = st
     lib.dq_stream_read.argtypes = [vp, i64, vp, i64, vp]
     lib.dq_stream_read.restype = st
+    lib.dq_row_sumsq.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    lib.dq_row_sumsq.restype = st
+    lib.dq_quantize_pack_sumsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.dq_quantize_pack_sumsq.restype = st
+    lib.dq_sensitivity.argtypes = [vp, vp, vp, i64, vp]
+    lib.dq_sensitivity.restype = st
+    lib.dq_allocate_bits.argtypes = [vp, vp, i64, vp, i32, i64, vp, vp, vp, i64, vp, vp]
+    lib.dq_allocate_bits.restype = st
     lib.dq_status_string.argtypes = [st]
     lib.dq_status_string.restype = ctypes.c_char_p
     lib.dq_last_error.argtypes = []
@@ -87,6 +103,29 @@ def dq_packed_row_bytes(K: int, bits: int) -> int:
 def dq_quantize_pack(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int, scales: int,
                      stream: int = 0) -> int:
     return int(load().dq_quantize_pack(w, w_dtype, N, K, bits, packed, scales, stream))
+
+
+def dq_row_sumsq(w: int, w_dtype: int, N: int, K: int, row_sumsq: int, matrix_sumsq: int,
+                 stream: int = 0) -> int:
+    return int(load().dq_row_sumsq(w, w_dtype, N, K, row_sumsq, matrix_sumsq, stream))
+
+
+def dq_quantize_pack_sumsq(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int,
+                           scales: int, row_sumsq: int, matrix_sumsq: int, stream: int = 0) -> int:
+    return int(load().dq_quantize_pack_sumsq(w, w_dtype, N, K, bits, packed, scales, row_sumsq,
+                                             matrix_sumsq, stream))
+
+
+def dq_sensitivity(h_trace: int, sumsq: int, params: int, n: int, out: int) -> int:
+    return int(load().dq_sensitivity(h_trace, sumsq, params, n, out))
+
+
+def dq_allocate_bits(sensitivity: int, params: int, n: int, levels: int, n_levels: int,
+                     budget_bits: int, bits_out: int, step_matrix: int, step_bits: int,
+                     step_capacity: int, n_steps: int, loss: int) -> int:
+    return int(load().dq_allocate_bits(sensitivity, params, n, levels, n_levels, budget_bits,
+                                       bits_out, step_matrix, step_bits, step_capacity, n_steps,
+                                       loss))
 
 
 def dq_unpack(packed: int, scales: int, N: int, K: int, bits: int, q_out: int, w_out: int,
@@ -171,6 +210,93 @@ def quantize_pack(w, bits: int, packed=None, scales=None):
     _check(dq_quantize_pack(w.data_ptr(), dt, N, K, bits, packed.data_ptr(), scales.data_ptr(),
                             _stream(w)), "dq_quantize_pack")
     return packed, scales
+
+
+def row_sumsq(w, want_total: bool = True):
+    """fp64 sum of w^2 of every row of W[N, K] (float32 or bfloat16, on the GPU),
+    and of the whole matrix.  Returns (row_sumsq float64 [N], matrix_sumsq float64
+    [1] or None)."""
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16), 2)
+    N, K = w.shape
+    row = torch.empty((N,), dtype=torch.float64, device=w.device)
+    total = torch.empty((1,), dtype=torch.float64, device=w.device) if want_total else None
+    dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
+    _check(dq_row_sumsq(w.data_ptr(), dt, N, K, row.data_ptr(),
+                        total.data_ptr() if total is not None else 0, _stream(w)), "dq_row_sumsq")
+    return row, total
+
+
+def quantize_pack_sumsq(w, bits: int, want_total: bool = True):
+    """``quantize_pack`` plus the fp64 sum of w^2 of every row, taken in the same
+    pass.  Returns (packed, scales, row_sumsq float64 [N], matrix_sumsq float64 [1]
+    or None)."""
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16), 2)
+    N, K = w.shape
+    rw = packed_row_bytes(K, bits) // 4
+    packed = torch.empty((N, rw), dtype=torch.int32, device=w.device)
+    scales = torch.empty((N,), dtype=torch.float32, device=w.device)
+    row = torch.empty((N,), dtype=torch.float64, device=w.device)
+    total = torch.empty((1,), dtype=torch.float64, device=w.device) if want_total else None
+    dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
+    _check(dq_quantize_pack_sumsq(w.data_ptr(), dt, N, K, bits, packed.data_ptr(),
+                                  scales.data_ptr(), row.data_ptr(),
+                                  total.data_ptr() if total is not None else 0, _stream(w)),
+           "dq_quantize_pack_sumsq")
+    return packed, scales, row, total
+
+
+def _host(a, dtype, name):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if a.ndim != 1:
+        raise ValueError("%s must be 1-D" % name)
+    return a
+
+
+def _addr(a) -> int:
+    return a.ctypes.data
+
+
+def sensitivity(h_trace, sumsq, params):
+    """Sensitivity per matrix, h_trace * (sumsq / params), on the host (numpy in,
+    numpy float64 out)."""
+    import numpy as np
+    h = _host(h_trace, np.float64, "h_trace")
+    ss = _host(sumsq, np.float64, "sumsq")
+    p = _host(params, np.int64, "params")
+    if not h.size == ss.size == p.size:
+        raise ValueError("h_trace, sumsq and params must have one entry per matrix")
+    out = np.empty(h.size, dtype=np.float64)
+    _check(dq_sensitivity(_addr(h), _addr(ss), _addr(p), h.size, _addr(out)), "dq_sensitivity")
+    return out
+
+
+def allocate_bits(sens, params, levels=FULL_LEVELS, budget_bits=None):
+    """Water-filling allocation on the host.  Returns (bits int32 [n], steps as a
+    list of (matrix, new width) in the order taken, predicted loss).  A budget
+    of None walks the whole frontier."""
+    import numpy as np
+    s = _host(sens, np.float64, "sensitivity")
+    p = _host(params, np.int64, "params")
+    lv = _host(levels, np.int32, "levels")
+    if s.size != p.size:
+        raise ValueError("one sensitivity and one parameter count per matrix")
+    bits = np.empty(s.size, dtype=np.int32)
+    cap = s.size * max(lv.size - 1, 0)
+    sm = np.empty(max(cap, 1), dtype=np.int64)
+    sb = np.empty(max(cap, 1), dtype=np.int32)
+    nsteps = np.zeros(1, dtype=np.int64)
+    loss = np.zeros(1, dtype=np.float64)
+    budget = -1 if budget_bits is None else int(budget_bits)
+    if budget_bits is not None and budget < 0:
+        raise ValueError("budget_bits must be >= 0 (None = no limit)")
+    _check(dq_allocate_bits(_addr(s), _addr(p), s.size, _addr(lv), lv.size, budget, _addr(bits),
+                            _addr(sm), _addr(sb), cap, _addr(nsteps), _addr(loss)),
+           "dq_allocate_bits")
+    n = int(nsteps[0])
+    return bits, list(zip(sm[:n].tolist(), sb[:n].tolist())), float(loss[0])
 
 
 def unpack(packed, scales, K: int, bits: int, want_q: bool = True, want_w: bool = False):

@@ -1,6 +1,7 @@
 // C ABI of the library (declared in include/dq.h): argument validation on the
-// host, then one kernel launch on the caller's stream.  No allocation, no
+// host, then the kernel launches on the caller's stream.  No allocation, no
 // synchronisation, no state beyond the per-thread text of the last HIP error.
+// (The host-only allocation entry points live in recipe.cpp.)
 #include "../../include/dq.h"
 
 #include <hip/hip_runtime.h>
@@ -51,6 +52,34 @@ dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K,
     if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DQ_ERR_ALIGN;
     return hip_status(dq::launch_quantize_pack(w, w_dtype == DQ_BF16, N, K, bits, packed, scales,
                                                static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_quantize_pack_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                 int32_t bits, uint32_t* packed, float* scales,
+                                 double* row_sumsq, double* matrix_sumsq, void* stream)
+{
+    if (!w || !packed || !scales || !row_sumsq) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(row_sumsq, 8) ||
+        !aligned(matrix_sumsq, 8))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_quantize_pack_sumsq(w, w_dtype == DQ_BF16, N, K, bits, packed,
+                                                     scales, row_sumsq, matrix_sumsq,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_row_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K, double* row_sumsq,
+                       double* matrix_sumsq, void* stream)
+{
+    if (!w || !row_sumsq) return DQ_ERR_NULL;
+    if (N < 1 || N > 0x7fffffffLL || K < 1 || K > DQ_MAX_K) return DQ_ERR_SHAPE;
+    if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
+    if (!aligned(w, 16) || !aligned(row_sumsq, 8) || !aligned(matrix_sumsq, 8))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_row_sumsq(w, w_dtype == DQ_BF16, N, K, row_sumsq, matrix_sumsq,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
@@ -107,11 +136,15 @@ const char* dq_status_string(dq_status status)
     switch (status) {
     case DQ_OK: return "ok";
     case DQ_ERR_NULL: return "a required pointer is NULL";
-    case DQ_ERR_BITS: return "bits must be in [2, 15]";
+    case DQ_ERR_BITS: return "bits must be in [2, 15] (allocation levels: increasing, in [2, 16])";
     case DQ_ERR_SHAPE: return "N, K or M out of range";
-    case DQ_ERR_ALIGN: return "pointer not aligned (W, packed, x: 16 bytes; others: 4 bytes)";
+    case DQ_ERR_ALIGN:
+        return "pointer not aligned (W, packed, x: 16 bytes; fp64 sums: 8; others: 4)";
     case DQ_ERR_DTYPE: return "w_dtype must be DQ_F32 or DQ_BF16";
     case DQ_ERR_HIP: return "HIP launch or runtime error";
+    case DQ_ERR_BUDGET: return "bit budget below every matrix at its lowest level";
+    case DQ_ERR_VALUE:
+        return "sensitivity, trace or sum not finite and >= 0, or parameter count out of range";
     default: return "unknown status";
     }
 }

@@ -10,6 +10,11 @@ namespace dq {
 
 hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
                                 uint32_t* packed, float* scales, hipStream_t stream);
+hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                      uint32_t* packed, float* scales, double* row_sumsq,
+                                      double* matrix_sumsq, hipStream_t stream);
+hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
+                            double* matrix_sumsq, hipStream_t stream);
 hipError_t launch_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
                          int bits, int32_t* q_out, float* w_out, hipStream_t stream);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,

@@ -12,6 +12,10 @@
 // result is exact and NaN/Inf are seen as larger than every finite value).
 // Pass 2 re-reads the row (L2-resident), and each lane turns 32 consecutive
 // elements into exactly B whole output words, so no two lanes share a word.
+//
+// The statistic behind a matrix's sensitivity (DynaQuant page, "第一步：敏感度
+// 测量": mean(w^2)) rides along in pass 1 when asked for: an fp64 sum of
+// squares per row, and optionally one more launch that adds the rows up.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -115,17 +119,33 @@ __device__ __forceinline__ void store_chunk(uint32_t* __restrict__ prow, int64_t
     }
 }
 
+// Sum of squares of a chunk, added to acc in fp64: each square of an fp32
+// value is exact in fp64, so the only roundings are those of the additions.
+__device__ __forceinline__ double chunk_sumsq(const float (&v)[kChunk], double acc)
+{
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        const double d = (double)v[j];
+        acc += d * d;
+    }
+    return acc;
+}
+
 // One workgroup of 64..256 threads per row (enough for one chunk per thread
 // when K <= 8192).  kAligned (K a multiple of 32): every chunk is whole, so
 // loads take the 16-byte vector path without per-lane bounds checks.  Each thread keeps its first chunk in registers between the
 // max pass and the quantize pass; further chunks (long rows) are read again.
-template <int B, bool BF16, bool kAligned>
+// kSumsq: pass 1 also sums w^2 over the row in fp64 (per lane in chunk order,
+// then across the wave by a fixed butterfly, then over the waves in order) and
+// writes it to row_sumsq[n]; the codes and scales are unchanged.
+template <int B, bool BF16, bool kAligned, bool kSumsq>
 __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t K, int64_t row_words, uint32_t* __restrict__ packed,
-    float* __restrict__ scales)
+    float* __restrict__ scales, double* __restrict__ row_sumsq)
 {
     constexpr int32_t kQmax = (1 << (B - 1)) - 1;
     __shared__ uint32_t red[kQuantThreads / kWave];
+    __shared__ double red_sq[kQuantThreads / kWave];
 
     const int64_t n = blockIdx.x;
     const int tid = threadIdx.x;
@@ -140,6 +160,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     // ---- pass 1: max |w| as an integer max over sign-cleared bit patterns
     float v0[kChunk];
     uint32_t amax = 0;
+    double sq = 0.0;
     if (tid < nchunks) {
         load_row_chunk<BF16, kAligned>(w, row_off, K, tid, vec_ok, v0);
 #pragma unroll
@@ -147,6 +168,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
             const uint32_t m = __float_as_uint(v0[j]) & 0x7fffffffu;
             amax = m > amax ? m : amax;
         }
+        if (kSumsq) sq = chunk_sumsq(v0, sq);
     }
     for (int64_t c = tid + threads; c < nchunks; c += threads) {
         float v[kChunk];
@@ -156,11 +178,22 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
             const uint32_t m = __float_as_uint(v[j]) & 0x7fffffffu;
             amax = m > amax ? m : amax;
         }
+        if (kSumsq) sq = chunk_sumsq(v, sq);
     }
     amax = wave_max_u32(amax);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
+    if (kSumsq) {
+#pragma unroll
+        for (int d = kWave / 2; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, kWave);
+        if ((tid & (kWave - 1)) == 0) red_sq[tid / kWave] = sq;
+    }
     __syncthreads();
     for (int i = 0; i < waves; ++i) amax = red[i] > amax ? red[i] : amax;
+    if (kSumsq && tid == 0) {
+        double row = red_sq[0];
+        for (int i = 1; i < waves; ++i) row += red_sq[i];
+        row_sumsq[n] = row;
+    }
 
     // ---- scale
     const float qmaxf = (float)kQmax;
@@ -251,9 +284,60 @@ __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
     }
 }
 
-template <int B>
+// The statistic alone (the measurement step comes before any width is
+// chosen): one workgroup per row, the chunks of pass 1 above, fp64 sums in
+// the same fixed order as the fused kernel, so both give the same bits.
+template <bool BF16, bool kAligned>
+__global__ __launch_bounds__(kQuantThreads) void row_sumsq_kernel(const void* __restrict__ w,
+                                                                  int64_t K,
+                                                                  double* __restrict__ row_sumsq)
+{
+    __shared__ double red_sq[kQuantThreads / kWave];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int threads = blockDim.x;
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int esize = BF16 ? 2 : 4;
+    const bool vec_ok = ((K * esize) & 15) == 0;
+    double sq = 0.0;
+    for (int64_t c = tid; c < nchunks; c += threads) {
+        float v[kChunk];
+        load_row_chunk<BF16, kAligned>(w, n * K, K, c, vec_ok, v);
+        sq = chunk_sumsq(v, sq);
+    }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, kWave);
+    if ((tid & (kWave - 1)) == 0) red_sq[tid / kWave] = sq;
+    __syncthreads();
+    if (tid == 0) {
+        double row = red_sq[0];
+        for (int i = 1; i < threads / kWave; ++i) row += red_sq[i];
+        row_sumsq[n] = row;
+    }
+}
+
+// One workgroup adds the N row sums in a fixed order: thread t takes rows
+// t, t + 256, ... in turn, then the 256 partial sums meet by a fixed tree.
+constexpr int kSumThreads = 256;
+
+__global__ __launch_bounds__(kSumThreads) void sum_rows_kernel(const double* __restrict__ rows,
+                                                               int64_t N, double* __restrict__ out)
+{
+    __shared__ double part[kSumThreads];
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < N; i += kSumThreads) acc += rows[i];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int d = kSumThreads / 2; d >= 1; d >>= 1) {
+        if ((int)threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = part[0];
+}
+
+template <int B, bool kSumsq>
 hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K, uint32_t* packed,
-                                  float* scales, hipStream_t stream)
+                                  float* scales, double* row_sumsq, hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
     // one chunk per thread where the row allows, in whole waves, 64..256 threads
@@ -263,13 +347,17 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
     const dim3 grid((unsigned)N), block(threads);
     const bool aligned = K % kChunk == 0;
     if (bf16 && aligned)
-        quantize_pack_kernel<B, true, true><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+        quantize_pack_kernel<B, true, true, kSumsq>
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
     else if (bf16)
-        quantize_pack_kernel<B, true, false><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+        quantize_pack_kernel<B, true, false, kSumsq>
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
     else if (aligned)
-        quantize_pack_kernel<B, false, true><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+        quantize_pack_kernel<B, false, true, kSumsq>
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
     else
-        quantize_pack_kernel<B, false, false><<<grid, block, 0, stream>>>(w, K, rw, packed, scales);
+        quantize_pack_kernel<B, false, false, kSumsq>
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
     return hipGetLastError();
 }
 
@@ -288,9 +376,44 @@ hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, int64_t 
 hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
                                 uint32_t* packed, float* scales, hipStream_t stream)
 {
-#define CALL(B) launch_quantize_pack_b<B>(w, bf16, N, K, packed, scales, stream)
+#define CALL(B) launch_quantize_pack_b<B, false>(w, bf16, N, K, packed, scales, nullptr, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
+}
+
+hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                      uint32_t* packed, float* scales, double* row_sumsq,
+                                      double* matrix_sumsq, hipStream_t stream)
+{
+    hipError_t e;
+#define CALL(B) launch_quantize_pack_b<B, true>(w, bf16, N, K, packed, scales, row_sumsq, stream)
+    e = [&]() -> hipError_t { DQ_BITS_SWITCH(bits, CALL) }();
+#undef CALL
+    if (e != hipSuccess || !matrix_sumsq) return e;
+    sum_rows_kernel<<<dim3(1), dim3(kSumThreads), 0, stream>>>(row_sumsq, N, matrix_sumsq);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
+                            double* matrix_sumsq, hipStream_t stream)
+{
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
+                                                       : ceil_div(nchunks, kWave) * kWave);
+    const dim3 grid((unsigned)N), block(threads);
+    const bool aligned = K % kChunk == 0;
+    if (bf16 && aligned)
+        row_sumsq_kernel<true, true><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+    else if (bf16)
+        row_sumsq_kernel<true, false><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+    else if (aligned)
+        row_sumsq_kernel<false, true><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+    else
+        row_sumsq_kernel<false, false><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !matrix_sumsq) return e;
+    sum_rows_kernel<<<dim3(1), dim3(kSumThreads), 0, stream>>>(row_sumsq, N, matrix_sumsq);
+    return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,

@@ -29,7 +29,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
-                 "dq_status_string", "dq_last_error"):
+                 "dq_status_string", "dq_last_error", "dq_quantize_pack_sumsq", "dq_sensitivity",
+                 "dq_row_sumsq",
+                 "dq_allocate_bits"):
         assert want in names
 
 
@@ -50,8 +52,8 @@ def test_row_bytes():
 
 
 def test_status_strings():
-    for s in range(7):
-        assert dq.dq_status_string(s)
+    for s in range(9):
+        assert dq.dq_status_string(s) != "unknown status"
     assert dq.dq_status_string(99) == "unknown status"
     assert dq.dq_last_error() == ""
 
@@ -133,3 +135,27 @@ def test_tensor_wrappers_refuse_cpu_tensors():
         dq.quantize_pack(w, 6)
     with pytest.raises(dq.DQError):
         dq.packed_row_bytes(64, 1)
+
+
+def test_quantize_pack_sumsq_arguments_rejected():
+    f = dq.dq_quantize_pack_sumsq
+    assert f(A, dq.DQ_BF16, 4, 64, 6, A, A, 0, A) == dq.DQ_ERR_NULL   # row sums required
+    assert f(0, dq.DQ_BF16, 4, 64, 6, A, A, A, 0) == dq.DQ_ERR_NULL
+    assert f(A, dq.DQ_BF16, 4, 64, 16, A, A, A, 0) == dq.DQ_ERR_BITS
+    assert f(A, dq.DQ_BF16, 0, 64, 6, A, A, A, 0) == dq.DQ_ERR_SHAPE
+    assert f(A, 3, 4, 64, 6, A, A, A, 0) == dq.DQ_ERR_DTYPE
+    assert f(A, dq.DQ_BF16, 4, 64, 6, A, A, A + 4, 0) == dq.DQ_ERR_ALIGN
+    assert f(A, dq.DQ_BF16, 4, 64, 6, A, A, A, A + 4) == dq.DQ_ERR_ALIGN
+    assert f(MIS, dq.DQ_BF16, 4, 64, 6, A, A, A, 0) == dq.DQ_ERR_ALIGN
+
+
+def test_row_sumsq_arguments_rejected():
+    f = dq.dq_row_sumsq
+    assert f(0, dq.DQ_BF16, 4, 64, A, 0) == dq.DQ_ERR_NULL
+    assert f(A, dq.DQ_BF16, 4, 64, 0, A) == dq.DQ_ERR_NULL
+    for N, K in ((0, 64), (4, 0), (1 << 31, 64), (4, (1 << 22) + 1)):
+        assert f(A, dq.DQ_F32, N, K, A, 0) == dq.DQ_ERR_SHAPE
+    assert f(A, 2, 4, 64, A, 0) == dq.DQ_ERR_DTYPE
+    assert f(MIS, dq.DQ_F32, 4, 64, A, 0) == dq.DQ_ERR_ALIGN
+    assert f(A, dq.DQ_F32, 4, 64, A + 4, 0) == dq.DQ_ERR_ALIGN
+    assert f(A, dq.DQ_F32, 4, 64, A, A + 4) == dq.DQ_ERR_ALIGN
