@@ -95,14 +95,18 @@ def stack_context(torch, dq, workload, dev, stream):
     then GEMV at M = 1 and M = 8 over every matrix in layer order."""
     shapes, recipe = workload.stack_shapes(), workload.stack_bits()
     gen = torch.Generator(device=dev)
-    packs, total = [], 0
+    packs, total, sums = [], 0, []
     for idx, ((N, K), b) in enumerate(zip(shapes, recipe)):
         gen.manual_seed(3000 + idx)
         W = (torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        sums.append(dq.row_sumsq(W)[1])  # mean(w^2) for the allocation context
         P, S = dq.quantize_pack(W, b)
         packs.append((P, S, K, b, N))
         total += N * K * b // 8
         del W
+    torch.cuda.synchronize()
+    sumsq = torch.cat(sums).cpu().numpy()
+    del sums
     xs = {K: torch.from_numpy(workload.activations(3, K, 8, K).view(np.int16)).view(torch.bfloat16).to(dev)
           for K in {k for _, k in shapes}}
     ys = {(N, M): torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -129,7 +133,70 @@ def stack_context(torch, dq, workload, dev, stream):
     out["packed_gb"] = round(total / 1e9, 3)
     out["what"] = ("decode GEMV over the 448-matrix layer stack (17.8 GB packed, mostly 6-bit), "
                    "every matrix in layer order per pass; packed-weight GB/s; context, not the value")
-    return out
+    return out, sumsq
+
+
+def allocation_context(dq, workload, sumsq, reps: int = 20):
+    """The allocation step on the 448-matrix stack, outside the timed steps:
+    sensitivities from the GPU-measured sum(w^2) of every matrix and synthetic
+    Hessian traces, then the full-mode recipe at 5.7 bits per parameter (the
+    DynaQuant knee) and the hardware-native one at the same budget."""
+    params = np.array([n * k for n, k in workload.stack_shapes()], dtype=np.int64)
+    h = workload.hessian_traces(3, len(params))
+    sens = dq.sensitivity(h, sumsq, params)
+    budget = int(5.7 * int(params.sum()))
+    out = {}
+    for name, levels in (("full", dq.FULL_LEVELS), ("native", dq.NATIVE_LEVELS)):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            bits, steps, loss = dq.allocate_bits(sens, params, levels, budget)
+            ts.append(time.perf_counter() - t0)
+        hist = {str(b): int((bits == b).sum()) for b in sorted(set(bits.tolist()))}
+        out[name] = {
+            "recipe": hist, "steps": len(steps),
+            "avg_bits": round(float((bits.astype(np.int64) * params).sum()) / float(params.sum()), 4),
+            "call_us": round(float(np.median(ts)) * 1e6, 1),
+        }
+    out["what"] = ("water-filling allocation over the 448 matrices at 5.7 bits per parameter: "
+                   "sum(w^2) measured on the GPU (dq_row_sumsq), synthetic Hessian traces, host "
+                   "call time of dq_allocate_bits (Python marshalling included)")
+    return out, (sens, params, budget)
+
+
+def row_sumsq_context(torch, dq, stream, mats, reps: int):
+    """dq_row_sumsq over the given bf16 matrices back to back (more bytes than
+    the 256 MB last-level cache, so each is read from HBM), median of reps."""
+    nbytes = sum(w.numel() * 2 + w.shape[0] * 8 for w in mats)
+    rows = [torch.empty((w.shape[0],), dtype=torch.float64, device=w.device) for w in mats]
+    tot = [torch.empty((1,), dtype=torch.float64, device=w.device) for w in mats]
+
+    def group(with_total):
+        for w, r, t in zip(mats, rows, tot):
+            dq._check(dq.dq_row_sumsq(w.data_ptr(), dq.DQ_BF16, w.shape[0], w.shape[1],
+                                      r.data_ptr(), t.data_ptr() if with_total else 0,
+                                      stream.cuda_stream), "dq_row_sumsq")
+
+    def timed(with_total):
+        group(with_total)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            group(with_total)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    ms_rows, ms_tot = timed(False), timed(True)
+    g = nbytes / (ms_rows * 1e-3) / 1e9
+    return {"kernel": "dq_row_sumsq row sums over %d bf16 %dx%d matrices back to back"
+                      % (len(mats), mats[0].shape[0], mats[0].shape[1]),
+            "bound": "hbm", "gbs": round(g, 1), "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4),
+            "per_matrix_us": round(ms_rows / len(mats) * 1e3, 2),
+            "with_matrix_total_us": round(ms_tot / len(mats) * 1e3, 2),
+            "bytes": "N*K*2 read + N*8 written per matrix"}
 
 
 def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: int):
@@ -183,10 +250,20 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     }
 
 
-def cpu_baseline(decode_w, x1, target_s: float):
+def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
     """The oracle's fp64 GEMV (unpack bit by bit + dot product) over the decode
-    matrices, repeated until about target_s seconds of CPU time."""
+    matrices, repeated until about target_s seconds of CPU time; and, given the
+    stack's allocation inputs, the oracle's allocator on them."""
     import oracle
+    from oracle import recipe as orc
+    alloc = None
+    if allocation is not None:
+        sens, params, budget = allocation
+        alloc = {}
+        for name, levels in (("full", orc.FULL_LEVELS), ("native", orc.NATIVE_LEVELS)):
+            t0 = time.perf_counter()
+            orc.allocate(sens, params, levels, budget)
+            alloc[name + "_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
     packs = []
     for b, w in decode_w.items():
         p, s, _ = oracle.quantize_pack(w, b)
@@ -211,7 +288,7 @@ def cpu_baseline(decode_w, x1, target_s: float):
             "kind": "oracle",
             "sample": "fp64 GEMV M=1 over the five 4096x4096 decode matrices (b=4..8), "
                       "%d passes, %.1f s" % (reps, el),
-            "cpu": cpu}
+            "cpu": cpu, "allocation_oracle": alloc}
 
 
 def device_info(torch, dev) -> dict:
@@ -493,12 +570,19 @@ def main():
         lambda: [dq.gemv(xt, pt, st, DECODE["K"], b, yt) for xt, pt, st, b, yt in decode],
         [pt for _, pt, _, _, _ in decode],
         lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
+    out["allocation"] = {"row_sumsq": row_sumsq_context(torch, dq, stream, list(W4.values()),
+                                                        reps=max(5, args.steps))}
     if not args.no_stack:
         del P4, W4, X4, Y4, Q2
         torch.cuda.empty_cache()
-        out["roofline"]["context_layer_stack"] = stack_context(torch, dq, workload, dev, stream)
+        out["roofline"]["context_layer_stack"], stack_sumsq = stack_context(
+            torch, dq, workload, dev, stream)
+        out["allocation"]["stack_recipe"], alloc_inputs = allocation_context(dq, workload,
+                                                                             stack_sumsq)
+    else:
+        alloc_inputs = None
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(decode_np, x1_np, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(decode_np, x1_np, args.cpu_seconds, alloc_inputs)
     print(json.dumps(out))
 
 

@@ -117,7 +117,9 @@ dq_status dq_row_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K, dou
 /* dq_quantize_pack and dq_row_sumsq in one pass over W, for callers that
  * quantize a matrix anyway and want the statistic of exactly what they store
  * (say, to re-run the allocation after a change).  packed and scales are
- * bit-identical to dq_quantize_pack's, the sums to dq_row_sumsq's. */
+ * bit-identical to dq_quantize_pack's; the sums obey the same bound as
+ * dq_row_sumsq's (and are the same on every call) but add in another fixed
+ * order, so they may differ from dq_row_sumsq's in the last bits. */
 dq_status dq_quantize_pack_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K,
                                  int32_t bits, uint32_t* packed, float* scales,
                                  double* row_sumsq, double* matrix_sumsq, void* stream);

@@ -285,47 +285,92 @@ __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
 }
 
 // The statistic alone (the measurement step comes before any width is
-// chosen): one workgroup per row, the chunks of pass 1 above, fp64 sums in
-// the same fixed order as the fused kernel, so both give the same bits.
-template <bool BF16, bool kAligned>
-__global__ __launch_bounds__(kQuantThreads) void row_sumsq_kernel(const void* __restrict__ w,
-                                                                  int64_t K,
-                                                                  double* __restrict__ row_sumsq)
+// chosen): one wave per row, so a row needs no workgroup barrier, and each
+// lane keeps 256 bytes of loads in flight (4 chunks of bf16, 2 of fp32), held
+// as raw words until they are added.  Lane l adds the chunks l, l + 64,
+// l + 128, ... of its row in that order, element by element, then the wave
+// meets by a fixed butterfly: the same bits on every call.
+constexpr int kSumsqWaves = 4;
+
+__device__ __forceinline__ double add_sq(double acc, float v)
 {
-    __shared__ double red_sq[kQuantThreads / kWave];
-    const int64_t n = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int threads = blockDim.x;
+    const double d = (double)v;
+    return acc + d * d;
+}
+
+template <bool BF16, bool kAligned>
+__global__ __launch_bounds__(kSumsqWaves * kWave) void row_sumsq_kernel(
+    const void* __restrict__ w, int64_t N, int64_t K, double* __restrict__ row_sumsq)
+{
+    constexpr int kU = BF16 ? 4 : 2;            // chunks per lane per round
+    constexpr int kVec = BF16 ? 4 : 8;          // 16-byte loads per chunk
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t n = (int64_t)blockIdx.x * kSumsqWaves + (threadIdx.x >> 6);
+    if (n >= N) return;  // the whole wave leaves; nothing below waits on it
     const int64_t nchunks = ceil_div(K, kChunk);
     const int esize = BF16 ? 2 : 4;
     const bool vec_ok = ((K * esize) & 15) == 0;
     double sq = 0.0;
-    for (int64_t c = tid; c < nchunks; c += threads) {
-        float v[kChunk];
-        load_row_chunk<BF16, kAligned>(w, n * K, K, c, vec_ok, v);
-        sq = chunk_sumsq(v, sq);
+    if (kAligned && vec_ok) {
+        const uint4* row = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(w) +
+                                                          n * K * esize);
+        for (int64_t c0 = lane; c0 < nchunks; c0 += (int64_t)kWave * kU) {
+            uint4 raw[kU][kVec];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t c = c0 + (int64_t)u * kWave;
+#pragma unroll
+                for (int i = 0; i < kVec; ++i)
+                    raw[u][i] = c < nchunks ? row[c * kVec + i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    const uint32_t e[4] = {raw[u][i].x, raw[u][i].y, raw[u][i].z, raw[u][i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (BF16) {
+                            sq = add_sq(sq, __uint_as_float(e[j] << 16));
+                            sq = add_sq(sq, __uint_as_float(e[j] & 0xffff0000u));
+                        } else {
+                            sq = add_sq(sq, __uint_as_float(e[j]));
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        for (int64_t c = lane; c < nchunks; c += kWave) {
+            float v[kChunk];
+            load_row_chunk<BF16, false>(w, n * K, K, c, vec_ok, v);
+            sq = chunk_sumsq(v, sq);
+        }
     }
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, kWave);
-    if ((tid & (kWave - 1)) == 0) red_sq[tid / kWave] = sq;
-    __syncthreads();
-    if (tid == 0) {
-        double row = red_sq[0];
-        for (int i = 1; i < threads / kWave; ++i) row += red_sq[i];
-        row_sumsq[n] = row;
-    }
+    if (lane == 0) row_sumsq[n] = sq;
 }
 
-// One workgroup adds the N row sums in a fixed order: thread t takes rows
-// t, t + 256, ... in turn, then the 256 partial sums meet by a fixed tree.
-constexpr int kSumThreads = 256;
+// One workgroup adds the N row sums in a fixed order: thread t takes the
+// runs of 8 rows starting at 8t, 8t + 8192, ... (all 8 loads issued before the
+// adds), then the 1024 partial sums meet by a fixed tree in LDS.
+constexpr int kSumThreads = 1024;
+constexpr int kSumRun = 8;
 
 __global__ __launch_bounds__(kSumThreads) void sum_rows_kernel(const double* __restrict__ rows,
                                                                int64_t N, double* __restrict__ out)
 {
     __shared__ double part[kSumThreads];
     double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < N; i += kSumThreads) acc += rows[i];
+    for (int64_t base = (int64_t)threadIdx.x * kSumRun; base < N;
+         base += (int64_t)kSumThreads * kSumRun) {
+        double v[kSumRun];
+#pragma unroll
+        for (int u = 0; u < kSumRun; ++u) v[u] = base + u < N ? rows[base + u] : 0.0;
+#pragma unroll
+        for (int u = 0; u < kSumRun; ++u) acc += v[u];
+    }
     part[threadIdx.x] = acc;
     __syncthreads();
     for (int d = kSumThreads / 2; d >= 1; d >>= 1) {
@@ -397,19 +442,16 @@ hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64
 hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
                             double* matrix_sumsq, hipStream_t stream)
 {
-    const int64_t nchunks = ceil_div(K, kChunk);
-    const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
-                                                       : ceil_div(nchunks, kWave) * kWave);
-    const dim3 grid((unsigned)N), block(threads);
+    const dim3 grid((unsigned)ceil_div(N, kSumsqWaves)), block(kSumsqWaves * kWave);
     const bool aligned = K % kChunk == 0;
     if (bf16 && aligned)
-        row_sumsq_kernel<true, true><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+        row_sumsq_kernel<true, true><<<grid, block, 0, stream>>>(w, N, K, row_sumsq);
     else if (bf16)
-        row_sumsq_kernel<true, false><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+        row_sumsq_kernel<true, false><<<grid, block, 0, stream>>>(w, N, K, row_sumsq);
     else if (aligned)
-        row_sumsq_kernel<false, true><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+        row_sumsq_kernel<false, true><<<grid, block, 0, stream>>>(w, N, K, row_sumsq);
     else
-        row_sumsq_kernel<false, false><<<grid, block, 0, stream>>>(w, K, row_sumsq);
+        row_sumsq_kernel<false, false><<<grid, block, 0, stream>>>(w, N, K, row_sumsq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !matrix_sumsq) return e;
     sum_rows_kernel<<<dim3(1), dim3(kSumThreads), 0, stream>>>(row_sumsq, N, matrix_sumsq);

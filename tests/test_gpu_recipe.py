@@ -48,8 +48,13 @@ def exact_total(w_np: np.ndarray) -> float:
     return math.fsum((f.astype(np.float64).ravel() ** 2).tolist())
 
 
+# beside the quantizer's shapes, rows whose K is a multiple of 32 (the
+# unrolled path of dq_row_sumsq) with whole and ragged rounds of loads
+SUMSQ_SHAPES = QUANT_SHAPES + [(5, 5120), (6, 8192), (3, 17408), (4, 64), (13, 96)]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("N,K", QUANT_SHAPES)
+@pytest.mark.parametrize("N,K", SUMSQ_SHAPES)
 def test_row_sumsq_parity(N, K, dtype):
     w_np = workload.weights(1, 40, N, K, dtype=dtype)
     report("row_sumsq N=%d K=%d %s" % (N, K, dtype))
@@ -62,8 +67,9 @@ def test_row_sumsq_parity(N, K, dtype):
 @pytest.mark.parametrize("bits", [2, 6, 9, 15])
 @pytest.mark.parametrize("N,K", [(3, 31), (33, 1000), (9, 8192 + 40)])
 def test_fused_sumsq_matches_both(N, K, bits):
-    """The fused pass gives dq_quantize_pack's words and scales and
-    dq_row_sumsq's sums, bit for bit."""
+    """The fused pass gives dq_quantize_pack's words and scales bit for bit,
+    and sums within the bound (it adds in another fixed order than
+    dq_row_sumsq, so the last bits may differ)."""
     w_np = workload.weights(1, 41, N, K, dtype="bf16")
     w = weights_gpu(w_np)
     report("quantize_pack_sumsq N=%d K=%d bits=%d" % (N, K, bits))
@@ -75,9 +81,11 @@ def test_fused_sumsq_matches_both(N, K, bits):
     assert np.array_equal(u32(packed), o_packed)
     assert np.array_equal(f32_bits(scales), o_scales.view(np.uint32))
     assert np.array_equal(u32(packed), u32(p2)) and np.array_equal(f32_bits(scales), f32_bits(s2))
-    assert row.cpu().numpy().tobytes() == r2.cpu().numpy().tobytes()
-    assert total.cpu().numpy().tobytes() == t2.cpu().numpy().tobytes()
-    sums_within(row.cpu().numpy(), recipe.row_sumsq(w_np), K)
+    want = recipe.row_sumsq(w_np)
+    sums_within(row.cpu().numpy(), want, K)
+    sums_within(r2.cpu().numpy(), want, K)
+    sums_within(total.cpu().numpy(), [exact_total(w_np)], N * K)
+    sums_within(t2.cpu().numpy(), [exact_total(w_np)], N * K)
 
 
 @pytest.mark.parametrize("K", [1, 33, 614])
@@ -94,7 +102,7 @@ def test_sumsq_special_rows(K):
     torch().cuda.synchronize()
     want = recipe.row_sumsq(w_np)
     sums_within(row.cpu().numpy(), want, K)
-    assert row.cpu().numpy().tobytes() == row2.cpu().numpy().tobytes()
+    sums_within(row2.cpu().numpy(), want, K)
     t = float(total.cpu()[0])
     if np.isnan(want).any():
         assert math.isnan(t)  # a NaN row makes the total NaN
@@ -116,14 +124,18 @@ def test_row_sumsq_full_size_sampled():
     sums_within(total.cpu().numpy(), [math.fsum(row.tolist())], w5.N)
 
 
-def test_deterministic():
-    w_np = workload.weights(1, 42, 300, 5000, dtype="bf16")
+@pytest.mark.parametrize("K", [5000, 5120])
+def test_deterministic(K):
+    w_np = workload.weights(1, 42, 301, K, dtype="bf16")
     w = weights_gpu(w_np)
     a = [dq.row_sumsq(w) for _ in range(3)]
+    f = [dq.quantize_pack_sumsq(w, 6)[2:] for _ in range(2)]
     torch().cuda.synchronize()
     for r, t in a[1:]:
         assert r.cpu().numpy().tobytes() == a[0][0].cpu().numpy().tobytes()
         assert t.cpu().numpy().tobytes() == a[0][1].cpu().numpy().tobytes()
+    assert f[0][0].cpu().numpy().tobytes() == f[1][0].cpu().numpy().tobytes()
+    assert f[0][1].cpu().numpy().tobytes() == f[1][1].cpu().numpy().tobytes()
 
 
 @pytest.mark.parametrize("levels", [dq.NATIVE_LEVELS, dq.FULL_LEVELS], ids=["native", "full"])
