@@ -75,6 +75,8 @@ typedef int32_t dq_status;
 #define DQ_ERR_HIP 6   /* a HIP launch or runtime call failed                */
 #define DQ_ERR_BUDGET 7 /* bit budget below every matrix at its lowest level */
 #define DQ_ERR_VALUE 8 /* a sensitivity, trace, sum or parameter count out of range */
+#define DQ_ERR_IO 9     /* a file could not be opened, written, sized or mapped   */
+#define DQ_ERR_FORMAT 10 /* a file is not a packed-weight file, or is corrupt     */
 
 #define DQ_F32 0  /* W holds IEEE fp32 values                               */
 #define DQ_BF16 1 /* W holds bf16 bit patterns (uint16)                     */
@@ -196,6 +198,66 @@ dq_status dq_allocate_bits(const double* sensitivity, const int64_t* params, int
                            const int32_t* levels, int32_t n_levels, int64_t budget_bits,
                            int32_t* bits_out, int64_t* step_matrix, int32_t* step_bits,
                            int64_t step_capacity, int64_t* n_steps, double* loss);
+
+/* On-disk packed-weight format (DynaQuant page, "项目现状与路线图": a packed
+ * storage format on disk is listed as in progress; this layout is the
+ * library's own).  One file holds a recipe: every matrix's name, shape and
+ * width, its packed words exactly as in device memory and its scales, each
+ * region at a 4096-byte boundary so that the file maps straight into memory.
+ * Layout (little-endian): 64-byte header {"DQWPACK1", u32 version = 1, u32
+ * count, u64 table offset = 64, u64 file bytes, 32 zero bytes}; then count
+ * 128-byte entries {char name[64] NUL-padded, i64 N, i64 K, i32 bits, u32 0,
+ * u64 data offset, u64 data bytes, u64 scales offset (0 if none), u64
+ * checksum, u64 0}; then the regions in entry order.  bits 2..15: data =
+ * packed [N, row_words] uint32 and fp32 scales [N]; bits 16: the BF16 weights
+ * kept, data = bf16 [N, K], no scales.  checksum = 64-bit FNV-1a over the
+ * data bytes then the scale bytes: h = 0xcbf29ce484222325, then for each byte
+ * h = (h ^ byte) * 0x100000001b3 mod 2^64. */
+#define DQ_FILE_MAX_MATRICES (1LL << 20)
+
+typedef struct {
+    char name[64];        /* UTF-8, NUL-terminated within the 64 bytes        */
+    int64_t N;
+    int64_t K;
+    int32_t bits;         /* 2..15 packed, 16 = BF16 weights kept             */
+    const void* data;     /* HOST: packed words [N, row_words] or bf16 [N, K]  */
+    const float* scales;  /* HOST: fp32 [N]; NULL when bits == 16             */
+} dq_file_matrix;
+
+typedef struct dq_file dq_file; /* an open, memory-mapped file (read only) */
+
+/* Write `count` matrices (host buffers) to `path` (created or truncated).
+ * Descriptions are checked before the file is touched: DQ_ERR_BITS,
+ * DQ_ERR_SHAPE (N, K as for dq_quantize_pack; 1 <= count <=
+ * DQ_FILE_MAX_MATRICES), DQ_ERR_NULL, DQ_ERR_VALUE (a name without its NUL);
+ * DQ_ERR_IO if writing fails (the file may then be partial). */
+dq_status dq_file_write(const char* path, const dq_file_matrix* mats, int64_t count);
+
+/* Map `path` read-only and check its header and every entry (magic, version,
+ * sizes consistent with N, K and bits, regions aligned, in order and inside
+ * the file): DQ_ERR_FORMAT otherwise.  The handle is the caller's until
+ * dq_file_close. */
+dq_status dq_file_open(const char* path, dq_file** out);
+
+/* Number of matrices in an open file (0 for NULL). */
+int64_t dq_file_count(const dq_file* f);
+
+/* Entry i: name, shape, width, and host pointers into the mapping (valid
+ * until dq_file_close). */
+dq_status dq_file_matrix_info(const dq_file* f, int64_t i, dq_file_matrix* out);
+
+/* Recompute entry i's checksum: DQ_OK if it matches, DQ_ERR_FORMAT if not. */
+dq_status dq_file_verify(const dq_file* f, int64_t i);
+
+/* Copy entry i into device buffers on `stream` (hipMemcpyAsync from the
+ * mapping; the mapping must stay open until the copy is done):
+ *   data    out  device, the entry's data bytes (16-byte aligned)
+ *   scales  out  device, fp32 [N] (4-byte aligned); ignored and may be NULL
+ *                when the entry has no scales */
+dq_status dq_file_load(const dq_file* f, int64_t i, void* data, float* scales, void* stream);
+
+/* Unmap and free the handle (NULL is ignored). */
+void dq_file_close(dq_file* f);
 
 /* Static text for a status code. */
 const char* dq_status_string(dq_status status);

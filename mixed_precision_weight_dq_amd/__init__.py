@@ -15,6 +15,9 @@ kernels behind the C ABI declared in ``include/dq.h``):
   allocate outputs with torch and raise ``DQError`` on a non-zero status.
 * ``sensitivity``, ``allocate_bits`` -- the host-side allocation calls on
   numpy arrays (the recipe: one bit width per matrix).
+* ``write_packed_file``, ``PackedFile`` -- the on-disk packed-weight format
+  (``dq_file_*``): write a recipe's packed matrices from host arrays, map a
+  file, read its entries as numpy views and copy them into GPU tensors.
 
 ``dq_stream_read`` is not a step of the method: a plain streaming read that
 measures what a kernel bound by HBM reaches at a given size.
@@ -32,11 +35,12 @@ __all__ = [
     "dq_unpack", "dq_gemv", "dq_gemm", "dq_stream_read", "dq_status_string", "dq_last_error",
     "packed_row_bytes", "quantize_pack", "unpack", "gemv", "gemm", "stream_read", "load",
     "dq_row_sumsq", "row_sumsq", "dq_quantize_pack_sumsq", "dq_sensitivity", "dq_allocate_bits", "quantize_pack_sumsq",
-    "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS",
+    "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS", "DQFileMatrix",
+    "write_packed_file", "PackedFile",
 ]
 
 (DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP,
- DQ_ERR_BUDGET, DQ_ERR_VALUE) = range(9)
+ DQ_ERR_BUDGET, DQ_ERR_VALUE, DQ_ERR_IO, DQ_ERR_FORMAT) = range(11)
 DQ_F32, DQ_BF16 = 0, 1
 GEMV_MAX_M = 16
 NATIVE_LEVELS = (4, 8, 16)        # hardware-native allocation levels (16 = BF16 kept)
@@ -45,6 +49,12 @@ FULL_LEVELS = tuple(range(4, 17))  # every width from 4 to 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdq.so")
 _lib = None
+
+
+class DQFileMatrix(ctypes.Structure):
+    """``dq_file_matrix`` of include/dq.h."""
+    _fields_ = [("name", ctypes.c_char * 64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class DQError(RuntimeError):
@@ -80,6 +90,21 @@ def load():
     lib.dq_stream_read.restype = st
     lib.dq_row_sumsq.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     lib.dq_row_sumsq.restype = st
+    fp = ctypes.POINTER(DQFileMatrix)
+    lib.dq_file_write.argtypes = [ctypes.c_char_p, fp, i64]
+    lib.dq_file_write.restype = st
+    lib.dq_file_open.argtypes = [ctypes.c_char_p, ctypes.POINTER(vp)]
+    lib.dq_file_open.restype = st
+    lib.dq_file_count.argtypes = [vp]
+    lib.dq_file_count.restype = i64
+    lib.dq_file_matrix_info.argtypes = [vp, i64, fp]
+    lib.dq_file_matrix_info.restype = st
+    lib.dq_file_verify.argtypes = [vp, i64]
+    lib.dq_file_verify.restype = st
+    lib.dq_file_load.argtypes = [vp, i64, vp, vp, vp]
+    lib.dq_file_load.restype = st
+    lib.dq_file_close.argtypes = [vp]
+    lib.dq_file_close.restype = None
     lib.dq_quantize_pack_sumsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.dq_quantize_pack_sumsq.restype = st
     lib.dq_sensitivity.argtypes = [vp, vp, vp, i64, vp]
@@ -361,3 +386,103 @@ def stream_read(buf, nparts: int, partial=None):
     _check(dq_stream_read(buf.data_ptr(), nbytes, partial.data_ptr(), nparts, _stream(buf)),
            "dq_stream_read")
     return partial
+
+
+# ------------------------------------------------------ on-disk packed format
+
+def write_packed_file(path: str, matrices) -> None:
+    """Write matrices to a packed-weight file.  ``matrices``: (name, N, K, bits,
+    data, scales) with host numpy arrays -- data the packed words [N, row_words]
+    (any 4-byte dtype) for bits 2..15, or bf16 bit patterns [N, K] (uint16) for
+    bits 16; scales float32 [N] (None for bits 16)."""
+    import numpy as np
+    keep = []
+    arr = (DQFileMatrix * len(matrices))()
+    for i, (name, N, K, bits, data, scales) in enumerate(matrices):
+        raw = name.encode("utf-8")
+        if len(raw) > 63 or b"\0" in raw:
+            raise ValueError("a name takes at most 63 UTF-8 bytes and no NUL")
+        data = np.ascontiguousarray(data)
+        want = N * (K * 2 if bits == 16 else dq_packed_row_bytes(K, bits))
+        if data.nbytes != want:
+            raise ValueError("matrix %r: data holds %d bytes, %d expected" % (name, data.nbytes, want))
+        arr[i].name = raw
+        arr[i].N, arr[i].K, arr[i].bits = N, K, bits
+        arr[i].data = data.ctypes.data
+        if scales is not None:
+            scales = np.ascontiguousarray(scales, dtype=np.float32)
+            if scales.shape != (N,):
+                raise ValueError("matrix %r: scales must be float32 [N]" % name)
+            arr[i].scales = scales.ctypes.data
+        keep.append((data, scales))
+    _check(int(load().dq_file_write(path.encode(), arr, len(matrices))), "dq_file_write")
+
+
+class PackedFile:
+    """A packed-weight file mapped read-only (``dq_file_open``); use as a
+    context manager or call ``close``."""
+
+    def __init__(self, path: str):
+        h = ctypes.c_void_p()
+        _check(int(load().dq_file_open(path.encode(), ctypes.byref(h))), "dq_file_open")
+        self._h = h
+
+    def __len__(self):
+        return int(load().dq_file_count(self._h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def close(self):
+        if self._h:
+            load().dq_file_close(self._h)
+            self._h = ctypes.c_void_p()
+
+    def info(self, i: int):
+        """(name, N, K, bits, data, scales): numpy views into the mapping (valid
+        until ``close``); data is uint32 [N, row_words] or uint16 (bf16) [N, K]."""
+        import numpy as np
+        m = DQFileMatrix()
+        _check(int(load().dq_file_matrix_info(self._h, i, ctypes.byref(m))), "dq_file_matrix_info")
+        N, K, bits = int(m.N), int(m.K), int(m.bits)
+        if bits == 16:
+            data = np.ctypeslib.as_array(ctypes.cast(m.data, ctypes.POINTER(ctypes.c_uint16)),
+                                         shape=(N, K))
+            scales = None
+        else:
+            rw = dq_packed_row_bytes(K, bits) // 4
+            data = np.ctypeslib.as_array(ctypes.cast(m.data, ctypes.POINTER(ctypes.c_uint32)),
+                                         shape=(N, rw))
+            scales = np.ctypeslib.as_array(ctypes.cast(m.scales, ctypes.POINTER(ctypes.c_float)),
+                                           shape=(N,))
+        return m.name.decode("utf-8"), N, K, bits, data, scales
+
+    def verify(self, i: int) -> bool:
+        st = int(load().dq_file_verify(self._h, i))
+        if st == DQ_ERR_FORMAT:
+            return False
+        _check(st, "dq_file_verify")
+        return True
+
+    def load(self, i: int, device="cuda"):
+        """Copy entry i into new GPU tensors: (packed int32 [N, row_words], scales
+        float32 [N]) for bits 2..15, (bf16 [N, K], None) for bits 16.  Waits for
+        the copy, so the tensors are ready when it returns."""
+        torch = _torch()
+        name, N, K, bits, _, _ = self.info(i)
+        dev = torch.device(device)
+        if bits == 16:
+            data = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+            scales = None
+        else:
+            data = torch.empty((N, dq_packed_row_bytes(K, bits) // 4), dtype=torch.int32, device=dev)
+            scales = torch.empty((N,), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        _check(int(load().dq_file_load(self._h, i, data.data_ptr(),
+                                       scales.data_ptr() if scales is not None else 0,
+                                       stream.cuda_stream)), "dq_file_load")
+        stream.synchronize()
+        return data, scales

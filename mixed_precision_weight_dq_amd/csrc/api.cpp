@@ -34,6 +34,8 @@ dq_status check_common(int64_t N, int64_t K, int32_t bits)
 
 }  // namespace
 
+int32_t dq::record_hip_error(hipError_t e) { return hip_status(e); }
+
 extern "C" {
 
 size_t dq_packed_row_bytes(int64_t K, int32_t bits)
@@ -144,7 +146,10 @@ const char* dq_status_string(dq_status status)
     case DQ_ERR_HIP: return "HIP launch or runtime error";
     case DQ_ERR_BUDGET: return "bit budget below every matrix at its lowest level";
     case DQ_ERR_VALUE:
-        return "sensitivity, trace or sum not finite and >= 0, or parameter count out of range";
+        return "sensitivity, trace or sum not finite and >= 0, parameter count out of range, or "
+               "a name without its terminating NUL";
+    case DQ_ERR_IO: return "file could not be opened, written, sized or mapped";
+    case DQ_ERR_FORMAT: return "file is not a packed-weight file of this version, or is corrupt";
     default: return "unknown status";
     }
 }

@@ -24,6 +24,10 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, con
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
                               hipStream_t stream);
 
+// DQ_OK for hipSuccess; otherwise keeps the HIP message for dq_last_error on
+// this thread and returns DQ_ERR_HIP (defined with the C ABI in api.cpp).
+int32_t record_hip_error(hipError_t e);
+
 inline int64_t packed_row_words(int64_t K, int bits)
 {
     return ((K * bits + 7) / 8 + 127) / 128 * 128 / 4;

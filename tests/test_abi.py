@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
                  "dq_status_string", "dq_last_error", "dq_quantize_pack_sumsq", "dq_sensitivity",
-                 "dq_row_sumsq",
+                 "dq_row_sumsq", "dq_file_write", "dq_file_open", "dq_file_count",
+                 "dq_file_matrix_info", "dq_file_verify", "dq_file_load", "dq_file_close",
                  "dq_allocate_bits"):
         assert want in names
 
@@ -52,7 +53,7 @@ def test_row_bytes():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(11):
         assert dq.dq_status_string(s) != "unknown status"
     assert dq.dq_status_string(99) == "unknown status"
     assert dq.dq_last_error() == ""
