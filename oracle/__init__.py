@@ -14,7 +14,10 @@ names the passage it follows:
 * packing -- DynaQuant page (zingnex.cn), "custom kernel architecture" (packed
   N-bit storage) and "status and roadmap" (pack / unpack utilities);
 * matmul -- BPDQ article (devpress.csdn.net) section 3.2 (dequantize fused
-  with the product, fp32 scales, fp32 output), computed here in fp64.
+  with the product, fp32 scales, fp32 output), computed here in fp64;
+* asymmetric variant -- "量化" tutorial, "how quantization works" (a zero
+  point added to the rounded quotient for distributions not centred on zero):
+  per-row scale and zero point, unsigned codes.
 """
 from __future__ import annotations
 
@@ -70,6 +73,12 @@ class Oracle:
         lib.oracle_matmul.restype = None
         lib.oracle_matmul_pairs.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp, i64, vp, vp]
         lib.oracle_matmul_pairs.restype = None
+        lib.oracle_quantize_pack_asym.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
+        lib.oracle_quantize_pack_asym.restype = None
+        lib.oracle_unpack_asym.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp]
+        lib.oracle_unpack_asym.restype = None
+        lib.oracle_matmul_asym.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, vp, vp]
+        lib.oracle_matmul_asym.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -163,6 +172,51 @@ class Oracle:
         return y, bound
 
 
+    # -- asymmetric variant ([TUT] "how quantization works": zero point)
+
+    def quantize_pack_asym(self, w: np.ndarray, bits: int):
+        """Per-row scale and zero point.  Returns (packed uint32 [N, row_bytes/4],
+        scales float32 [N], zeros int32 [N], codes uint32 [N, K])."""
+        _check_bits(bits)
+        w = np.ascontiguousarray(w)
+        dtype = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1}.get(w.dtype)
+        if dtype is None:
+            raise TypeError("w must be float32 or uint16 (bf16 bits)")
+        N, K = w.shape
+        packed = np.empty((N, self.row_bytes(K, bits) // 4), dtype=np.uint32)
+        scales = np.empty((N,), dtype=np.float32)
+        zeros = np.empty((N,), dtype=np.int32)
+        u = np.empty((N, K), dtype=np.uint32)
+        self.lib.oracle_quantize_pack_asym(_ptr(w), dtype, N, K, bits, _ptr(packed), _ptr(scales),
+                                           _ptr(zeros), _ptr(u))
+        return packed, scales, zeros, u
+
+    def unpack_asym(self, packed, scales, zeros, N: int, K: int, bits: int):
+        """(q = u - z int32 [N, K], w_hat = fl32(q * s) float32 [N, K])."""
+        _check_bits(bits)
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        zeros = np.ascontiguousarray(zeros, dtype=np.int32)
+        q = np.empty((N, K), dtype=np.int32)
+        w_hat = np.empty((N, K), dtype=np.float32)
+        self.lib.oracle_unpack_asym(_ptr(packed), _ptr(scales), _ptr(zeros), N, K, bits, _ptr(q),
+                                    _ptr(w_hat))
+        return q, w_hat
+
+    def matmul_asym(self, x_bf16, packed, scales, zeros, N: int, K: int, bits: int):
+        """fp64 y = s * sum x (u - z) and bound = |s| * sum |x (u - z)|, [M, N]."""
+        _check_bits(bits)
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M = x.shape[0]
+        y = np.empty((M, N), dtype=np.float64)
+        bound = np.empty((M, N), dtype=np.float64)
+        self.lib.oracle_matmul_asym(_ptr(x), M, _ptr(np.ascontiguousarray(packed, dtype=np.uint32)),
+                                    _ptr(np.ascontiguousarray(scales, dtype=np.float32)),
+                                    _ptr(np.ascontiguousarray(zeros, dtype=np.int32)), N, K, bits,
+                                    _ptr(y), _ptr(bound))
+        return y, bound
+
+
 def default() -> Oracle:
     """The oracle built from ``dq_oracle.c`` (compiled on first use if absent)."""
     global _default
@@ -199,3 +253,15 @@ def matmul(x_bf16, packed, scales, N: int, K: int, bits: int):
 
 def matmul_pairs(x_bf16, packed, scales, N: int, K: int, bits: int, ms, ns):
     return default().matmul_pairs(x_bf16, packed, scales, N, K, bits, ms, ns)
+
+
+def quantize_pack_asym(w: np.ndarray, bits: int):
+    return default().quantize_pack_asym(w, bits)
+
+
+def unpack_asym(packed, scales, zeros, N: int, K: int, bits: int):
+    return default().unpack_asym(packed, scales, zeros, N, K, bits)
+
+
+def matmul_asym(x_bf16, packed, scales, zeros, N: int, K: int, bits: int):
+    return default().matmul_asym(x_bf16, packed, scales, zeros, N, K, bits)

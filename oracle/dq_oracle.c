@@ -288,6 +288,172 @@ void oracle_matmul(const uint16_t *x, int64_t M, const uint32_t *packed,
     }
 }
 
+/* ---- asymmetric variant ([TUT] "量化怎么工作": a zero point added to the
+ * rounded quotient, for distributions not centred on zero) ---------------- */
+
+/*
+ * Quantize one row to unsigned b-bit codes with a zero point.
+ *   L     = 2^b - 1                       (largest code)
+ *   lo    = min(0, min w), hi = max(0, max w)   (the range holds zero)
+ *   s     = fl32(fl32(hi - lo) / L); if hi == lo the divide uses 1.0
+ *   z     = clip(rint(fl32(-lo / s)), 0, L)
+ *   u[k]  = clip(rint(fl32(w[k] / s)) + z, 0, L)
+ *   w_hat = (u - z) * s
+ * Readings (the pages give only "rounded quotient plus zero point"):
+ *   - the range is widened to hold 0, so w = 0 is exactly representable;
+ *   - a row with a NaN or +-Inf, or whose range overflows fp32, has scale NaN
+ *     and z = every code = 2^(b-1);
+ *   - if the range is > 0 but s underflows to 0, the row is treated like an
+ *     all-zero row (s = fl32(1/L), z = 0, every code 0).
+ */
+static void quantize_row_asym(const void *w, int dtype, int64_t row, int64_t K,
+                              int32_t bits, uint32_t *u, float *scale,
+                              int32_t *zero)
+{
+    const int32_t L = (1 << bits) - 1;
+    const uint32_t half = 1u << (bits - 1);
+    float lo = 0.0f, hi = 0.0f;
+    int nonfinite = 0;
+    for (int64_t k = 0; k < K; k++) {
+        float v = load_weight(w, dtype, row * K + k);
+        if (!isfinite(v))
+            nonfinite = 1;
+        else {
+            if (v < lo)
+                lo = v;
+            if (v > hi)
+                hi = v;
+        }
+    }
+    float range = hi - lo;
+    if (nonfinite || !isfinite(range)) {
+        uint32_t nan_bits = 0x7FC00000u;
+        memcpy(scale, &nan_bits, sizeof *scale);
+        *zero = (int32_t)half;
+        for (int64_t k = 0; k < K; k++)
+            u[k] = half;
+        return;
+    }
+    float s = (range == 0.0f ? 1.0f : range) / (float)L;
+    if (s == 0.0f) {
+        *scale = 1.0f / (float)L;
+        *zero = 0;
+        for (int64_t k = 0; k < K; k++)
+            u[k] = 0;
+        return;
+    }
+    *scale = s;
+    float zf = rintf(-lo / s);
+    if (zf < 0.0f)
+        zf = 0.0f;
+    if (zf > (float)L)
+        zf = (float)L;
+    *zero = (int32_t)zf;
+    for (int64_t k = 0; k < K; k++) {
+        float v = load_weight(w, dtype, row * K + k);
+        float t = v / s;
+        float c = rintf(t) + zf; /* both integers of at most 16 bits: exact */
+        if (c < 0.0f)
+            c = 0.0f;
+        if (c > (float)L)
+            c = (float)L;
+        u[k] = (uint32_t)c;
+    }
+}
+
+/* Pack unsigned codes u (each in [0, 2^b)) bit by bit, as pack_row does for
+ * the offset codes of the symmetric scheme. */
+static void pack_row_unsigned(const uint32_t *u, int64_t K, int32_t bits,
+                              uint32_t *words, int64_t row_words)
+{
+    for (int64_t i = 0; i < row_words; i++)
+        words[i] = 0;
+    for (int64_t k = 0; k < K; k++) {
+        for (int32_t j = 0; j < bits; j++) {
+            int64_t pos = k * bits + j;
+            words[pos / 32] |= ((u[k] >> j) & 1u) << (pos % 32);
+        }
+    }
+}
+
+static void unpack_row_unsigned(const uint32_t *words, int64_t K, int32_t bits,
+                                uint32_t *u)
+{
+    for (int64_t k = 0; k < K; k++) {
+        uint32_t v = 0;
+        for (int32_t j = 0; j < bits; j++) {
+            int64_t pos = k * bits + j;
+            v |= ((words[pos / 32] >> (pos % 32)) & 1u) << j;
+        }
+        u[k] = v;
+    }
+}
+
+/* Quantize [N, K] with per-row scale and zero point; u_out (nullable) gets
+ * the unsigned codes. */
+void oracle_quantize_pack_asym(const void *w, int32_t dtype, int64_t N,
+                               int64_t K, int32_t bits, uint32_t *packed,
+                               float *scales, int32_t *zeros, uint32_t *u_out)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        uint32_t *u = u_out ? u_out + n * K
+                            : (uint32_t *)malloc((size_t)K * sizeof *u);
+        quantize_row_asym(w, dtype, n, K, bits, u, &scales[n], &zeros[n]);
+        pack_row_unsigned(u, K, bits, packed + n * row_words, row_words);
+        if (!u_out)
+            free(u);
+    }
+}
+
+/* Inverse: q_out[n,k] = u - z[n]; w_out (nullable) = fl32((u - z) * s[n]). */
+void oracle_unpack_asym(const uint32_t *packed, const float *scales,
+                        const int32_t *zeros, int64_t N, int64_t K,
+                        int32_t bits, int32_t *q_out, float *w_out)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        uint32_t *u = (uint32_t *)malloc((size_t)K * sizeof *u);
+        unpack_row_unsigned(packed + n * row_words, K, bits, u);
+        for (int64_t k = 0; k < K; k++) {
+            int32_t q = (int32_t)u[k] - zeros[n];
+            q_out[n * K + k] = q;
+            if (w_out)
+                w_out[n * K + k] = (float)q * scales[n];
+        }
+        free(u);
+    }
+}
+
+/* fp64 reference of the asymmetric product:
+ *     y[m,n]     = s[n] * sum_k x[m,k] * (u[n,k] - z[n])
+ *     bound[m,n] = |s[n]| * sum_k |x[m,k] * (u[n,k] - z[n])| */
+void oracle_matmul_asym(const uint16_t *x, int64_t M, const uint32_t *packed,
+                        const float *scales, const int32_t *zeros, int64_t N,
+                        int64_t K, int32_t bits, double *y, double *bound)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; n++) {
+        uint32_t *u = (uint32_t *)malloc((size_t)(K > 0 ? K : 1) * sizeof *u);
+        unpack_row_unsigned(packed + n * row_words, K, bits, u);
+        for (int64_t m = 0; m < M; m++) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)bf16_bits_to_float(x[m * K + k]) *
+                           (double)((int32_t)u[k] - zeros[n]);
+                acc += p;
+                mag += fabs(p);
+            }
+            y[m * N + n] = (double)scales[n] * acc;
+            bound[m * N + n] = fabs((double)scales[n]) * mag;
+        }
+        free(u);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -1,0 +1,200 @@
+"""Pins of the oracle's asymmetric (zero-point) quantizer, and a mutation check
+that plants mistakes in a copy of its C source.  None of the pins re-runs the
+oracle's arithmetic: they use closed forms, exact rational arithmetic and
+invariants that follow from the definition.
+
+Source: "量化" tutorial (aiknowledge.cn), "量化怎么工作": asymmetric
+quantization adds a zero point to the rounded quotient, for distributions not
+centred on zero (its example: non-negative ReLU outputs, where a symmetric
+range wastes half of the codes).  Readings (stated in the oracle): the range
+is widened to hold 0; L = 2^b - 1 codes above 0; s = fl32(range / L);
+z = rint(-lo / s); codes rint(w / s) + z clipped to [0, L]."""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dq_oracle.c")
+
+
+def f32(v):
+    return np.float32(v)
+
+
+def check_nonnegative_rows(orc) -> list[str]:
+    """A non-negative row (the page's ReLU case) needs no negative codes: the
+    zero point is 0, the largest element takes the top code L, the zeros code
+    0, and every code is the nearest integer to fl32(w / s) (ties to even)."""
+    bad = []
+    rng = np.random.default_rng(21)
+    for bits in (2, 4, 5, 8, 11, 15):
+        L = (1 << bits) - 1
+        w = np.abs(rng.standard_normal((3, 37))).astype(np.float32)
+        w[:, 5] = 0.0
+        packed, s, z, u = orc.quantize_pack_asym(w, bits)
+        for n in range(3):
+            if z[n] != 0:
+                bad.append("b=%d nonneg row %d: zero point %d" % (bits, n, z[n]))
+            if u[n, int(np.argmax(w[n]))] != L or u[n, 5] != 0:
+                bad.append("b=%d nonneg row %d: max/zero codes" % (bits, n))
+            # the scale: fl32(max / L), as an exact rational rounded once
+            want_s = f32(float(Fraction(float(w[n].max())) / L))
+            if s[n] != want_s and abs(Fraction(float(s[n])) - Fraction(float(w[n].max())) / L) > \
+                    abs(Fraction(float(want_s)) - Fraction(float(w[n].max())) / L):
+                bad.append("b=%d nonneg row %d: scale %r" % (bits, n, s[n]))
+            for k in range(37):
+                t = Fraction(float(f32(w[n, k]) / s[n]))
+                c = int(u[n, k])
+                d = abs(t - c)
+                if d > Fraction(1, 2) or (d == Fraction(1, 2) and c % 2):
+                    bad.append("b=%d nonneg code %d,%d" % (bits, n, k))
+                    break
+        # exact ties: the top element L * 2^-6 makes s = 2^-6 exactly, so
+        # (j + 1/2) * 2^-6 sits halfway between codes j and j + 1: the even one
+        s0 = 2.0 ** -6
+        js = np.arange(min(L, 40))
+        row = np.concatenate([[L * s0], (js + 0.5) * s0]).astype(np.float32)[None, :]
+        _, s1, z1, u1 = orc.quantize_pack_asym(row, bits)
+        want = np.where(js % 2 == 0, js, js + 1)
+        if s1[0] != f32(s0) or z1[0] != 0 or not np.array_equal(u1[0, 1:], want):
+            bad.append("b=%d ties" % bits)
+    return bad
+
+
+def check_nonpositive_rows(orc) -> list[str]:
+    """A non-positive row: the zero point is L and the smallest element gets
+    code 0 (-lo / s lies within L * 2^-24 of L)."""
+    bad = []
+    rng = np.random.default_rng(22)
+    for bits in (3, 6, 9, 14):
+        L = (1 << bits) - 1
+        w = -np.abs(rng.standard_normal((2, 29))).astype(np.float32)
+        _, s, z, u = orc.quantize_pack_asym(w, bits)
+        for n in range(2):
+            if z[n] != L or u[n, int(np.argmin(w[n]))] != 0:
+                bad.append("b=%d nonpos row %d: z=%d" % (bits, n, z[n]))
+    return bad
+
+
+def check_error_bound(orc) -> list[str]:
+    """|w - (u - z) s| <= s (1 + 2^-20): half a step from rounding w / s and half
+    a step from rounding the zero point, plus the fp32 roundings."""
+    bad = []
+    for bits in range(2, 16):
+        w = workload.weights(97, bits, 8, 300, dtype="f32")
+        w[1] += np.float32(0.05)  # shifted rows: the zero point moves
+        w[2] = np.abs(w[2])
+        packed, s, z, u = orc.quantize_pack_asym(w, bits)
+        for n in range(8):
+            err = np.abs(w[n].astype(np.float64) - (u[n].astype(np.float64) - z[n]) * float(s[n]))
+            if err.max() > float(s[n]) * (1 + 2 ** -20):
+                bad.append("b=%d row %d error %g > s %g" % (bits, n, err.max(), s[n]))
+            if u[n].max() >= (1 << bits) or z[n] < 0 or z[n] >= (1 << bits):
+                bad.append("b=%d row %d out of range" % (bits, n))
+    return bad
+
+
+def check_special_rows(orc) -> list[str]:
+    bad = []
+    for bits in (2, 7, 15):
+        L = (1 << bits) - 1
+        half = 1 << (bits - 1)
+        w = np.zeros((4, 5), np.float32)
+        w[1, 2] = np.nan
+        w[2] = [3e38, -1e38, 0, 1, 2]          # range overflows fp32
+        w[3] = [1.4e-45, 0, 0, 0, 0]            # one subnormal step: range / L underflows
+        _, s, z, u = orc.quantize_pack_asym(w, bits)
+        if not (s[0] == f32(1.0) / f32(L) and z[0] == 0 and not u[0].any()):
+            bad.append("b=%d zero row" % bits)
+        for n in (1, 2):
+            if not (np.isnan(s[n]) and z[n] == half and (u[n] == half).all()):
+                bad.append("b=%d non-finite row %d" % (bits, n))
+        if not (s[3] == f32(1.0) / f32(L) and z[3] == 0 and not u[3].any()):
+            bad.append("b=%d underflow row" % bits)
+    return bad
+
+
+def check_unpack_and_matmul(orc) -> list[str]:
+    """Unpack gives u - z and fl32((u - z) s); the fp64 product equals the exact
+    rational s * sum x (u - z) (N, K small), and a one-hot x picks one weight."""
+    bad = []
+    for bits in (2, 5, 8, 12, 15):
+        w = workload.weights(98, bits, 5, 7, dtype="f32")
+        w[0] = np.abs(w[0])
+        packed, s, z, u = orc.quantize_pack_asym(w, bits)
+        q, w_hat = orc.unpack_asym(packed, s, z, 5, 7, bits)
+        if not np.array_equal(q, u.astype(np.int64) - z[:, None]):
+            bad.append("b=%d unpack codes" % bits)
+        if not np.array_equal(w_hat, q.astype(np.float32) * s[:, None]):
+            bad.append("b=%d unpack dequant" % bits)
+        x = workload.activations(98, bits, 3, 7)
+        xf = workload.bf16_to_f32(x)
+        y, bound = orc.matmul_asym(x, packed, s, z, 5, 7, bits)
+        for m in range(3):
+            for n in range(5):
+                acc = sum(Fraction(float(xf[m, k])) * (int(u[n, k]) - int(z[n])) for k in range(7))
+                mag = sum(abs(Fraction(float(xf[m, k])) * (int(u[n, k]) - int(z[n]))) for k in range(7))
+                if y[m, n] != float(Fraction(float(s[n])) * acc) or \
+                        bound[m, n] != float(abs(Fraction(float(s[n]))) * mag):
+                    bad.append("b=%d matmul (%d,%d)" % (bits, m, n))
+        onehot = np.zeros((1, 7), np.uint16)
+        onehot[0, 3] = 0x3F80  # 1.0
+        y, _ = orc.matmul_asym(onehot, packed, s, z, 5, 7, bits)
+        if not np.array_equal(y[0].astype(np.float32), w_hat[:, 3]):
+            bad.append("b=%d one-hot" % bits)
+    return bad
+
+
+CHECKS = [check_nonnegative_rows, check_nonpositive_rows, check_error_bound, check_special_rows,
+          check_unpack_and_matmul]
+
+
+def run_all(orc) -> list[str]:
+    bad = []
+    for c in CHECKS:
+        bad += c(orc)
+    return bad
+
+
+@pytest.mark.parametrize("check", CHECKS)
+def test_asym_oracle_pinned(check):
+    assert check(oracle.default()) == []
+
+
+MUTANTS = [
+    ("levels_minus_one", "const int32_t L = (1 << bits) - 1;", "const int32_t L = (1 << bits) - 2;"),
+    ("range_without_zero", "float lo = 0.0f, hi = 0.0f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;",
+     "float lo = 1e30f, hi = -1e30f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;"),
+    ("zero_point_truncated", "float zf = rintf(-lo / s);", "float zf = truncf(-lo / s);"),
+    ("zero_point_subtracted", "float c = rintf(t) + zf;", "float c = rintf(t) - zf;"),
+    ("codes_round_half_up", "float c = rintf(t) + zf;", "float c = roundf(t) + zf;"),
+    ("nonfinite_zero_point_0", "*zero = (int32_t)half;", "*zero = 0;"),
+    ("unpack_adds_zero", "int32_t q = (int32_t)u[k] - zeros[n];", "int32_t q = (int32_t)u[k] + zeros[n];"),
+    ("matmul_ignores_zero", "(double)((int32_t)u[k] - zeros[n]);", "(double)((int32_t)u[k]);"),
+    ("unsigned_pack_msb_first", "words[pos / 32] |= ((u[k] >> j) & 1u) << (pos % 32);",
+     "words[pos / 32] |= ((u[k] >> (bits - 1 - j)) & 1u) << (pos % 32);"),
+]
+
+
+def test_asym_pins_accept_the_oracle():
+    assert run_all(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_asym_pins_reject_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not unique/found: %s" % name
+    mut = tmp_path / ("oracle_%s.c" % name)
+    mut.write_text(src.replace(old, new))
+    path = oracle.build(force=True, src=str(mut), out=str(tmp_path / ("lib_%s.so" % name)))
+    try:
+        bad = run_all(oracle.Oracle(path))
+    except Exception as e:  # a mutant may also crash a check outright
+        bad = ["raised %r" % e]
+    assert bad, "mutant %s passed every pin" % name
