@@ -351,8 +351,8 @@ static void quantize_row_asym(const void *w, int dtype, int64_t row, int64_t K,
     *zero = (int32_t)zf;
     for (int64_t k = 0; k < K; k++) {
         float v = load_weight(w, dtype, row * K + k);
-        float t = v / s;
-        float c = rintf(t) + zf; /* both integers of at most 16 bits: exact */
+        float quot = v / s;     /* one IEEE fp32 divide */
+        float c = rintf(quot) + zf; /* both integers of at most 16 bits: exact */
         if (c < 0.0f)
             c = 0.0f;
         if (c > (float)L)

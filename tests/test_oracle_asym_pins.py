@@ -172,8 +172,8 @@ MUTANTS = [
     ("range_without_zero", "float lo = 0.0f, hi = 0.0f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;",
      "float lo = 1e30f, hi = -1e30f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;"),
     ("zero_point_truncated", "float zf = rintf(-lo / s);", "float zf = truncf(-lo / s);"),
-    ("zero_point_subtracted", "float c = rintf(t) + zf;", "float c = rintf(t) - zf;"),
-    ("codes_round_half_up", "float c = rintf(t) + zf;", "float c = roundf(t) + zf;"),
+    ("zero_point_subtracted", "float c = rintf(quot) + zf;", "float c = rintf(quot) - zf;"),
+    ("codes_round_half_up", "float c = rintf(quot) + zf;", "float c = roundf(quot) + zf;"),
     ("nonfinite_zero_point_0", "*zero = (int32_t)half;", "*zero = 0;"),
     ("unpack_adds_zero", "int32_t q = (int32_t)u[k] - zeros[n];", "int32_t q = (int32_t)u[k] + zeros[n];"),
     ("matmul_ignores_zero", "(double)((int32_t)u[k] - zeros[n]);", "(double)((int32_t)u[k]);"),
