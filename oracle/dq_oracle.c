@@ -440,15 +440,15 @@ void oracle_matmul_asym(const uint16_t *x, int64_t M, const uint32_t *packed,
         uint32_t *u = (uint32_t *)malloc((size_t)(K > 0 ? K : 1) * sizeof *u);
         unpack_row_unsigned(packed + n * row_words, K, bits, u);
         for (int64_t m = 0; m < M; m++) {
-            double acc = 0.0, mag = 0.0;
+            double sum = 0.0, absum = 0.0;
             for (int64_t k = 0; k < K; k++) {
-                double p = (double)bf16_bits_to_float(x[m * K + k]) *
-                           (double)((int32_t)u[k] - zeros[n]);
-                acc += p;
-                mag += fabs(p);
+                double term = (double)bf16_bits_to_float(x[m * K + k]) *
+                              (double)((int32_t)u[k] - zeros[n]);
+                sum += term;
+                absum += fabs(term);
             }
-            y[m * N + n] = (double)scales[n] * acc;
-            bound[m * N + n] = fabs((double)scales[n]) * mag;
+            y[m * N + n] = (double)scales[n] * sum;
+            bound[m * N + n] = fabs((double)scales[n]) * absum;
         }
         free(u);
     }
