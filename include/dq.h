@@ -103,6 +103,44 @@ size_t dq_packed_row_bytes(int64_t K, int32_t bits);
 dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
                            uint32_t* packed, float* scales, void* stream);
 
+/* Asymmetric variant ("量化" tutorial, "量化怎么工作": a zero point added to
+ * the rounded quotient, for distributions not centred on zero).  Per row n,
+ * with L = 2^b - 1:  lo = min(0, min_k W), hi = max(0, max_k W);
+ * s[n] = fl32(fl32(hi - lo) / L) (1.0 replaces a zero range);
+ * z[n] = clip(rint(fl32(-lo / s)), 0, L);
+ * code u = clip(rint(fl32(W / s)) + z, 0, L), stored unsigned in the same
+ * packed layout (no offset added); w_hat = (u - z) * s.
+ *   zeros   out  device, [N] int32 zero points
+ * A row with a NaN or +-Inf, or whose range overflows fp32, gets s = NaN and
+ * z = every code = 2^(b-1); a row whose s underflows to 0 gets s = fl32(1/L),
+ * z = 0 and codes 0. */
+dq_status dq_quantize_pack_asym(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                int32_t bits, uint32_t* packed, float* scales, int32_t* zeros,
+                                void* stream);
+
+/* Inverse of dq_quantize_pack_asym: q_out = u - zeros[n] (int32), w_out =
+ * fl32(q * s[n]); arguments as for dq_unpack plus zeros (device, [N]). */
+dq_status dq_unpack_asym(const uint32_t* packed, const float* scales, const int32_t* zeros,
+                         int64_t N, int64_t K, int32_t bits, int32_t* q_out, float* w_out,
+                         void* stream);
+
+/* xsum[m] = sum_k x[m, k] (device, fp32 [M]; summed in fp64 in a fixed order
+ * and rounded once), the activation term the asymmetric products need; one
+ * call serves every matrix that multiplies the same x. */
+dq_status dq_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, void* stream);
+
+/* Asymmetric products: y[m,n] = s[n] * sum_k x[m,k] (u[n,k] - z[n]), computed
+ * as s[n] * (sum_k x (u - 2^(b-1)) + (2^(b-1) - z[n]) * xsum[m]) with the
+ * kernels of dq_gemv / dq_gemm (same M ranges and layouts; zeros [N] int32
+ * and xsum [M] fp32 from dq_x_sum of the same x, both device, 4-byte
+ * aligned). */
+dq_status dq_gemv_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
+                       float* y, void* stream);
+dq_status dq_gemm_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
+                       float* y, void* stream);
+
 /* The statistic a matrix's sensitivity needs (DynaQuant page, "第一步：敏感度
  * 测量": mean(w^2) of the matrix), measured before any width is chosen: one
  * read of W.

@@ -13,6 +13,8 @@ kernels behind the C ABI declared in ``include/dq.h``):
   ``stream_read`` -- the same calls on torch tensors (torch provides device
   memory and the current stream); they check device, dtype and contiguity,
   allocate outputs with torch and raise ``DQError`` on a non-zero status.
+* ``quantize_pack_asym``, ``unpack_asym``, ``x_sum``, ``gemv_asym``,
+  ``gemm_asym`` -- the asymmetric (zero-point) variant on torch tensors.
 * ``sensitivity``, ``allocate_bits`` -- the host-side allocation calls on
   numpy arrays (the recipe: one bit width per matrix).
 * ``write_packed_file``, ``PackedFile`` -- the on-disk packed-weight format
@@ -36,7 +38,9 @@ __all__ = [
     "packed_row_bytes", "quantize_pack", "unpack", "gemv", "gemm", "stream_read", "load",
     "dq_row_sumsq", "row_sumsq", "dq_quantize_pack_sumsq", "dq_sensitivity", "dq_allocate_bits", "quantize_pack_sumsq",
     "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS", "DQFileMatrix",
-    "write_packed_file", "PackedFile",
+    "write_packed_file", "PackedFile", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
+    "dq_gemv_asym", "dq_gemm_asym", "quantize_pack_asym", "unpack_asym", "x_sum", "gemv_asym",
+    "gemm_asym",
 ]
 
 (DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP,
@@ -90,6 +94,16 @@ def load():
     lib.dq_stream_read.restype = st
     lib.dq_row_sumsq.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     lib.dq_row_sumsq.restype = st
+    lib.dq_quantize_pack_asym.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
+    lib.dq_quantize_pack_asym.restype = st
+    lib.dq_unpack_asym.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp]
+    lib.dq_unpack_asym.restype = st
+    lib.dq_x_sum.argtypes = [vp, i64, i64, vp, vp]
+    lib.dq_x_sum.restype = st
+    lib.dq_gemv_asym.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemv_asym.restype = st
+    lib.dq_gemm_asym.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemm_asym.restype = st
     fp = ctypes.POINTER(DQFileMatrix)
     lib.dq_file_write.argtypes = [ctypes.c_char_p, fp, i64]
     lib.dq_file_write.restype = st
@@ -128,6 +142,30 @@ def dq_packed_row_bytes(K: int, bits: int) -> int:
 def dq_quantize_pack(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int, scales: int,
                      stream: int = 0) -> int:
     return int(load().dq_quantize_pack(w, w_dtype, N, K, bits, packed, scales, stream))
+
+
+def dq_quantize_pack_asym(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int,
+                          scales: int, zeros: int, stream: int = 0) -> int:
+    return int(load().dq_quantize_pack_asym(w, w_dtype, N, K, bits, packed, scales, zeros, stream))
+
+
+def dq_unpack_asym(packed: int, scales: int, zeros: int, N: int, K: int, bits: int, q_out: int,
+                   w_out: int, stream: int = 0) -> int:
+    return int(load().dq_unpack_asym(packed, scales, zeros, N, K, bits, q_out, w_out, stream))
+
+
+def dq_x_sum(x: int, M: int, K: int, xsum: int, stream: int = 0) -> int:
+    return int(load().dq_x_sum(x, M, K, xsum, stream))
+
+
+def dq_gemv_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int, N: int, K: int,
+                 bits: int, y: int, stream: int = 0) -> int:
+    return int(load().dq_gemv_asym(x, M, packed, scales, zeros, xsum, N, K, bits, y, stream))
+
+
+def dq_gemm_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int, N: int, K: int,
+                 bits: int, y: int, stream: int = 0) -> int:
+    return int(load().dq_gemm_asym(x, M, packed, scales, zeros, xsum, N, K, bits, y, stream))
 
 
 def dq_row_sumsq(w: int, w_dtype: int, N: int, K: int, row_sumsq: int, matrix_sumsq: int,
@@ -235,6 +273,89 @@ def quantize_pack(w, bits: int, packed=None, scales=None):
     _check(dq_quantize_pack(w.data_ptr(), dt, N, K, bits, packed.data_ptr(), scales.data_ptr(),
                             _stream(w)), "dq_quantize_pack")
     return packed, scales
+
+
+def quantize_pack_asym(w, bits: int):
+    """Asymmetric per-row quantization: W[N, K] (float32 / bfloat16, GPU) ->
+    (packed int32 [N, row_words] holding unsigned codes, scales float32 [N],
+    zeros int32 [N])."""
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16), 2)
+    N, K = w.shape
+    packed = torch.empty((N, packed_row_bytes(K, bits) // 4), dtype=torch.int32, device=w.device)
+    scales = torch.empty((N,), dtype=torch.float32, device=w.device)
+    zeros = torch.empty((N,), dtype=torch.int32, device=w.device)
+    dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
+    _check(dq_quantize_pack_asym(w.data_ptr(), dt, N, K, bits, packed.data_ptr(), scales.data_ptr(),
+                                 zeros.data_ptr(), _stream(w)), "dq_quantize_pack_asym")
+    return packed, scales, zeros
+
+
+def unpack_asym(packed, scales, zeros, K: int, bits: int, want_q: bool = True,
+                want_w: bool = False):
+    """(q = u - z int32 [N, K] or None, w_hat float32 [N, K] or None)."""
+    torch = _torch()
+    _need(packed, "packed", (torch.int32,), 2)
+    _need(zeros, "zeros", (torch.int32,), 1)
+    N = packed.shape[0]
+    if packed.shape[1] != packed_row_bytes(K, bits) // 4 or zeros.shape[0] != N:
+        raise ValueError("packed / zeros do not match N, K and bits")
+    q = torch.empty((N, K), dtype=torch.int32, device=packed.device) if want_q else None
+    w = torch.empty((N, K), dtype=torch.float32, device=packed.device) if want_w else None
+    if scales is not None:
+        _need(scales, "scales", (torch.float32,), 1)
+    _check(dq_unpack_asym(packed.data_ptr(), scales.data_ptr() if scales is not None else 0,
+                          zeros.data_ptr(), N, K, bits, q.data_ptr() if q is not None else 0,
+                          w.data_ptr() if w is not None else 0, _stream(packed)), "dq_unpack_asym")
+    return q, w
+
+
+def x_sum(x, xsum=None):
+    """sum_k x[m, k] for bf16 x [M, K] on the GPU -> float32 [M]."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    M, K = x.shape
+    if xsum is None:
+        xsum = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _need(xsum, "xsum", (torch.float32,), 1)
+    if xsum.shape[0] != M:
+        raise ValueError("xsum must be [M]")
+    _check(dq_x_sum(x.data_ptr(), M, K, xsum.data_ptr(), _stream(x)), "dq_x_sum")
+    return xsum
+
+
+def _matmul_asym(fn, name, x, packed, scales, zeros, xsum, K: int, bits: int, y=None):
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(packed, "packed", (torch.int32,), 2)
+    _need(scales, "scales", (torch.float32,), 1)
+    _need(zeros, "zeros", (torch.int32,), 1)
+    M, N = x.shape[0], packed.shape[0]
+    if xsum is None:
+        xsum = x_sum(x)
+    _need(xsum, "xsum", (torch.float32,), 1)
+    if (x.shape[1] != K or packed.shape[1] != packed_row_bytes(K, bits) // 4
+            or scales.shape[0] != N or zeros.shape[0] != N or xsum.shape[0] != M):
+        raise ValueError("shape mismatch between x, packed, scales, zeros, xsum, K and bits")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(fn(x.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+              xsum.data_ptr(), N, K, bits, y.data_ptr(), _stream(x)), name)
+    return y
+
+
+def gemv_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
+    """y = s * x . (u - z)^T for 1 <= M <= 16; xsum (from ``x_sum``) is computed
+    when not given."""
+    return _matmul_asym(dq_gemv_asym, "dq_gemv_asym", x, packed, scales, zeros, xsum, K, bits, y)
+
+
+def gemm_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
+    """y = s * x . (u - z)^T on the matrix cores (any M >= 1)."""
+    return _matmul_asym(dq_gemm_asym, "dq_gemm_asym", x, packed, scales, zeros, xsum, K, bits, y)
 
 
 def row_sumsq(w, want_total: bool = True):

@@ -92,8 +92,44 @@ dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int6
     if (st != DQ_OK) return st;
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(q_out, 4) || !aligned(w_out, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_unpack(packed, scales, N, K, bits, q_out, w_out,
+    return hip_status(dq::launch_unpack(packed, scales, nullptr, N, K, bits, q_out, w_out,
                                         static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_quantize_pack_asym(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                                uint32_t* packed, float* scales, int32_t* zeros, void* stream)
+{
+    if (!w || !packed || !scales || !zeros) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_quantize_pack_asym(w, w_dtype == DQ_BF16, N, K, bits, packed,
+                                                    scales, zeros,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_unpack_asym(const uint32_t* packed, const float* scales, const int32_t* zeros,
+                         int64_t N, int64_t K, int32_t bits, int32_t* q_out, float* w_out,
+                         void* stream)
+{
+    if (!packed || !zeros || (!q_out && !w_out) || (w_out && !scales)) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(q_out, 4) ||
+        !aligned(w_out, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_unpack(packed, scales, zeros, N, K, bits, q_out, w_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, void* stream)
+{
+    if (!x || !xsum) return DQ_ERR_NULL;
+    if (M < 1 || M > 0x7fffffffLL || K < 1 || K > DQ_MAX_K) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(xsum, 4)) return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_x_sum(x, M, K, xsum, static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
@@ -105,8 +141,23 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
     if (M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(
-        dq::launch_gemv(x, M, packed, scales, N, K, bits, y, static_cast<hipStream_t>(stream)));
+    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemv_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
+                       float* y, void* stream)
+{
+    if (!x || !packed || !scales || !zeros || !xsum || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4) ||
+        !aligned(zeros, 4) || !aligned(xsum, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, zeros, xsum,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
@@ -118,8 +169,23 @@ dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
     if (M < 1 || M > 0x7fffffffLL) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(
-        dq::launch_gemm(x, M, packed, scales, N, K, bits, y, static_cast<hipStream_t>(stream)));
+    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemm_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
+                       float* y, void* stream)
+{
+    if (!x || !packed || !scales || !zeros || !xsum || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > 0x7fffffffLL) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4) ||
+        !aligned(zeros, 4) || !aligned(xsum, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, zeros, xsum,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,

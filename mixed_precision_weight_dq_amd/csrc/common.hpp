@@ -153,4 +153,29 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
+// Zero points of the asymmetric scheme, for the products' epilogues.  Codes
+// are stored unsigned, u = rint(w / s) + z[n]; every product kernel sums
+// x * (u - 2^(b-1)) (the two's-complement view of the code), so adding
+// (2^(b-1) - z[n]) * sum_k x[m, k] gives sum_k x * (u - z[n]).  The product
+// kernels take the type as a template parameter: NoZeroPoints (the symmetric
+// scheme) adds nothing and compiles to the plain epilogue.
+struct NoZeroPoints {
+    template <int B>
+    __device__ __forceinline__ float add(float v, int64_t, int64_t) const
+    {
+        return v;
+    }
+};
+
+struct ZeroPoints {
+    const int32_t* zeros;  // [N]
+    const float* xsum;     // [M]: sum_k x[m, k]
+
+    template <int B>
+    __device__ __forceinline__ float add(float v, int64_t n, int64_t m) const
+    {
+        return fmaf((float)((1 << (B - 1)) - zeros[n]), xsum[m], v);
+    }
+};
+
 }  // namespace dq

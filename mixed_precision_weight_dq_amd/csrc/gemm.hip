@@ -41,11 +41,11 @@ __device__ __forceinline__ uint16_t exact_bf16_bits(int32_t v)
     return (uint16_t)(__float_as_uint((float)v) >> 16);
 }
 
-template <int B>
+template <int B, class ZP>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     constexpr bool kSplit = B >= 10;
     constexpr int kPlanes = kSplit ? 2 : 1;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-                if (m < M) y[m * N + n] = s * acc[i][j][r];
+                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r], n, m);
             }
         }
     }
@@ -205,11 +205,11 @@ struct MfmaTile {
 
 __device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
 
-template <int B, int kMT, int kNT, int kOcc>
+template <int B, int kMT, int kNT, int kOcc, class ZP>
 __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     using T = MfmaTile<kMT, kNT>;
     constexpr bool kSplit = B >= 10;
@@ -355,8 +355,10 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
                 float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    __builtin_nontemporal_store(s * (acc[i][j][r] * kUnscale),
-                                                yp + (8 * (r >> 2) + (r & 3)) * N);
+                    __builtin_nontemporal_store(
+                        s * zp.template add<B>(acc[i][j][r] * kUnscale, n,
+                                      m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                        yp + (8 * (r >> 2) + (r & 3)) * N);
             }
         }
         return;
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
+                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r] * kUnscale, n, m);
             }
         }
     }
@@ -406,11 +408,11 @@ struct WideTile {
     static constexpr int kPieces = BM * 8;  // 16-byte pieces of one x tile
 };
 
-template <int B, int kNT, int kDepth>
+template <int B, int kNT, int kDepth, class ZP>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     using T = WideTile<kNT>;
     constexpr int kStages = kDepth + 1;  // x (LDS) and code (register) stages
@@ -621,7 +623,10 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    buf_store_f32_nt(yb, s * (acc[i][j][r] * kUnscale), voff,
+                    buf_store_f32_nt(yb,
+                                     s * zp.template add<B>(acc[i][j][r] * kUnscale, n,
+                                                   m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                                     voff,
                                      (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * row4);
         }
         return;
@@ -636,41 +641,43 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
+                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r] * kUnscale, n, m);
             }
         }
     }
 }
 
-template <int B, int kNT, int kDepth>
+template <int B, int kNT, int kDepth, class ZP>
 hipError_t launch_gemm_wide(const uint16_t* x, int64_t M, const uint32_t* packed,
-                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                            const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                            hipStream_t stream)
 {
     using T = WideTile<kNT>;
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, T::BN) * ceil_div(M, T::BM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    gemm_wide_kernel<B, kNT, kDepth><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(x, M, packed, scales, N,
-                                                                             K, rw, y);
+    gemm_wide_kernel<B, kNT, kDepth><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
+        x, M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
 }
 
-template <int B, int kMT, int kNT, int kOcc>
+template <int B, int kMT, int kNT, int kOcc, class ZP>
 hipError_t launch_gemm_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
-                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                            const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                            hipStream_t stream)
 {
     using T = MfmaTile<kMT, kNT>;
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, T::BN) * ceil_div(M, T::BM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     gemm_mfma_kernel<B, kMT, kNT, kOcc><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
-        x, M, packed, scales, N, K, rw, y);
+        x, M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
 }
 
-template <int B>
+template <int B, class ZP>
 hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                         int64_t N, int64_t K, float* y, hipStream_t stream)
+                         int64_t N, int64_t K, float* y, ZP zp, hipStream_t stream)
 {
     if (K % 64 == 0) {
         // 256-row tiles with one workgroup per CU when they fill the 256 CUs
@@ -678,7 +685,7 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
         constexpr int kWideNT = B <= 8 ? 2 : 1;
         const int64_t wide = ceil_div(M, 256) * ceil_div(N, WideTile<kWideNT>::BN);
         if (M >= 256 && wide >= 256 && wide * 5 >= ceil_div(wide, 256) * 256 * 4)
-            return launch_gemm_wide<B, kWideNT, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, stream);
+            return launch_gemm_wide<B, kWideNT, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, zp, stream);
         // 256 x 128 tiles when the wider ones are too few (e.g. M = 256 with N
         // in the tens of thousands): taken when they fill the CUs in at most
         // two rounds, at least 85 % busy; one row tile then reads each code
@@ -686,31 +693,39 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
         const int64_t wide1 = ceil_div(M, 256) * ceil_div(N, WideTile<1>::BN);
         const int64_t rounds1 = ceil_div(wide1, 256);
         if (M >= 256 && rounds1 <= 2 && wide1 * 20 >= rounds1 * 256 * 17)
-            return launch_gemm_wide<B, 1, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, stream);
+            return launch_gemm_wide<B, 1, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, zp, stream);
         // 128 x 256 tiles (codes up to 8 bits: wider ones need more registers
         // than two workgroups per CU leave), when they fill the 256 CUs twice
         // over; else 128 x 128
         if constexpr (B <= 8) {
             if (ceil_div(M, 128) * ceil_div(N, 256) >= 400)
                 return launch_gemm_mfma<B, DQ_GEMM_MT, DQ_GEMM_NT, DQ_GEMM_OCC>(x, M, packed, scales,
-                                                                               N, K, y, stream);
+                                                                               N, K, y, zp, stream);
         }
-        return launch_gemm_mfma<B, 4, 1, 2>(x, M, packed, scales, N, K, y, stream);
+        return launch_gemm_mfma<B, 4, 1, 2>(x, M, packed, scales, N, K, y, zp, stream);
     }
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, kBN) * ceil_div(M, kBM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles);
-    gemm_kernel<B><<<grid, dim3(kGemmThreads), 0, stream>>>(x, M, packed, scales, N, K, rw, y);
+    gemm_kernel<B><<<grid, dim3(kGemmThreads), 0, stream>>>(x, M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       int64_t N, int64_t K, int bits, float* y, hipStream_t stream)
+                       int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
+                       const float* xsum, hipStream_t stream)
 {
-#define CALL(B) launch_gemm_b<B>(x, M, packed, scales, N, K, y, stream)
+    if (zeros) {
+        const ZeroPoints zp{zeros, xsum};
+#define CALL(B) launch_gemm_b<B>(x, M, packed, scales, N, K, y, zp, stream)
+        DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+    }
+    const NoZeroPoints zp{};
+#define CALL(B) launch_gemm_b<B>(x, M, packed, scales, N, K, y, zp, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
 }

@@ -202,11 +202,11 @@ __device__ __forceinline__ void chunk_fma(const uint32_t (&w)[B], const uint32_t
     }
 }
 
-template <int B, int MT, int kRows, int kWaves, bool kAligned>
+template <int B, int MT, int kRows, int kWaves, bool kAligned, class ZP>
 __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     constexpr int kThreads = kWaves * kWave;
     constexpr int kXPerThread = kSlice * kChunk / kThreads;  // x elements staged per thread
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
                 const float s = scales[n];
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    if (m < M) y[(int64_t)m * N + n] = s * (acc[r][m] * kUnscale);
+                    if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(acc[r][m] * kUnscale, n, m);
             }
         }
     }
@@ -394,11 +394,11 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 #endif
 constexpr int kGemvMfmaWaves = DQ_GEMV_MFMA_WAVES;
 
-template <int B, int kNT, int kDepth>
+template <int B, int kNT, int kDepth, class ZP>
 __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
     typedef float f32x4m_t __attribute__((ext_vector_type(4)));
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
+                if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(v * kUnscale, n, m);
             }
         }
     }
@@ -550,11 +550,11 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
 template <int B>
 constexpr int words_loads() { return B / 4 + (B % 4 != 0 ? 1 : 0); }
 
-template <int B, int kNT, int kDepth, int kMR>
+template <int B, int kNT, int kDepth, int kMR, class ZP>
 __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
     typedef float f32x4m_t __attribute__((ext_vector_type(4)));
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
+                if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(v * kUnscale, n, m);
             }
         }
     }
@@ -733,35 +733,37 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 #define DQ_GEMV_MFMA_DEPTH 2
 #endif
 
-template <int B, int kNT>
+template <int B, int kNT, class ZP>
 hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* packed,
-                               const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                               const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 16 * kNT)), block(kGemvMfmaWaves * kWave);
     if (K % kChunk == 0 && M <= 8)
         gemv_mfma_xlds_kernel<B, kNT, 2, 8><<<grid, block, 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
+            x, (int)M, packed, scales, N, K, rw, y, zp);
     else if (K % kChunk == 0)  // twice the x per stage: one step ahead, so two workgroups fit per CU
         gemv_mfma_xlds_kernel<B, kNT, 1, 16><<<grid, block, 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
+            x, (int)M, packed, scales, N, K, rw, y, zp);
     else
         gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH><<<grid, block, 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
+            x, (int)M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
 }
 
 // 32 rows per workgroup (x fragments shared by two row tiles) above 2^24
 // weights, where there are workgroups enough for every CU; 16 rows below
-template <int B>
+template <int B, class ZP>
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
-                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                            const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                hipStream_t stream)
 {
 #ifndef DQ_GEMV_MFMA_NT2_MIN
 #define DQ_GEMV_MFMA_NT2_MIN (1LL << 24)
 #endif
-    if (N * K > DQ_GEMV_MFMA_NT2_MIN) return launch_gemv_mfma_nt<B, 2>(x, M, packed, scales, N, K, y, stream);
-    return launch_gemv_mfma_nt<B, 1>(x, M, packed, scales, N, K, y, stream);
+    if (N * K > DQ_GEMV_MFMA_NT2_MIN) return launch_gemv_mfma_nt<B, 2>(x, M, packed, scales, N, K, y, zp, stream);
+    return launch_gemv_mfma_nt<B, 1>(x, M, packed, scales, N, K, y, zp, stream);
 }
 
 #ifndef DQ_GEMV_ROWS_NARROW
@@ -783,11 +785,11 @@ hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed
 // (waiting only for x), then the slice loop.
 constexpr int kXResMax = 48 * 1024;
 
-template <int B, int MT, int kWaves, int kR>
+template <int B, int MT, int kWaves, int kR, class ZP>
 __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y)
+    float* __restrict__ y, ZP zp)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
     constexpr int kThreads = kWaves * kWave;
@@ -868,7 +870,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
         const float s = scales[n];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            if (m < M) y[(int64_t)m * N + n] = s * (acc[m] * kUnscale);
+            if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(acc[m] * kUnscale, n, m);
     }
 }
 
@@ -876,9 +878,10 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
 #define DQ_GEMV_XRES_WAVES 4
 #endif
 
-template <int B, int MT>
+template <int B, int MT, class ZP>
 hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed,
-                            const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                            const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                hipStream_t stream)
 {
     constexpr int kWaves = DQ_GEMV_XRES_WAVES;
     constexpr int kThreads = kWaves * kWave;
@@ -887,7 +890,7 @@ hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed
     const size_t lds = (size_t)MT * nchunks * kXPitch * 2;
     const int64_t pieces = MT * nchunks * 4;
     const dim3 grid((unsigned)ceil_div(N, kWaves)), block(kThreads);
-#define DQ_XRES(R) gemv_xres_kernel<B, MT, kWaves, R><<<grid, block, lds, stream>>>(x, (int)M, packed, scales, N, K, rw, y)
+#define DQ_XRES(R) gemv_xres_kernel<B, MT, kWaves, R><<<grid, block, lds, stream>>>(x, (int)M, packed, scales, N, K, rw, y, zp)
     // pieces per thread: every piece of x must be covered
     static_assert(10 * kThreads >= kXResMax / (kXPitch * 2) * 4, "x staging covers the largest x");
     if (pieces <= kThreads) DQ_XRES(1);
@@ -899,9 +902,10 @@ hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed
     return hipGetLastError();
 }
 
-template <int B, int MT>
+template <int B, int MT, class ZP>
 hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
-                           const float* scales, int64_t N, int64_t K, float* y, hipStream_t stream)
+                           const float* scales, int64_t N, int64_t K, float* y, ZP zp,
+                hipStream_t stream)
 {
     constexpr int kRows = B <= 8 ? DQ_GEMV_ROWS_NARROW : DQ_GEMV_ROWS_WIDE;
     constexpr int kWaves = DQ_GEMV_WAVES;
@@ -910,37 +914,45 @@ hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
     const int64_t blocks = ceil_div(N, rows_per_block);
     if (K % kChunk == 0)
         gemv_lds_kernel<B, MT, kRows, kWaves, true><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
+            x, (int)M, packed, scales, N, K, rw, y, zp);
     else
         gemv_lds_kernel<B, MT, kRows, kWaves, false><<<dim3((unsigned)blocks), dim3(kWaves * kWave), 0, stream>>>(
-            x, (int)M, packed, scales, N, K, rw, y);
+            x, (int)M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
 }
 
-template <int B>
+template <int B, class ZP>
 hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                         int64_t N, int64_t K, float* y, hipStream_t stream)
+                         int64_t N, int64_t K, float* y, ZP zp, hipStream_t stream)
 {
 #ifndef DQ_GEMV_NO_XRES
     // x resident in LDS when it fits, up to 2^27 weights (beyond, the sliced
     // kernel's eight waves per workgroup stream slightly faster)
     if (M <= 2 && K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax &&
         N * K <= (1LL << 27)) {
-        if (M <= 1) return launch_gemv_xres<B, 1>(x, M, packed, scales, N, K, y, stream);
-        return launch_gemv_xres<B, 2>(x, M, packed, scales, N, K, y, stream);
+        if (M <= 1) return launch_gemv_xres<B, 1>(x, M, packed, scales, N, K, y, zp, stream);
+        return launch_gemv_xres<B, 2>(x, M, packed, scales, N, K, y, zp, stream);
     }
 #endif
-    if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, stream);
-    if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, stream);
-    return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, stream);
+    if (M <= 1) return launch_gemv_lds<B, 1>(x, M, packed, scales, N, K, y, zp, stream);
+    if (M <= 2) return launch_gemv_lds<B, 2>(x, M, packed, scales, N, K, y, zp, stream);
+    return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, zp, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       int64_t N, int64_t K, int bits, float* y, hipStream_t stream)
+                       int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
+                       const float* xsum, hipStream_t stream)
 {
-#define CALL(B) launch_gemv_b<B>(x, M, packed, scales, N, K, y, stream)
+    if (zeros) {
+        const ZeroPoints zp{zeros, xsum};
+#define CALL(B) launch_gemv_b<B>(x, M, packed, scales, N, K, y, zp, stream)
+        DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+    }
+    const NoZeroPoints zp{};
+#define CALL(B) launch_gemv_b<B>(x, M, packed, scales, N, K, y, zp, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
 }

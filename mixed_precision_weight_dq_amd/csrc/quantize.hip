@@ -233,6 +233,163 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
 }
 
+// Asymmetric scheme ("量化" tutorial, "量化怎么工作": a zero point added to the
+// rounded quotient, for rows not centred on zero).  Per row, with L = 2^b - 1:
+// lo = min(0, min w), hi = max(0, max w), s = fl32(fl32(hi - lo) / L) (1.0
+// replaces a zero range), z = clip(rint(fl32(-lo / s)), 0, L), codes
+// u = clip(rint(fl32(w / s)) + z, 0, L), stored unsigned.  A row with a NaN
+// or an infinity, or whose range overflows, gets s = NaN and z = every code =
+// 2^(b-1); a row whose s underflows gets s = fl32(1/L), z = 0, codes 0.  Same
+// structure as the symmetric kernel: pass 1 reduces the row's min and max
+// (order-independent, exact), pass 2 turns each lane's chunk into B words.
+template <int B>
+__device__ __forceinline__ void quantize_chunk_asym(const float (&v)[kChunk], float s, float r,
+                                                    float margin, float zf, int mode, int64_t k0,
+                                                    int64_t K, uint32_t (&out)[B])
+{
+    constexpr float kL = (float)((1 << B) - 1);
+#pragma unroll
+    for (int i = 0; i < B; ++i) out[i] = 0;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        float t = v[j] * r;
+        float q = rintf(t);
+        if (!(fabsf(t - q) < margin)) q = rintf(v[j] / s);  // near a tie, or not finite
+        const float c = fminf(fmaxf(q + zf, 0.0f), kL);
+        uint32_t u = mode == 0 ? (uint32_t)c : (mode == 1 ? (1u << (B - 1)) : 0u);
+        if (k0 + j >= K) u = 0;
+        const int pos = j * B;
+        const int wi = pos >> 5;
+        const int off = pos & 31;
+        out[wi] |= u << off;
+        if (off + B > 32) out[wi + 1] |= u >> (32 - off);
+    }
+}
+
+template <int B, bool BF16, bool kAligned>
+__global__ __launch_bounds__(kQuantThreads) void quantize_pack_asym_kernel(
+    const void* __restrict__ w, int64_t K, int64_t row_words, uint32_t* __restrict__ packed,
+    float* __restrict__ scales, int32_t* __restrict__ zeros)
+{
+    constexpr int32_t kL = (1 << B) - 1;
+    __shared__ float red_lo[kQuantThreads / kWave], red_hi[kQuantThreads / kWave];
+    __shared__ int red_bad[kQuantThreads / kWave];
+
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int threads = blockDim.x;
+    const int waves = threads / kWave;
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int64_t row_off = n * K;
+    const int esize = BF16 ? 2 : 4;
+    const bool vec_ok = ((K * esize) & 15) == 0;
+
+    // ---- pass 1: min and max (with 0) and whether anything is not finite
+    float v0[kChunk];
+    float lo = 0.0f, hi = 0.0f;
+    bool bad = false;
+    auto scan = [&](const float (&v)[kChunk]) {
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            bad |= !__builtin_isfinite(v[j]);
+            lo = fminf(lo, v[j]);
+            hi = fmaxf(hi, v[j]);
+        }
+    };
+    if (tid < nchunks) {
+        load_row_chunk<BF16, kAligned>(w, row_off, K, tid, vec_ok, v0);
+        scan(v0);
+    }
+    for (int64_t c = tid + threads; c < nchunks; c += threads) {
+        float v[kChunk];
+        load_row_chunk<BF16, kAligned>(w, row_off, K, c, vec_ok, v);
+        scan(v);
+    }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, d, kWave));
+    }
+    const bool wave_bad = __any(bad);
+    if ((tid & (kWave - 1)) == 0) {
+        red_lo[tid / kWave] = lo;
+        red_hi[tid / kWave] = hi;
+        red_bad[tid / kWave] = wave_bad ? 1 : 0;
+    }
+    __syncthreads();
+    int any_bad = 0;
+    for (int i = 0; i < waves; ++i) {
+        lo = fminf(lo, red_lo[i]);
+        hi = fmaxf(hi, red_hi[i]);
+        any_bad |= red_bad[i];
+    }
+
+    // ---- scale and zero point
+    const float Lf = (float)kL;
+    const float range = hi - lo;
+    float s, zf = 0.0f;
+    int mode = 0;  // 0 quantize, 1 every code 2^(b-1), 2 every code 0
+    if (any_bad || !__builtin_isfinite(range)) {
+        s = __uint_as_float(0x7fc00000u);
+        zf = (float)(1 << (B - 1));
+        mode = 1;
+    } else {
+        s = (range == 0.0f ? 1.0f : range) / Lf;
+        if (s == 0.0f) {  // range / L underflowed: treated as an all-zero row
+            s = 1.0f / Lf;
+            mode = 2;
+        } else {
+            zf = fminf(fmaxf(rintf(-lo / s), 0.0f), Lf);
+        }
+    }
+    if (tid == 0) {
+        scales[n] = s;
+        zeros[n] = (int32_t)zf;
+    }
+    const float r = 1.0f / s;
+    // |w / s| <= L (1 + 2^-22): the reciprocal product stays within
+    // 2^-22 (L + 1) of fl32(w / s), so rint agrees outside that margin
+    const float margin = 0.5f - ldexpf(Lf + 1.0f, -21);
+
+    // ---- pass 2: codes, packed 32 to B whole words
+    uint32_t* __restrict__ prow = packed + n * row_words;
+    if (tid < nchunks) {
+        uint32_t out[B];
+        quantize_chunk_asym<B>(v0, s, r, margin, zf, mode, (int64_t)tid * kChunk, K, out);
+        store_chunk<B>(prow, tid, row_words, out);
+    }
+    for (int64_t c = tid + threads; c < nchunks; c += threads) {
+        float v[kChunk];
+        load_row_chunk<BF16, kAligned>(w, row_off, K, c, vec_ok, v);
+        uint32_t out[B];
+        quantize_chunk_asym<B>(v, s, r, margin, zf, mode, c * kChunk, K, out);
+        store_chunk<B>(prow, c, row_words, out);
+    }
+    for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
+}
+
+// sum_k x[m, k] for the asymmetric products: one workgroup per row of x, fp64
+// partial sums in a fixed order (lane t: k = t, t + 256, ...; then a fixed
+// tree), rounded once to fp32.
+constexpr int kXSumThreads = 256;
+
+__global__ __launch_bounds__(kXSumThreads) void x_sum_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t K, float* __restrict__ xsum)
+{
+    __shared__ double part[kXSumThreads];
+    const int64_t m = blockIdx.x;
+    double acc = 0.0;
+    for (int64_t k = threadIdx.x; k < K; k += kXSumThreads)
+        acc += (double)bf16_bits_to_float(x[m * K + k]);
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int d = kXSumThreads / 2; d >= 1; d >>= 1) {
+        if ((int)threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) xsum[m] = (float)part[0];
+}
+
 // One workgroup per row; thread t turns codes 4t .. 4t+3 (then + 1024, ...)
 // into int32 q (and fl32(q * s)), so every store instruction of a wave writes
 // one contiguous 1 KB run (or 256 B of dword stores when rows are not 16-byte
@@ -243,12 +400,14 @@ constexpr int kUnpackThreads = 256;
 
 template <int B>
 __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
-    const uint32_t* __restrict__ packed, const float* __restrict__ scales, int64_t K,
-    int64_t row_words, int32_t* __restrict__ q_out, float* __restrict__ w_out)
+    const uint32_t* __restrict__ packed, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int64_t K, int64_t row_words, int32_t* __restrict__ q_out,
+    float* __restrict__ w_out)
 {
-    constexpr int32_t kBias = 1 << (B - 1);
     constexpr uint32_t kMask = (1u << B) - 1u;
     const int64_t n = blockIdx.x;
+    // the code's offset: 2^(b-1) (symmetric scheme) or the row's zero point
+    const int32_t kBias = zeros ? zeros[n] : (1 << (B - 1));
     const uint32_t* __restrict__ row = packed + n * row_words;
     const float s = w_out ? scales[n] : 0.0f;
     // 16-byte stores need every output row start 16-byte aligned
@@ -407,12 +566,12 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
 }
 
 template <int B>
-hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
-                           int32_t* q_out, float* w_out, hipStream_t stream)
+hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, const int32_t* zeros,
+                           int64_t N, int64_t K, int32_t* q_out, float* w_out, hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
-    unpack_kernel<B><<<dim3((unsigned)N), dim3(kUnpackThreads), 0, stream>>>(packed, scales, K, rw,
-                                                                            q_out, w_out);
+    unpack_kernel<B><<<dim3((unsigned)N), dim3(kUnpackThreads), 0, stream>>>(packed, scales, zeros,
+                                                                            K, rw, q_out, w_out);
     return hipGetLastError();
 }
 
@@ -439,6 +598,32 @@ hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64
     return hipGetLastError();
 }
 
+template <int B>
+hipError_t launch_quantize_pack_asym_b(const void* w, bool bf16, int64_t N, int64_t K,
+                                       uint32_t* packed, float* scales, int32_t* zeros,
+                                       hipStream_t stream)
+{
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
+                                                       : ceil_div(nchunks, kWave) * kWave);
+    const dim3 grid((unsigned)N), block(threads);
+    const bool aligned = K % kChunk == 0;
+    if (bf16 && aligned)
+        quantize_pack_asym_kernel<B, true, true><<<grid, block, 0, stream>>>(w, K, rw, packed, scales,
+                                                                             zeros);
+    else if (bf16)
+        quantize_pack_asym_kernel<B, true, false><<<grid, block, 0, stream>>>(w, K, rw, packed,
+                                                                              scales, zeros);
+    else if (aligned)
+        quantize_pack_asym_kernel<B, false, true><<<grid, block, 0, stream>>>(w, K, rw, packed,
+                                                                              scales, zeros);
+    else
+        quantize_pack_asym_kernel<B, false, false><<<grid, block, 0, stream>>>(w, K, rw, packed,
+                                                                               scales, zeros);
+    return hipGetLastError();
+}
+
 hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
                             double* matrix_sumsq, hipStream_t stream)
 {
@@ -458,10 +643,26 @@ hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, doub
     return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
-                         int bits, int32_t* q_out, float* w_out, hipStream_t stream)
+hipError_t launch_quantize_pack_asym(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                     uint32_t* packed, float* scales, int32_t* zeros,
+                                     hipStream_t stream)
 {
-#define CALL(B) launch_unpack_b<B>(packed, scales, N, K, q_out, w_out, stream)
+#define CALL(B) launch_quantize_pack_asym_b<B>(w, bf16, N, K, packed, scales, zeros, stream)
+    DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+}
+
+hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hipStream_t stream)
+{
+    x_sum_kernel<<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint32_t* packed, const float* scales, const int32_t* zeros,
+                         int64_t N, int64_t K, int bits, int32_t* q_out, float* w_out,
+                         hipStream_t stream)
+{
+#define CALL(B) launch_unpack_b<B>(packed, scales, zeros, N, K, q_out, w_out, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
 }

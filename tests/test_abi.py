@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
                  "dq_status_string", "dq_last_error", "dq_quantize_pack_sumsq", "dq_sensitivity",
-                 "dq_row_sumsq", "dq_file_write", "dq_file_open", "dq_file_count",
+                 "dq_row_sumsq", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
+                 "dq_gemv_asym", "dq_gemm_asym", "dq_file_write", "dq_file_open", "dq_file_count",
                  "dq_file_matrix_info", "dq_file_verify", "dq_file_load", "dq_file_close",
                  "dq_allocate_bits"):
         assert want in names
@@ -160,3 +161,28 @@ def test_row_sumsq_arguments_rejected():
     assert f(MIS, dq.DQ_F32, 4, 64, A, 0) == dq.DQ_ERR_ALIGN
     assert f(A, dq.DQ_F32, 4, 64, A + 4, 0) == dq.DQ_ERR_ALIGN
     assert f(A, dq.DQ_F32, 4, 64, A, A + 4) == dq.DQ_ERR_ALIGN
+
+
+def test_asym_arguments_rejected():
+    q = dq.dq_quantize_pack_asym
+    assert q(A, dq.DQ_BF16, 4, 64, 6, A, A, 0) == dq.DQ_ERR_NULL
+    assert q(A, dq.DQ_BF16, 4, 64, 16, A, A, A) == dq.DQ_ERR_BITS
+    assert q(A, dq.DQ_BF16, 0, 64, 6, A, A, A) == dq.DQ_ERR_SHAPE
+    assert q(A, 9, 4, 64, 6, A, A, A) == dq.DQ_ERR_DTYPE
+    assert q(A, dq.DQ_BF16, 4, 64, 6, A, A, A + 2) == dq.DQ_ERR_ALIGN
+    u = dq.dq_unpack_asym
+    assert u(A, A, 0, 4, 64, 6, A, 0) == dq.DQ_ERR_NULL
+    assert u(A, 0, A, 4, 64, 6, 0, A) == dq.DQ_ERR_NULL  # w_out needs scales
+    assert u(A, A, A + 1, 4, 64, 6, A, 0) == dq.DQ_ERR_ALIGN
+    x = dq.dq_x_sum
+    assert x(0, 1, 64, A) == dq.DQ_ERR_NULL
+    assert x(A, 0, 64, A) == dq.DQ_ERR_SHAPE
+    assert x(A, 1, (1 << 22) + 1, A) == dq.DQ_ERR_SHAPE
+    assert x(MIS, 1, 64, A) == dq.DQ_ERR_ALIGN
+    for fn, bad_m in ((dq.dq_gemv_asym, 17), (dq.dq_gemm_asym, 0)):
+        assert fn(A, 1, A, A, 0, A, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, 1, A, A, A, 0, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, bad_m, A, A, A, A, 4, 64, 6, A) == dq.DQ_ERR_SHAPE
+        assert fn(A, 1, A, A, A, A, 4, 64, 1, A) == dq.DQ_ERR_BITS
+        assert fn(A, 1, A, A, A + 2, A, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, A, A, A, A + 2, 4, 64, 6, A) == dq.DQ_ERR_ALIGN

@@ -1,0 +1,169 @@
+"""Parity of the asymmetric (zero-point) variant with the oracle: quantize +
+pack and unpack bit-exact, the activation sums within their fp64-then-fp32
+rounding, GEMV / GEMM within 1e-4 * sum_k |x * w_hat| of the fp64 reference,
+one-hot activations exact, on rows shifted off zero, non-negative and
+non-positive rows and the special rows, through every product kernel (the
+resident-x and sliced GEMVs, the matrix-core GEMVs, the 128-row, wide and
+fallback GEMMs).
+
+Source: "量化" tutorial (aiknowledge.cn), "量化怎么工作" (a zero point added to
+the rounded quotient for distributions not centred on zero)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import mixed_precision_weight_dq_amd as dq
+import oracle
+import workload
+from gpu_util import bf16_gpu, f32_bits, report, torch, u32, weights_gpu
+from pins import within_tolerance
+from test_gpu_parity import GEMM_SHAPES, GEMV_SHAPES, QUANT_SHAPES, special_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def shifted_weights(seed: int, N: int, K: int, dtype: str = "bf16") -> np.ndarray:
+    """N(0, 0.02^2) rows moved off zero by a per-row offset in [-0.04, 0.04]; every
+    fifth row non-negative, every seventh non-positive."""
+    w = workload.weights(31, seed, N, K, dtype="f32")
+    off = np.random.default_rng(seed).uniform(-0.04, 0.04, N).astype(np.float32)
+    w = w + off[:, None]
+    w[::5] = np.abs(w[::5])
+    w[3::7] = -np.abs(w[3::7])
+    return workload.bf16_from_f32(w) if dtype == "bf16" else w.astype(np.float32)
+
+
+def assert_quantize_asym(w_np: np.ndarray, bits: int):
+    report("quantize_pack_asym shape=%s dtype=%s bits=%d" % (w_np.shape, w_np.dtype, bits))
+    P, S, Z = dq.quantize_pack_asym(weights_gpu(w_np), bits)
+    torch().cuda.synchronize()
+    o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w_np, bits)
+    assert np.array_equal(f32_bits(S), o_scales.view(np.uint32)), "scale bits differ"
+    assert np.array_equal(Z.cpu().numpy(), o_zeros), "zero points differ"
+    if not np.array_equal(u32(P), o_packed):
+        pytest.fail("packed words differ at %s" % np.argwhere(u32(P) != o_packed)[:5].tolist())
+    return o_packed, o_scales, o_zeros
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_quantize_asym_bitexact(bits):
+    for i, (N, K) in enumerate(QUANT_SHAPES):
+        assert_quantize_asym(shifted_weights(bits * 100 + i, N, K, "bf16"), bits)
+        assert_quantize_asym(shifted_weights(bits * 100 + 50 + i, N, K, "f32"), bits)
+
+
+@pytest.mark.parametrize("bits", [2, 5, 8, 9, 15])
+def test_quantize_asym_special_rows(bits):
+    for K in (1, 33, 300):
+        rows = special_rows(K, bits)
+        extra = np.zeros((2, K), np.float32)
+        extra[0, 0] = 1.4e-45  # the range over L underflows
+        extra[1] = np.abs(rows[8]) + 1.0  # all positive, far from zero
+        assert_quantize_asym(np.concatenate([rows, extra]), bits)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_unpack_asym_bitexact(bits):
+    for i, (N, K) in enumerate([(3, 31), (33, 1000), (9, 8232)]):
+        w = shifted_weights(bits * 10 + i, N, K)
+        o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
+        q_ref, w_ref = oracle.unpack_asym(o_packed, o_scales, o_zeros, N, K, bits)
+        report("unpack_asym N=%d K=%d bits=%d" % (N, K, bits))
+        P = torch().from_numpy(o_packed.view(np.int32)).cuda()
+        q, w_hat = dq.unpack_asym(P, torch().from_numpy(o_scales).cuda(),
+                                  torch().from_numpy(o_zeros).cuda(), K, bits, want_q=True,
+                                  want_w=True)
+        torch().cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), q_ref)
+        assert np.array_equal(f32_bits(w_hat), w_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 1000), (16, 4133), (2048, 8192)])
+def test_x_sum(M, K):
+    x = workload.activations(32, K, M, K)
+    report("x_sum M=%d K=%d" % (M, K))
+    got = dq.x_sum(bf16_gpu(x)).cpu().numpy().astype(np.float64)
+    xf = workload.bf16_to_f32(x).astype(np.float64)
+    exact = np.array([np.sum(xf[m]) for m in range(M)])  # every partial sum exact in fp64 here
+    mag = np.abs(xf).sum(axis=1)
+    assert (np.abs(got - exact) <= 2.0 ** -24 * np.abs(exact) + K * 2.0 ** -52 * mag).all()
+
+
+def assert_asym_product(kind: str, M: int, N: int, K: int, bits: int, seed: int):
+    w = shifted_weights(seed, N, K)
+    x = workload.activations(33, seed, M, K)
+    o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
+    y_ref, bound = oracle.matmul_asym(x, o_packed, o_scales, o_zeros, N, K, bits)
+    report("%s_asym M=%d N=%d K=%d bits=%d" % (kind, M, N, K, bits))
+    P = torch().from_numpy(o_packed.view(np.int32)).cuda()
+    S = torch().from_numpy(o_scales).cuda()
+    Z = torch().from_numpy(o_zeros).cuda()
+    fn = dq.gemv_asym if kind == "gemv" else dq.gemm_asym
+    y = fn(bf16_gpu(x), P, S, Z, K, bits)
+    torch().cuda.synchronize()
+    y = y.cpu().numpy()
+    ok = within_tolerance(y, y_ref, bound)
+    if not ok.all():
+        m, n = np.argwhere(~ok)[0]
+        pytest.fail("%s_asym M=%d N=%d K=%d b=%d: y[%d,%d]=%r ref %r bound %r (%d bad)" % (
+            kind, M, N, K, bits, m, n, y[m, n], y_ref[m, n], bound[m, n], int((~ok).sum())))
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemv_asym_parity(bits):
+    for M in (1, 2, 3, 8, 16):
+        for i, (N, K) in enumerate(GEMV_SHAPES):
+            assert_asym_product("gemv", M, N, K, bits, seed=bits * 1000 + M * 10 + i)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemm_asym_parity(bits):
+    for i, (M, N, K) in enumerate(GEMM_SHAPES):
+        assert_asym_product("gemm", M, N, K, bits, seed=bits * 1000 + 500 + i)
+
+
+@pytest.mark.parametrize("bits", [2, 6, 9, 12])
+def test_gemm_asym_wide_tiles(bits):
+    """Shapes that take the 256 x 256 and the 256 x 128 wide kernels."""
+    for M, N, K in ((2000, 8100, 448), (300, 30000, 448)):
+        assert_asym_product("gemm", M, N, K, bits, seed=bits * 7 + M)
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("bits", [2, 6, 9, 10, 15])
+def test_asym_one_hot_is_exact(kind, bits):
+    """x = e_k: the kernels' sum is u - 2^(b-1) exactly and the zero-point term
+    (2^(b-1) - z) * 1 makes it u - z exactly, so y[k, n] = fl32(s[n] (u - z))."""
+    N, K = 70, 16 if kind == "gemv" else 40
+    w = shifted_weights(bits + 900, N, K)
+    o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
+    _, w_hat = oracle.unpack_asym(o_packed, o_scales, o_zeros, N, K, bits)
+    eye = workload.bf16_from_f32(np.eye(K, dtype=np.float32))
+    P = torch().from_numpy(o_packed.view(np.int32)).cuda()
+    S = torch().from_numpy(o_scales).cuda()
+    Z = torch().from_numpy(o_zeros).cuda()
+    report("%s_asym one-hot bits=%d" % (kind, bits))
+    fn = dq.gemv_asym if kind == "gemv" else dq.gemm_asym
+    for k0 in range(0, K, 16):
+        xs = eye[k0:k0 + 16]
+        y = fn(bf16_gpu(xs), P, S, Z, K, bits)
+        torch().cuda.synchronize()
+        assert np.array_equal(f32_bits(y), w_hat.T[k0:k0 + 16].copy().view(np.uint32))
+
+
+def test_quantize_asym_then_products_end_to_end():
+    """GPU quantize -> GPU x_sum -> GPU GEMV and GEMM, against the oracle's flow."""
+    N, K, bits = 640, 2048, 5
+    w = shifted_weights(4242, N, K)
+    P, S, Z = dq.quantize_pack_asym(weights_gpu(w), bits)
+    x = workload.activations(34, 1, 300, K)
+    X = bf16_gpu(x)
+    xs = dq.x_sum(X)
+    yv = dq.gemv_asym(X[:4], P, S, Z, K, bits, xsum=xs[:4])
+    yg = dq.gemm_asym(X, P, S, Z, K, bits, xsum=xs)
+    torch().cuda.synchronize()
+    o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
+    y_ref, bound = oracle.matmul_asym(x, o_packed, o_scales, o_zeros, N, K, bits)
+    assert within_tolerance(yv.cpu().numpy(), y_ref[:4], bound[:4]).all()
+    assert within_tolerance(yg.cpu().numpy(), y_ref, bound).all()
