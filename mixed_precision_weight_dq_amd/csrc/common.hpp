@@ -159,12 +159,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 // (2^(b-1) - z[n]) * sum_k x[m, k] gives sum_k x * (u - z[n]).  The product
 // kernels take the type as a template parameter: NoZeroPoints (the symmetric
 // scheme) adds nothing and compiles to the plain epilogue.
+// Each type gives coef<B>(n), read once per output column before any store
+// (a load issued after the stores would wait for all of them), and
+// apply(v, coef, m) = v + coef * sum_k x[m, k].
 struct NoZeroPoints {
     template <int B>
-    __device__ __forceinline__ float add(float v, int64_t, int64_t) const
+    __device__ __forceinline__ float coef(int64_t) const
     {
-        return v;
+        return 0.0f;
     }
+    __device__ __forceinline__ float apply(float v, float, int64_t) const { return v; }
 };
 
 struct ZeroPoints {
@@ -172,10 +176,51 @@ struct ZeroPoints {
     const float* xsum;     // [M]: sum_k x[m, k]
 
     template <int B>
-    __device__ __forceinline__ float add(float v, int64_t n, int64_t m) const
+    __device__ __forceinline__ float coef(int64_t n) const
     {
-        return fmaf((float)((1 << (B - 1)) - zeros[n]), xsum[m], v);
+        return (float)((1 << (B - 1)) - zeros[n]);
+    }
+    __device__ __forceinline__ float apply(float v, float c, int64_t m) const
+    {
+        return fmaf(c, xsum[m], v);
     }
 };
+
+// ZeroPoints with one tile's activation sums staged in LDS (row m at
+// xs[m - m0]), for epilogues that read each row's sum many times.
+struct TileZeroPoints {
+    const int32_t* zeros;
+    const float* xs;
+    int64_t m0;
+
+    template <int B>
+    __device__ __forceinline__ float coef(int64_t n) const
+    {
+        return (float)((1 << (B - 1)) - zeros[n]);
+    }
+    __device__ __forceinline__ float apply(float v, float c, int64_t m) const
+    {
+        return fmaf(c, xs[m - m0], v);
+    }
+};
+
+// Stage rows [m0, m0 + rows) of the activation sums into `lds` (a buffer the
+// workgroup no longer uses) between two barriers; every thread of the
+// workgroup must call it.  The symmetric scheme stages nothing.
+__device__ __forceinline__ NoZeroPoints stage_tile_zero_points(NoZeroPoints, float*, int64_t,
+                                                               int64_t, int)
+{
+    return {};
+}
+
+__device__ __forceinline__ TileZeroPoints stage_tile_zero_points(ZeroPoints zp, float* lds,
+                                                                 int64_t m0, int64_t M, int rows)
+{
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows; i += blockDim.x)
+        lds[i] = m0 + i < M ? zp.xsum[m0 + i] : 0.0f;
+    __syncthreads();
+    return {zp.zeros, lds, m0};
+}
 
 }  // namespace dq

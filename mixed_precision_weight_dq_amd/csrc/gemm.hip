@@ -151,12 +151,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
         if (n >= N) continue;
         const float s = scales[n];
+        const float zc = zp.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r], n, m);
+                if (m < M) y[m * N + n] = s * zp.apply(acc[i][j][r], zc, m);
             }
         }
     }
@@ -345,19 +346,20 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4;
     // whole tiles store without bounds checks, as streaming stores
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
+    const auto zt = stage_tile_zero_points(zp, reinterpret_cast<float*>(&As[0][0]), m0, M, T::BM);
     if (m0 + T::BM <= M && n0 + T::BN <= N) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
             const float s = scales[n];
+            const float zc = zt.template coef<B>(n);
 #pragma unroll
             for (int i = 0; i < kMT; ++i) {
                 float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     __builtin_nontemporal_store(
-                        s * zp.template add<B>(acc[i][j][r] * kUnscale, n,
-                                      m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                        s * zt.apply(acc[i][j][r] * kUnscale, zc, m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
                         yp + (8 * (r >> 2) + (r & 3)) * N);
             }
         }
@@ -368,12 +370,13 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
         const float s = scales[n];
+        const float zc = zt.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r] * kUnscale, n, m);
+                if (m < M) y[m * N + n] = s * zt.apply(acc[i][j][r] * kUnscale, zc, m);
             }
         }
     }
@@ -611,6 +614,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     // arithmetic runs on the vector units; the tile's 256 rows of y must span
     // less than 4 GiB (N < 2^22), else the checked stores below serve.
     constexpr float kUnscale = 1.0f / expand8_scale<B>();
+    // the x staging buffer is free now: the tile's activation sums go there
+    const auto zt = stage_tile_zero_points(zp, reinterpret_cast<float*>(&As[0][0]), m0, M, T::BM);
     if (m0 + T::BM <= M && n0 + T::BN <= N && (int64_t)T::BM * N * 4 <= 0xffffffffLL) {
         const BufRef yb = uniform_buf(y + m0 * N, (uint32_t)(T::BM * N * 4));
         const uint32_t row4 = (uint32_t)(N * 4);
@@ -618,14 +623,14 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
             const float s = scales[n];
+            const float zc = zt.template coef<B>(n);
             const uint32_t voff = (uint32_t)(4 * h) * row4 + (uint32_t)n * 4;
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     buf_store_f32_nt(yb,
-                                     s * zp.template add<B>(acc[i][j][r] * kUnscale, n,
-                                                   m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                                     s * zt.apply(acc[i][j][r] * kUnscale, zc, m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
                                      voff,
                                      (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * row4);
         }
@@ -636,12 +641,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
         const float s = scales[n];
+        const float zc = zt.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * zp.template add<B>(acc[i][j][r] * kUnscale, n, m);
+                if (m < M) y[m * N + n] = s * zt.apply(acc[i][j][r] * kUnscale, zc, m);
             }
         }
     }

@@ -364,9 +364,10 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
             const int64_t n = n0 + r;
             if (n < N) {
                 const float s = scales[n];
+                const float zc = zp.template coef<B>(n);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(acc[r][m] * kUnscale, n, m);
+                    if (m < M) y[(int64_t)m * N + n] = s * zp.apply(acc[r][m] * kUnscale, zc, m);
             }
         }
     }
@@ -516,13 +517,14 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
             const int64_t n = n0 + 16 * j + c;
             if (n >= N) continue;
             const float s = scales[n];
+            const float zc = zp.template coef<B>(n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = acc[j][r];
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(v * kUnscale, n, m);
+                if (m < M) y[(int64_t)m * N + n] = s * zp.apply(v * kUnscale, zc, m);
             }
         }
     }
@@ -717,13 +719,14 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
             const int64_t n = n0 + 16 * j + c;
             if (n >= N) continue;
             const float s = scales[n];
+            const float zc = zp.template coef<B>(n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = acc[j][r];
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(v * kUnscale, n, m);
+                if (m < M) y[(int64_t)m * N + n] = s * zp.apply(v * kUnscale, zc, m);
             }
         }
     }
@@ -868,9 +871,10 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     if (lane == 0 && n < N) {
         constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
         const float s = scales[n];
+        const float zc = zp.template coef<B>(n);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            if (m < M) y[(int64_t)m * N + n] = s * zp.template add<B>(acc[m] * kUnscale, n, m);
+            if (m < M) y[(int64_t)m * N + n] = s * zp.apply(acc[m] * kUnscale, zc, m);
     }
 }
 

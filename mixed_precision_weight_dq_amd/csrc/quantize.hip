@@ -369,25 +369,50 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_asym_kernel(
 }
 
 // sum_k x[m, k] for the asymmetric products: one workgroup per row of x, fp64
-// partial sums in a fixed order (lane t: k = t, t + 256, ...; then a fixed
-// tree), rounded once to fp32.
+// partial sums in a fixed order, rounded once to fp32.  When rows are 16-byte
+// aligned, thread t adds the 8-element pieces t, t + 256, ... (four loads in
+// flight per round); otherwise elements t, t + 256, ...; then a fixed tree.
 constexpr int kXSumThreads = 256;
 
+template <bool kVec>
 __global__ __launch_bounds__(kXSumThreads) void x_sum_kernel(const uint16_t* __restrict__ x,
                                                              int64_t K, float* __restrict__ xsum)
 {
     __shared__ double part[kXSumThreads];
     const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
     double acc = 0.0;
-    for (int64_t k = threadIdx.x; k < K; k += kXSumThreads)
-        acc += (double)bf16_bits_to_float(x[m * K + k]);
-    part[threadIdx.x] = acc;
+    if (kVec) {
+        const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
+        const int64_t npieces = K / 8;
+        for (int64_t p0 = tid; p0 < npieces; p0 += 4 * kXSumThreads) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t p = p0 + (int64_t)u * kXSumThreads;
+                v[u] = p < npieces ? row[p] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc += (double)__uint_as_float(e[j] << 16);
+                    acc += (double)__uint_as_float(e[j] & 0xffff0000u);
+                }
+            }
+        }
+    } else {
+        for (int64_t k = tid; k < K; k += kXSumThreads)
+            acc += (double)bf16_bits_to_float(x[m * K + k]);
+    }
+    part[tid] = acc;
     __syncthreads();
     for (int d = kXSumThreads / 2; d >= 1; d >>= 1) {
-        if ((int)threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
+        if (tid < d) part[tid] += part[tid + d];
         __syncthreads();
     }
-    if (threadIdx.x == 0) xsum[m] = (float)part[0];
+    if (tid == 0) xsum[m] = (float)part[0];
 }
 
 // One workgroup per row; thread t turns codes 4t .. 4t+3 (then + 1024, ...)
@@ -654,7 +679,10 @@ hipError_t launch_quantize_pack_asym(const void* w, bool bf16, int64_t N, int64_
 
 hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hipStream_t stream)
 {
-    x_sum_kernel<<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
+    if (K % 8 == 0)  // 16-byte rows (x itself is 16-byte aligned)
+        x_sum_kernel<true><<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
+    else
+        x_sum_kernel<false><<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
     return hipGetLastError();
 }
 
