@@ -17,7 +17,9 @@ names the passage it follows:
   with the product, fp32 scales, fp32 output), computed here in fp64;
 * asymmetric variant -- "量化" tutorial, "how quantization works" (a zero
   point added to the rounded quotient for distributions not centred on zero):
-  per-row scale and zero point, unsigned codes.
+  per-row scale and zero point, unsigned codes;
+* group-wise scales -- "量化" tutorial, exercise 1 of its exercises section (one
+  scale per group of g weights instead of per channel).
 """
 from __future__ import annotations
 
@@ -79,6 +81,12 @@ class Oracle:
         lib.oracle_unpack_asym.restype = None
         lib.oracle_matmul_asym.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, vp, vp]
         lib.oracle_matmul_asym.restype = None
+        lib.oracle_quantize_pack_group.argtypes = [vp, i32, i64, i64, i32, i64, vp, vp, vp]
+        lib.oracle_quantize_pack_group.restype = None
+        lib.oracle_unpack_group.argtypes = [vp, vp, i64, i64, i32, i64, vp, vp]
+        lib.oracle_unpack_group.restype = None
+        lib.oracle_matmul_group.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
+        lib.oracle_matmul_group.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -217,6 +225,46 @@ class Oracle:
         return y, bound
 
 
+    # -- group-wise scales ([TUT] exercise: one scale per g weights of a row)
+
+    def quantize_pack_group(self, w: np.ndarray, bits: int, g: int):
+        """Returns (packed, scales float32 [N, ceil(K/g)], q int32 [N, K])."""
+        _check_bits(bits)
+        w = np.ascontiguousarray(w)
+        dtype = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1}.get(w.dtype)
+        if dtype is None:
+            raise TypeError("w must be float32 or uint16 (bf16 bits)")
+        N, K = w.shape
+        G = -(-K // g)
+        packed = np.empty((N, self.row_bytes(K, bits) // 4), dtype=np.uint32)
+        scales = np.empty((N, G), dtype=np.float32)
+        q = np.empty((N, K), dtype=np.int32)
+        self.lib.oracle_quantize_pack_group(_ptr(w), dtype, N, K, bits, g, _ptr(packed),
+                                            _ptr(scales), _ptr(q))
+        return packed, scales, q
+
+    def unpack_group(self, packed, scales, N: int, K: int, bits: int, g: int):
+        _check_bits(bits)
+        q = np.empty((N, K), dtype=np.int32)
+        w_hat = np.empty((N, K), dtype=np.float32)
+        self.lib.oracle_unpack_group(_ptr(np.ascontiguousarray(packed, dtype=np.uint32)),
+                                     _ptr(np.ascontiguousarray(scales, dtype=np.float32)), N, K,
+                                     bits, g, _ptr(q), _ptr(w_hat))
+        return q, w_hat
+
+    def matmul_group(self, x_bf16, packed, scales, N: int, K: int, bits: int, g: int):
+        """fp64 y = sum_k x q s[n, k/g] and bound = sum_k |x q s[n, k/g]|, [M, N]."""
+        _check_bits(bits)
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M = x.shape[0]
+        y = np.empty((M, N), dtype=np.float64)
+        bound = np.empty((M, N), dtype=np.float64)
+        self.lib.oracle_matmul_group(_ptr(x), M, _ptr(np.ascontiguousarray(packed, dtype=np.uint32)),
+                                     _ptr(np.ascontiguousarray(scales, dtype=np.float32)), N, K,
+                                     bits, g, _ptr(y), _ptr(bound))
+        return y, bound
+
+
 def default() -> Oracle:
     """The oracle built from ``dq_oracle.c`` (compiled on first use if absent)."""
     global _default
@@ -265,3 +313,15 @@ def unpack_asym(packed, scales, zeros, N: int, K: int, bits: int):
 
 def matmul_asym(x_bf16, packed, scales, zeros, N: int, K: int, bits: int):
     return default().matmul_asym(x_bf16, packed, scales, zeros, N, K, bits)
+
+
+def quantize_pack_group(w: np.ndarray, bits: int, g: int):
+    return default().quantize_pack_group(w, bits, g)
+
+
+def unpack_group(packed, scales, N: int, K: int, bits: int, g: int):
+    return default().unpack_group(packed, scales, N, K, bits, g)
+
+
+def matmul_group(x_bf16, packed, scales, N: int, K: int, bits: int, g: int):
+    return default().matmul_group(x_bf16, packed, scales, N, K, bits, g)

@@ -454,6 +454,86 @@ void oracle_matmul_asym(const uint16_t *x, int64_t M, const uint32_t *packed,
     }
 }
 
+/* ---- group-wise scales ([TUT] exercise 1 of "五、练习": one scale per group
+ * of g consecutive weights of a row instead of one per channel) ---------- */
+
+/*
+ * Row n, group j holds columns [j*g, min(K, (j+1)*g)).  Each group is
+ * quantized exactly like a row of the symmetric per-channel quantizer above
+ * (same absmax, scale, zero-group, non-finite and underflow rules), with its
+ * own scale scales[n*G + j], G = ceil(K/g).  Codes are packed per row as
+ * before, one bit stream over all K codes.
+ */
+void oracle_quantize_pack_group(const void *w, int32_t dtype, int64_t N,
+                                int64_t K, int32_t bits, int64_t g,
+                                uint32_t *packed, float *scales, int32_t *q_out)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+    const int64_t G = (K + g - 1) / g;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        int32_t *q = (int32_t *)malloc((size_t)K * sizeof *q);
+        float *piece = (float *)malloc((size_t)g * sizeof *piece);
+        for (int64_t j = 0; j < G; j++) {
+            int64_t k0 = j * g, len = (K - k0 < g) ? K - k0 : g;
+            for (int64_t k = 0; k < len; k++)
+                piece[k] = load_weight(w, dtype, n * K + k0 + k);
+            /* the group as a one-row fp32 matrix */
+            quantize_row(piece, 0, 0, len, bits, q + k0, &scales[n * G + j]);
+        }
+        pack_row(q, K, bits, packed + n * row_words, row_words);
+        if (q_out)
+            memcpy(q_out + n * K, q, (size_t)K * sizeof *q);
+        free(piece);
+        free(q);
+    }
+}
+
+/* Inverse with group scales: q_out = u - 2^(b-1), w_out = fl32(q * s[n, k/g]). */
+void oracle_unpack_group(const uint32_t *packed, const float *scales, int64_t N,
+                         int64_t K, int32_t bits, int64_t g, int32_t *q_out,
+                         float *w_out)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+    const int64_t G = (K + g - 1) / g;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        int32_t *q = q_out + n * K;
+        unpack_row(packed + n * row_words, K, bits, q);
+        if (w_out)
+            for (int64_t k = 0; k < K; k++)
+                w_out[n * K + k] = (float)q[k] * scales[n * G + k / g];
+    }
+}
+
+/* fp64 reference with group scales:
+ *     y[m,n]     = sum_k x[m,k] * q[n,k] * s[n, k/g]
+ *     bound[m,n] = sum_k |x[m,k] * q[n,k] * s[n, k/g]| */
+void oracle_matmul_group(const uint16_t *x, int64_t M, const uint32_t *packed,
+                         const float *scales, int64_t N, int64_t K, int32_t bits,
+                         int64_t g, double *y, double *bound)
+{
+    const int64_t row_words = oracle_row_bytes(K, bits) / 4;
+    const int64_t G = (K + g - 1) / g;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; n++) {
+        int32_t *q = (int32_t *)malloc((size_t)(K > 0 ? K : 1) * sizeof *q);
+        unpack_row(packed + n * row_words, K, bits, q);
+        for (int64_t m = 0; m < M; m++) {
+            double total = 0.0, total_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double term = (double)bf16_bits_to_float(x[m * K + k]) * (double)q[k] *
+                              (double)scales[n * G + k / g];
+                total += term;
+                total_abs += fabs(term);
+            }
+            y[m * N + n] = total;
+            bound[m * N + n] = total_abs;
+        }
+        free(q);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
