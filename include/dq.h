@@ -88,6 +88,7 @@ typedef int32_t dq_status;
 #define DQ_TOP_BITS 16                 /* allocation level meaning "BF16 kept" */
 #define DQ_MAX_MATRICES (1LL << 24)    /* matrices per allocation              */
 #define DQ_MAX_PARAMS (1LL << 40)      /* parameters per matrix                */
+#define DQ_MAX_GROUP 2048              /* largest group of the group-wise scales */
 
 /* Bytes of one packed row: ceil(K*bits/8) rounded up to a multiple of 128.
  * Returns 0 when K or bits is out of range.  Host-only, no HIP call. */
@@ -102,6 +103,28 @@ size_t dq_packed_row_bytes(int64_t K, int32_t bits);
  * treated like an all-zero row: scale = fl32(1/qmax), q = 0. */
 dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
                            uint32_t* packed, float* scales, void* stream);
+
+/* Group-wise scales ("量化" tutorial, exercise 1 of its exercises: one scale
+ * per group of weights instead of per channel, groups of 32 to 256 as
+ * GPTQ/AWQ use).  Group j of row n holds columns [j*g, min(K, (j+1)*g)) and
+ * is quantized exactly as a row of dq_quantize_pack (its own absmax, scale,
+ * zero, non-finite and underflow rules); codes are packed per row as before.
+ *   group   g, a power of two in [32, DQ_MAX_GROUP] (else DQ_ERR_SHAPE)
+ *   scales  device, fp32 [N, G], G = ceil(K / g), scale of group j of row n at
+ *           scales[n * G + j]
+ * dq_unpack_group: q_out as dq_unpack, w_out = fl32(q * s[n, k / g]).
+ * dq_gemv_group / dq_gemm_group: y[m,n] = sum_k x[m,k] q[n,k] s[n, k/g]; each
+ * group's partial sum (fp32, exact products) is scaled as the group ends.
+ * Other arguments as for the per-row entry points. */
+dq_status dq_quantize_pack_group(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                 int32_t bits, int64_t group, uint32_t* packed, float* scales,
+                                 void* stream);
+dq_status dq_unpack_group(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
+                          int32_t bits, int64_t group, int32_t* q_out, float* w_out, void* stream);
+dq_status dq_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                        int64_t N, int64_t K, int32_t bits, int64_t group, float* y, void* stream);
+dq_status dq_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                        int64_t N, int64_t K, int32_t bits, int64_t group, float* y, void* stream);
 
 /* Asymmetric variant ("量化" tutorial, "量化怎么工作": a zero point added to
  * the rounded quotient, for distributions not centred on zero).  Per row n,

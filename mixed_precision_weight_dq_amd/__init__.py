@@ -15,6 +15,8 @@ kernels behind the C ABI declared in ``include/dq.h``):
   allocate outputs with torch and raise ``DQError`` on a non-zero status.
 * ``quantize_pack_asym``, ``unpack_asym``, ``x_sum``, ``gemv_asym``,
   ``gemm_asym`` -- the asymmetric (zero-point) variant on torch tensors.
+* ``quantize_pack_group``, ``unpack_group``, ``gemv_group``, ``gemm_group``
+  -- group-wise scales (one per g codes of a row) on torch tensors.
 * ``sensitivity``, ``allocate_bits`` -- the host-side allocation calls on
   numpy arrays (the recipe: one bit width per matrix).
 * ``write_packed_file``, ``PackedFile`` -- the on-disk packed-weight format
@@ -40,7 +42,8 @@ __all__ = [
     "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS", "DQFileMatrix",
     "write_packed_file", "PackedFile", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
     "dq_gemv_asym", "dq_gemm_asym", "quantize_pack_asym", "unpack_asym", "x_sum", "gemv_asym",
-    "gemm_asym",
+    "gemm_asym", "dq_quantize_pack_group", "dq_unpack_group", "dq_gemv_group", "dq_gemm_group",
+    "quantize_pack_group", "unpack_group", "gemv_group", "gemm_group",
 ]
 
 (DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP,
@@ -104,6 +107,14 @@ def load():
     lib.dq_gemv_asym.restype = st
     lib.dq_gemm_asym.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
     lib.dq_gemm_asym.restype = st
+    lib.dq_quantize_pack_group.argtypes = [vp, i32, i64, i64, i32, i64, vp, vp, vp]
+    lib.dq_quantize_pack_group.restype = st
+    lib.dq_unpack_group.argtypes = [vp, vp, i64, i64, i32, i64, vp, vp, vp]
+    lib.dq_unpack_group.restype = st
+    lib.dq_gemv_group.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
+    lib.dq_gemv_group.restype = st
+    lib.dq_gemm_group.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
+    lib.dq_gemm_group.restype = st
     fp = ctypes.POINTER(DQFileMatrix)
     lib.dq_file_write.argtypes = [ctypes.c_char_p, fp, i64]
     lib.dq_file_write.restype = st
@@ -166,6 +177,26 @@ def dq_gemv_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int
 def dq_gemm_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int, N: int, K: int,
                  bits: int, y: int, stream: int = 0) -> int:
     return int(load().dq_gemm_asym(x, M, packed, scales, zeros, xsum, N, K, bits, y, stream))
+
+
+def dq_quantize_pack_group(w: int, w_dtype: int, N: int, K: int, bits: int, group: int,
+                           packed: int, scales: int, stream: int = 0) -> int:
+    return int(load().dq_quantize_pack_group(w, w_dtype, N, K, bits, group, packed, scales, stream))
+
+
+def dq_unpack_group(packed: int, scales: int, N: int, K: int, bits: int, group: int, q_out: int,
+                    w_out: int, stream: int = 0) -> int:
+    return int(load().dq_unpack_group(packed, scales, N, K, bits, group, q_out, w_out, stream))
+
+
+def dq_gemv_group(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, group: int,
+                  y: int, stream: int = 0) -> int:
+    return int(load().dq_gemv_group(x, M, packed, scales, N, K, bits, group, y, stream))
+
+
+def dq_gemm_group(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, group: int,
+                  y: int, stream: int = 0) -> int:
+    return int(load().dq_gemm_group(x, M, packed, scales, N, K, bits, group, y, stream))
 
 
 def dq_row_sumsq(w: int, w_dtype: int, N: int, K: int, row_sumsq: int, matrix_sumsq: int,
@@ -356,6 +387,69 @@ def gemv_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
 def gemm_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
     """y = s * x . (u - z)^T on the matrix cores (any M >= 1)."""
     return _matmul_asym(dq_gemm_asym, "dq_gemm_asym", x, packed, scales, zeros, xsum, K, bits, y)
+
+
+def quantize_pack_group(w, bits: int, group: int):
+    """Group-wise scales: W[N, K] -> (packed int32 [N, row_words], scales float32
+    [N, ceil(K / group)])."""
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16), 2)
+    N, K = w.shape
+    packed = torch.empty((N, packed_row_bytes(K, bits) // 4), dtype=torch.int32, device=w.device)
+    scales = torch.empty((N, -(-K // group)), dtype=torch.float32, device=w.device)
+    dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
+    _check(dq_quantize_pack_group(w.data_ptr(), dt, N, K, bits, group, packed.data_ptr(),
+                                  scales.data_ptr(), _stream(w)), "dq_quantize_pack_group")
+    return packed, scales
+
+
+def unpack_group(packed, scales, K: int, bits: int, group: int, want_q: bool = True,
+                 want_w: bool = False):
+    torch = _torch()
+    _need(packed, "packed", (torch.int32,), 2)
+    N = packed.shape[0]
+    if packed.shape[1] != packed_row_bytes(K, bits) // 4:
+        raise ValueError("packed row length does not match K and bits")
+    if scales is not None:
+        _need(scales, "scales", (torch.float32,), 2)
+        if tuple(scales.shape) != (N, -(-K // group)):
+            raise ValueError("scales must be [N, ceil(K / group)]")
+    q = torch.empty((N, K), dtype=torch.int32, device=packed.device) if want_q else None
+    w = torch.empty((N, K), dtype=torch.float32, device=packed.device) if want_w else None
+    _check(dq_unpack_group(packed.data_ptr(), scales.data_ptr() if scales is not None else 0, N, K,
+                           bits, group, q.data_ptr() if q is not None else 0,
+                           w.data_ptr() if w is not None else 0, _stream(packed)),
+           "dq_unpack_group")
+    return q, w
+
+
+def _matmul_group(fn, name, x, packed, scales, K: int, bits: int, group: int, y=None):
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(packed, "packed", (torch.int32,), 2)
+    _need(scales, "scales", (torch.float32,), 2)
+    M, N = x.shape[0], packed.shape[0]
+    if (x.shape[1] != K or packed.shape[1] != packed_row_bytes(K, bits) // 4
+            or tuple(scales.shape) != (N, -(-K // group))):
+        raise ValueError("shape mismatch between x, packed, scales, K, bits and group")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(fn(x.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K, bits, group,
+              y.data_ptr(), _stream(x)), name)
+    return y
+
+
+def gemv_group(x, packed, scales, K: int, bits: int, group: int, y=None):
+    """y = sum_k x q s[n, k / group] for 1 <= M <= 16."""
+    return _matmul_group(dq_gemv_group, "dq_gemv_group", x, packed, scales, K, bits, group, y)
+
+
+def gemm_group(x, packed, scales, K: int, bits: int, group: int, y=None):
+    """The same on the bf16 matrix cores (any M >= 1)."""
+    return _matmul_group(dq_gemm_group, "dq_gemm_group", x, packed, scales, K, bits, group, y)
 
 
 def row_sumsq(w, want_total: bool = True):

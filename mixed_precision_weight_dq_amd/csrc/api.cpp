@@ -32,6 +32,9 @@ dq_status check_common(int64_t N, int64_t K, int32_t bits)
     return DQ_OK;
 }
 
+// group sizes: powers of two from one chunk (32 codes) to 2048
+bool valid_group(int64_t g) { return g >= 32 && g <= DQ_MAX_GROUP && (g & (g - 1)) == 0; }
+
 }  // namespace
 
 int32_t dq::record_hip_error(hipError_t e) { return hip_status(e); }
@@ -92,7 +95,7 @@ dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int6
     if (st != DQ_OK) return st;
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(q_out, 4) || !aligned(w_out, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_unpack(packed, scales, nullptr, N, K, bits, q_out, w_out,
+    return hip_status(dq::launch_unpack(packed, scales, nullptr, 0, N, K, bits, q_out, w_out,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -120,8 +123,62 @@ dq_status dq_unpack_asym(const uint32_t* packed, const float* scales, const int3
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(q_out, 4) ||
         !aligned(w_out, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_unpack(packed, scales, zeros, N, K, bits, q_out, w_out,
+    return hip_status(dq::launch_unpack(packed, scales, zeros, 0, N, K, bits, q_out, w_out,
                                         static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_quantize_pack_group(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                 int32_t bits, int64_t group, uint32_t* packed, float* scales,
+                                 void* stream)
+{
+    if (!w || !packed || !scales) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (!valid_group(group)) return DQ_ERR_SHAPE;
+    if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_quantize_pack_group(w, w_dtype == DQ_BF16, N, K, bits, group,
+                                                     packed, scales,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_unpack_group(const uint32_t* packed, const float* scales, int64_t N, int64_t K,
+                          int32_t bits, int64_t group, int32_t* q_out, float* w_out, void* stream)
+{
+    if (!packed || (!q_out && !w_out) || (w_out && !scales)) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (!valid_group(group)) return DQ_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(q_out, 4) || !aligned(w_out, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_unpack(packed, scales, nullptr, group, N, K, bits, q_out, w_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                        int64_t N, int64_t K, int32_t bits, int64_t group, float* y, void* stream)
+{
+    if (!x || !packed || !scales || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > DQ_GEMV_MAX_M || !valid_group(group)) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_gemv_group(x, M, packed, scales, N, K, bits, group, y,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
+                        int64_t N, int64_t K, int32_t bits, int64_t group, float* y, void* stream)
+{
+    if (!x || !packed || !scales || !y) return DQ_ERR_NULL;
+    dq_status st = check_common(N, K, bits);
+    if (st != DQ_OK) return st;
+    if (M < 1 || M > 0x7fffffffLL || !valid_group(group)) return DQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return DQ_ERR_ALIGN;
+    return hip_status(dq::launch_gemm_group(x, M, packed, scales, N, K, bits, group, y,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, void* stream)

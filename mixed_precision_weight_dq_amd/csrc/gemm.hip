@@ -718,7 +718,173 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
     return hipGetLastError();
 }
 
+// Group-wise scales ("量化" tutorial, exercise 1 of its exercises; scales
+// [N, G], one per group of g codes, g a multiple of 32).  The 128 x 128 tile of
+// gemm_kernel with one change: each 32-wide K slice lies inside one group, so
+// the MFMAs of a group accumulate into a second set of registers that is
+// scaled per output column by that group's scale and added to the result
+// when the group ends.  No scale is left for the epilogue.
+template <int B>
+__global__ __launch_bounds__(kGemmThreads) void gemm_group_kernel(
+    const uint16_t* __restrict__ x, int64_t M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words, int64_t group,
+    int64_t G, float* __restrict__ y)
+{
+    constexpr bool kSplit = B >= 10;
+    constexpr int kPlanes = kSplit ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[kPlanes][kBN * kLd];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int64_t ntn = ceil_div(N, kBN);
+    const int64_t tile = blockIdx.x;
+    const int64_t m0 = (tile / ntn) * kBM;
+    const int64_t n0 = (tile % ntn) * kBN;
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const bool xvec = (K & 7) == 0;
+
+    f32x4_t acc[4][4], part[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            part[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int sr = tid >> 1;  // staging row within the tile
+    const int sh = tid & 1;   // which 32-wide half of the k slice
+
+    for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+        {
+            const int64_t m = m0 + sr;
+            const int64_t kb = k0 + kChunk * sh;
+            uint16_t* dst = &As[sr * kLd + kChunk * sh];
+            if (m < M && xvec && kb + kChunk <= K) {
+                const uint4* src = reinterpret_cast<const uint4*>(x + m * K + kb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(dst)[i] = src[i];
+            } else {
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j)
+                    dst[j] = (m < M && kb + j < K) ? x[m * K + kb + j] : (uint16_t)0;
+            }
+        }
+        {
+            const int64_t n = n0 + sr;
+            const int64_t c = k0 / kChunk + sh;
+            uint32_t wd[B];
+            const bool live = n < N && c < nchunks;
+            if (live) {
+                load_chunk_words<B>(packed + n * row_words, c, row_words, wd);
+            } else {
+#pragma unroll
+                for (int i = 0; i < B; ++i) wd[i] = 0;
+            }
+#pragma unroll
+            for (int i = 0; i < B; ++i) wd[i] ^= code_msb_mask<B>(i);
+            uint16_t* d0 = &Bs[0][sr * kLd + kChunk * sh];
+            uint16_t* d1 = &Bs[kPlanes - 1][sr * kLd + kChunk * sh];
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                int32_t q = chunk_code_signed<B>(wd, j);
+                if (!live || c * kChunk + j >= K) q = 0;
+                if (kSplit) {
+                    d0[j] = exact_bf16_bits((q >> 6) * 64);
+                    d1[j] = exact_bf16_bits(q & 63);
+                } else {
+                    d0[j] = exact_bf16_bits(q);
+                }
+            }
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int kk = 0; kk < kBK / 32; ++kk) {
+            const int kcol = kk * 32 + 8 * (lane >> 4);
+            bf16x8_t a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8_t*>(
+                    &As[(wm * 64 + i * 16 + (lane & 15)) * kLd + kcol]);
+#pragma unroll
+            for (int p = 0; p < kPlanes; ++p) {
+                bf16x8_t b[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b[j] = *reinterpret_cast<const bf16x8_t*>(
+                        &Bs[p][(wn * 64 + j * 16 + (lane & 15)) * kLd + kcol]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j],
+                                                                             part[i][j], 0, 0, 0);
+            }
+            // the slice [kend - 32, kend) closes its group: fold it in
+            const int64_t kend = k0 + 32 * (kk + 1);
+            if (kend % group == 0 || kend >= K) {
+                const int64_t gi = (kend - 1) / group;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+                    const float sg = n < N ? scales[n * G + gi] : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sg, part[i][j][r], acc[i][j][r]);
+                        part[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            }
+            if (kend >= K) break;
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds column lane&15, rows 4*(lane>>4)+r
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+                if (m < M) y[m * N + n] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+template <int B>
+hipError_t launch_gemm_group_b(const uint16_t* x, int64_t M, const uint32_t* packed,
+                               const float* scales, int64_t N, int64_t K, int64_t group, float* y,
+                               hipStream_t stream)
+{
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t tiles = ceil_div(N, kBN) * ceil_div(M, kBM);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    gemm_group_kernel<B><<<dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream>>>(
+        x, M, packed, scales, N, K, rw, group, ceil_div(K, group), y);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed,
+                             const float* scales, int64_t N, int64_t K, int bits, int64_t group,
+                             float* y, hipStream_t stream)
+{
+#define CALL(B) launch_gemm_group_b<B>(x, M, packed, scales, N, K, group, y, stream)
+    DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+}
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,

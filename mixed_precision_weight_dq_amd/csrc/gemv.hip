@@ -943,7 +943,101 @@ hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
     return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y, zp, stream);
 }
 
+// Group-wise scales ("量化" tutorial, exercise 1 of its exercises: one scale
+// per group of g = 32 gpc consecutive codes of a row, scales [N, G]): each
+// chunk's partial dot product is multiplied by its group's scale before it
+// joins the row's sum, so no scale is left for the epilogue.  Four waves, one
+// row per wave; lanes take chunks lane, lane + 64, ...; x is read straight
+// from global memory (at most 16 rows, cached).
+template <int B, int MT>
+__global__ __launch_bounds__(4 * kWave) void gemv_group_kernel(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words, int gpc, int64_t G,
+    float* __restrict__ y)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N) return;  // the whole wave leaves; nothing waits on it
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const uint32_t* __restrict__ row = packed + n * row_words;
+    const bool xvec = (K & 7) == 0;
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    for (int64_t c = lane; c < nchunks; c += kWave) {
+        const int64_t k0 = c * kChunk;
+        uint32_t wd[B];
+        load_chunk_words<B>(row, c, row_words, wd);
+#pragma unroll
+        for (int i = 0; i < B; ++i) wd[i] ^= code_msb_mask<B>(i);
+        float q[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j)
+            q[j] = k0 + j < K ? (float)chunk_code_signed<B>(wd, j) : 0.0f;
+        const float sg = scales[n * G + c / gpc];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m >= M) break;
+            const uint16_t* xr = x + (int64_t)m * K + k0;
+            float dot = 0.0f;
+            if (xvec && k0 + kChunk <= K) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 d = reinterpret_cast<const uint4*>(xr)[i];
+                    const uint32_t e[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        dot = fmaf(__uint_as_float(e[t] << 16), q[8 * i + 2 * t], dot);
+                        dot = fmaf(__uint_as_float(e[t] & 0xffff0000u), q[8 * i + 2 * t + 1], dot);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j)
+                    if (k0 + j < K) dot = fmaf(bf16_bits_to_float(xr[j]), q[j], dot);
+            }
+            acc[m] = fmaf(dot, sg, acc[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = wave_sum(acc[m]);
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < M) y[(int64_t)m * N + n] = acc[m];
+    }
+}
+
+template <int B>
+hipError_t launch_gemv_group_b(const uint16_t* x, int64_t M, const uint32_t* packed,
+                               const float* scales, int64_t N, int64_t K, int64_t group, float* y,
+                               hipStream_t stream)
+{
+    const int64_t rw = packed_row_words(K, B);
+    const dim3 grid((unsigned)ceil_div(N, 4)), block(4 * kWave);
+    const int gpc = (int)(group / kChunk);
+    const int64_t G = ceil_div(K, group);
+#define DQ_GROUP(MT) \
+    gemv_group_kernel<B, MT><<<grid, block, 0, stream>>>(x, (int)M, packed, scales, N, K, rw, gpc, G, y)
+    if (M <= 1) DQ_GROUP(1);
+    else if (M <= 2) DQ_GROUP(2);
+    else if (M <= 4) DQ_GROUP(4);
+    else if (M <= 8) DQ_GROUP(8);
+    else DQ_GROUP(16);
+#undef DQ_GROUP
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packed,
+                             const float* scales, int64_t N, int64_t K, int bits, int64_t group,
+                             float* y, hipStream_t stream)
+{
+#define CALL(B) launch_gemv_group_b<B>(x, M, packed, scales, N, K, group, y, stream)
+    DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+}
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,

@@ -15,10 +15,20 @@ hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64
                                       double* matrix_sumsq, hipStream_t stream);
 hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
                             double* matrix_sumsq, hipStream_t stream);
-// zeros: null for the symmetric scheme (q = u - 2^(b-1)), else q = u - zeros[n]
+// zeros: null for the symmetric scheme (q = u - 2^(b-1)), else q = u - zeros[n];
+// group: 0 for one scale per row, else scales [N, ceil(K / group)]
 hipError_t launch_unpack(const uint32_t* packed, const float* scales, const int32_t* zeros,
-                         int64_t N, int64_t K, int bits, int32_t* q_out, float* w_out,
-                         hipStream_t stream);
+                         int64_t group, int64_t N, int64_t K, int bits, int32_t* q_out,
+                         float* w_out, hipStream_t stream);
+hipError_t launch_quantize_pack_group(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                      int64_t group, uint32_t* packed, float* scales,
+                                      hipStream_t stream);
+hipError_t launch_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packed,
+                             const float* scales, int64_t N, int64_t K, int bits, int64_t group,
+                             float* y, hipStream_t stream);
+hipError_t launch_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed,
+                             const float* scales, int64_t N, int64_t K, int bits, int64_t group,
+                             float* y, hipStream_t stream);
 // zeros / xsum: the asymmetric scheme's zero points [N] and sum_k x[m, k]
 // [M]; both null for the symmetric scheme.
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,

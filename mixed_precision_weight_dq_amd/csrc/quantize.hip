@@ -233,6 +233,71 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
 }
 
+// Group-wise scales ("量化" tutorial, exercise 1 of its exercises: one scale
+// per group of g consecutive weights of a row, g = 32 gpc with gpc a power of
+// two up to 64).  Each group is quantized exactly as a row of the per-row
+// kernel above, with its own scale at scales[n * G + j], G = ceil(K / g).
+// A group is gpc whole chunks held by gpc neighbouring lanes (aligned, inside
+// one wave), so its max|w| is a butterfly over those lanes and the kernel
+// needs one pass: every lane loads its chunk once, quantizes and stores it.
+template <int B, bool BF16, bool kAligned>
+__global__ __launch_bounds__(kQuantThreads) void quantize_pack_group_kernel(
+    const void* __restrict__ w, int64_t K, int64_t row_words, int gpc, int64_t G,
+    uint32_t* __restrict__ packed, float* __restrict__ scales)
+{
+    constexpr int32_t kQmax = (1 << (B - 1)) - 1;
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int threads = blockDim.x;
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int64_t row_off = n * K;
+    const int esize = BF16 ? 2 : 4;
+    const bool vec_ok = ((K * esize) & 15) == 0;
+    const float qmaxf = (float)kQmax;
+    const float margin = 0.5f - ldexpf(qmaxf + 1.0f, -21);
+    uint32_t* __restrict__ prow = packed + n * row_words;
+
+    // every lane of a wave takes part in each round (the butterfly needs them)
+    for (int64_t c0 = 0; c0 < nchunks; c0 += threads) {
+        const int64_t c = c0 + tid;
+        float v[kChunk];
+        uint32_t amax = 0;
+        if (c < nchunks) {
+            load_row_chunk<BF16, kAligned>(w, row_off, K, c, vec_ok, v);
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                const uint32_t m = __float_as_uint(v[j]) & 0x7fffffffu;
+                amax = m > amax ? m : amax;
+            }
+        }
+        for (int d = 1; d < gpc; d <<= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)amax, d, kWave);
+            amax = o > amax ? o : amax;
+        }
+        float s;
+        bool zero_codes;
+        if (amax >= 0x7f800000u) {  // a NaN or an infinity in the group
+            s = __uint_as_float(0x7fc00000u);
+            zero_codes = true;
+        } else {
+            const float a = __uint_as_float(amax);
+            s = (a == 0.0f ? 1.0f : a) / qmaxf;
+            zero_codes = (a == 0.0f);
+            if (s == 0.0f) {  // max / qmax underflowed: an all-zero group
+                s = 1.0f / qmaxf;
+                zero_codes = true;
+            }
+        }
+        if (c < nchunks) {
+            if (c % gpc == 0) scales[n * G + c / gpc] = s;
+            uint32_t out[B];
+            quantize_chunk<B>(v, s, 1.0f / s, margin, zero_codes, c * kChunk, K, out);
+            store_chunk<B>(prow, c, row_words, out);
+        }
+    }
+    for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
+}
+
 // Asymmetric scheme ("量化" tutorial, "量化怎么工作": a zero point added to the
 // rounded quotient, for rows not centred on zero).  Per row, with L = 2^b - 1:
 // lo = min(0, min w), hi = max(0, max w), s = fl32(fl32(hi - lo) / L) (1.0
@@ -426,15 +491,18 @@ constexpr int kUnpackThreads = 256;
 template <int B>
 __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ scales,
-    const int32_t* __restrict__ zeros, int64_t K, int64_t row_words, int32_t* __restrict__ q_out,
-    float* __restrict__ w_out)
+    const int32_t* __restrict__ zeros, int64_t group, int64_t K, int64_t row_words,
+    int32_t* __restrict__ q_out, float* __restrict__ w_out)
 {
     constexpr uint32_t kMask = (1u << B) - 1u;
     const int64_t n = blockIdx.x;
     // the code's offset: 2^(b-1) (symmetric scheme) or the row's zero point
     const int32_t kBias = zeros ? zeros[n] : (1 << (B - 1));
     const uint32_t* __restrict__ row = packed + n * row_words;
-    const float s = w_out ? scales[n] : 0.0f;
+    // group > 0: a scale per group of `group` codes (a multiple of 4, so the
+    // 4 codes of a thread share it); else one per row
+    const int64_t G = group > 0 ? ceil_div(K, group) : 0;
+    const float s_row = w_out && group == 0 ? scales[n] : 0.0f;
     // 16-byte stores need every output row start 16-byte aligned
     const bool vec = (K & 3) == 0 && ((reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(w_out)) & 15) == 0;
     for (int64_t k0 = 4 * (int64_t)threadIdx.x; k0 < K; k0 += 4 * kUnpackThreads) {
@@ -451,6 +519,7 @@ __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) q[j] = (int32_t)((uint32_t)(v >> (j * B)) & kMask) - kBias;
         const int64_t o = n * K + k0;
+        const float s = w_out && group > 0 ? scales[n * G + k0 / group] : s_row;
         if (vec) {
             if (q_out) *reinterpret_cast<int4*>(q_out + o) = make_int4(q[0], q[1], q[2], q[3]);
             if (w_out)
@@ -592,11 +661,12 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
 
 template <int B>
 hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, const int32_t* zeros,
-                           int64_t N, int64_t K, int32_t* q_out, float* w_out, hipStream_t stream)
+                           int64_t group, int64_t N, int64_t K, int32_t* q_out, float* w_out,
+                           hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
-    unpack_kernel<B><<<dim3((unsigned)N), dim3(kUnpackThreads), 0, stream>>>(packed, scales, zeros,
-                                                                            K, rw, q_out, w_out);
+    unpack_kernel<B><<<dim3((unsigned)N), dim3(kUnpackThreads), 0, stream>>>(
+        packed, scales, zeros, group, K, rw, q_out, w_out);
     return hipGetLastError();
 }
 
@@ -649,6 +719,34 @@ hipError_t launch_quantize_pack_asym_b(const void* w, bool bf16, int64_t N, int6
     return hipGetLastError();
 }
 
+template <int B>
+hipError_t launch_quantize_pack_group_b(const void* w, bool bf16, int64_t N, int64_t K,
+                                        int64_t group, uint32_t* packed, float* scales,
+                                        hipStream_t stream)
+{
+    const int64_t rw = packed_row_words(K, B);
+    const int64_t nchunks = ceil_div(K, kChunk);
+    const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
+                                                       : ceil_div(nchunks, kWave) * kWave);
+    const dim3 grid((unsigned)N), block(threads);
+    const int gpc = (int)(group / kChunk);
+    const int64_t G = ceil_div(K, group);
+    const bool aligned = K % kChunk == 0;
+    if (bf16 && aligned)
+        quantize_pack_group_kernel<B, true, true>
+            <<<grid, block, 0, stream>>>(w, K, rw, gpc, G, packed, scales);
+    else if (bf16)
+        quantize_pack_group_kernel<B, true, false>
+            <<<grid, block, 0, stream>>>(w, K, rw, gpc, G, packed, scales);
+    else if (aligned)
+        quantize_pack_group_kernel<B, false, true>
+            <<<grid, block, 0, stream>>>(w, K, rw, gpc, G, packed, scales);
+    else
+        quantize_pack_group_kernel<B, false, false>
+            <<<grid, block, 0, stream>>>(w, K, rw, gpc, G, packed, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_row_sumsq(const void* w, bool bf16, int64_t N, int64_t K, double* row_sumsq,
                             double* matrix_sumsq, hipStream_t stream)
 {
@@ -677,6 +775,15 @@ hipError_t launch_quantize_pack_asym(const void* w, bool bf16, int64_t N, int64_
 #undef CALL
 }
 
+hipError_t launch_quantize_pack_group(const void* w, bool bf16, int64_t N, int64_t K, int bits,
+                                      int64_t group, uint32_t* packed, float* scales,
+                                      hipStream_t stream)
+{
+#define CALL(B) launch_quantize_pack_group_b<B>(w, bf16, N, K, group, packed, scales, stream)
+    DQ_BITS_SWITCH(bits, CALL)
+#undef CALL
+}
+
 hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hipStream_t stream)
 {
     if (K % 8 == 0)  // 16-byte rows (x itself is 16-byte aligned)
@@ -687,10 +794,10 @@ hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hi
 }
 
 hipError_t launch_unpack(const uint32_t* packed, const float* scales, const int32_t* zeros,
-                         int64_t N, int64_t K, int bits, int32_t* q_out, float* w_out,
-                         hipStream_t stream)
+                         int64_t group, int64_t N, int64_t K, int bits, int32_t* q_out,
+                         float* w_out, hipStream_t stream)
 {
-#define CALL(B) launch_unpack_b<B>(packed, scales, zeros, N, K, q_out, w_out, stream)
+#define CALL(B) launch_unpack_b<B>(packed, scales, zeros, group, N, K, q_out, w_out, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
 }

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
                  "dq_status_string", "dq_last_error", "dq_quantize_pack_sumsq", "dq_sensitivity",
                  "dq_row_sumsq", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
-                 "dq_gemv_asym", "dq_gemm_asym", "dq_file_write", "dq_file_open", "dq_file_count",
+                 "dq_gemv_asym", "dq_gemm_asym", "dq_quantize_pack_group", "dq_unpack_group",
+                 "dq_gemv_group", "dq_gemm_group", "dq_file_write", "dq_file_open", "dq_file_count",
                  "dq_file_matrix_info", "dq_file_verify", "dq_file_load", "dq_file_close",
                  "dq_allocate_bits"):
         assert want in names
@@ -186,3 +187,23 @@ def test_asym_arguments_rejected():
         assert fn(A, 1, A, A, A, A, 4, 64, 1, A) == dq.DQ_ERR_BITS
         assert fn(A, 1, A, A, A + 2, A, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
         assert fn(A, 1, A, A, A, A + 2, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("group", [0, 16, 31, 48, 96, 4096, -32])
+def test_group_sizes_rejected(group):
+    assert dq.dq_quantize_pack_group(A, dq.DQ_BF16, 4, 64, 6, group, A, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_unpack_group(A, A, 4, 64, 6, group, A, 0) == dq.DQ_ERR_SHAPE
+    assert dq.dq_gemv_group(A, 1, A, A, 4, 64, 6, group, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_gemm_group(A, 1, A, A, 4, 64, 6, group, A) == dq.DQ_ERR_SHAPE
+
+
+def test_group_arguments_rejected():
+    assert dq.dq_quantize_pack_group(A, dq.DQ_BF16, 4, 64, 6, 32, A, 0) == dq.DQ_ERR_NULL
+    assert dq.dq_quantize_pack_group(A, dq.DQ_BF16, 4, 64, 17, 32, A, A) == dq.DQ_ERR_BITS
+    assert dq.dq_quantize_pack_group(A, 5, 4, 64, 6, 32, A, A) == dq.DQ_ERR_DTYPE
+    assert dq.dq_quantize_pack_group(A, dq.DQ_BF16, 4, 64, 6, 32, A, A + 1) == dq.DQ_ERR_ALIGN
+    assert dq.dq_unpack_group(A, 0, 4, 64, 6, 32, 0, A) == dq.DQ_ERR_NULL
+    assert dq.dq_gemv_group(A, 17, A, A, 4, 64, 6, 32, A) == dq.DQ_ERR_SHAPE
+    assert dq.dq_gemv_group(MIS, 1, A, A, 4, 64, 6, 32, A) == dq.DQ_ERR_ALIGN
+    assert dq.dq_gemm_group(A, 1, A, 0, 4, 64, 6, 32, A) == dq.DQ_ERR_NULL
+    assert dq.dq_gemm_group(A, 0, A, A, 4, 64, 6, 32, A) == dq.DQ_ERR_SHAPE
