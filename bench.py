@@ -237,6 +237,64 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
                     "median of the step count, outside the timed steps"}
 
 
+def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 128):
+    """Group-wise scales (one per 128 codes), outside the timed steps, on the
+    step's own inputs: quantize + pack of the five decode matrices, the decode
+    group (8 tokens x 5 GEMVs on rotated copies) and the b = 6 prefill GEMM."""
+    Nd, Kd = next(iter(W2.values())).shape
+    q = {b: dq.quantize_pack_group(W, b, group) for b, W in W2.items()}
+    copies = [q] + [{b: (P.clone(), S) for b, (P, S) in q.items()} for _ in range(len(X1t) - 1)]
+    ys = {b: torch.empty((1, Nd), dtype=torch.float32, device=W.device) for b, W in W2.items()}
+    cs = stream.cuda_stream
+    lib = dq.load()
+    calls = [(lib.dq_gemv_group, (X.data_ptr(), 1, P.data_ptr(), S.data_ptr(), Nd, Kd, b, group,
+                                  ys[b].data_ptr(), cs))
+             for t, X in enumerate(X1t) for b, (P, S) in copies[t].items()]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    def quant():
+        for b, W in W2.items():
+            dq.quantize_pack_group(W, b, group)
+
+    def decode():
+        for fn, a in calls:
+            fn(*a)
+
+    P6, S6 = dq.quantize_pack_group(W4[6], 6, group)
+    Y = torch.empty((X4.shape[0], P6.shape[0]), dtype=torch.float32, device=X4.device)
+
+    def gemm():
+        dq.gemm_group(X4, P6, S6, X4.shape[1], 6, group, Y)
+
+    t_q, t_d, t_g = timed(quant), timed(decode), timed(gemm)
+    G = -(-Kd // group)
+    dec_bytes = len(X1t) * sum(Nd * (Kd * b // 8 + G * 4) for b in W2)
+    q_bytes = sum(Nd * (Kd * (16 + b) // 8 + G * 4) for b in W2)
+    M, K = X4.shape
+    N = P6.shape[0]
+    return {"group": group,
+            "quantize_pack_4096_gbs": round(q_bytes / (t_q * 1e-3) / 1e9, 1),
+            "gemv_m1_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
+            "gemv_m1_per_launch_us": round(t_d / len(calls) * 1e3, 3),
+            "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
+            "what": "group-wise scales (g=128) on the step's inputs: quantize+pack (read + write "
+                    "bytes), decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed "
+                    "words + group scales per second), prefill GEMM M=2048 b=6 (128x128 tiles); "
+                    "median of the step count, outside the timed steps"}
+
+
 def packed_file_context(torch, dq, stream, packs, reps: int = 5):
     """The on-disk format, outside the timed steps: the five packed decode
     matrices written to a temporary file, mapped, checked and copied back into
@@ -686,6 +744,7 @@ def main():
     out["allocation"] = {"row_sumsq": row_sumsq_context(torch, dq, stream, list(W4.values()),
                                                         reps=max(5, args.steps))}
     out["asymmetric"] = asym_context(torch, dq, stream, W2, X1t, W4, X4, reps=max(5, args.steps))
+    out["group_scales"] = group_context(torch, dq, stream, W2, X1t, W4, X4, reps=max(5, args.steps))
     out["packed_file"] = packed_file_context(
         torch, dq, stream, {b: (P2[b], S2[b], DECODE["K"]) for b in W2})
     if not args.no_stack:
