@@ -291,7 +291,7 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
             "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
             "what": "group-wise scales (g=128) on the step's inputs: quantize+pack (read + write "
                     "bytes), decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed "
-                    "words + group scales per second), prefill GEMM M=2048 b=6 (128x128 tiles); "
+                    "words + group scales per second), prefill GEMM M=2048 b=6 (pipelined 128-row tiles, each group folded in as it ends); "
                     "median of the step count, outside the timed steps"}
 
 

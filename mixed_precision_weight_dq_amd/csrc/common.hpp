@@ -204,11 +204,36 @@ struct TileZeroPoints {
     }
 };
 
+// Group-wise scales for the pipelined 128-row GEMM: one scale per row and
+// group of `steps` 64-wide K steps (scales [N, G]).  The kernel accumulates a
+// group's MFMAs apart and folds them in, scaled, when the group ends, so the
+// epilogue applies no row scale.  No zero points.
+struct GroupScales {
+    const float* scales;
+    int64_t G;
+    int64_t steps;
+};
+
+template <class P>
+struct is_group_scales {
+    static constexpr bool value = false;
+};
+template <>
+struct is_group_scales<GroupScales> {
+    static constexpr bool value = true;
+};
+
 // Stage rows [m0, m0 + rows) of the activation sums into `lds` (a buffer the
 // workgroup no longer uses) between two barriers; every thread of the
 // workgroup must call it.  The symmetric scheme stages nothing.
 __device__ __forceinline__ NoZeroPoints stage_tile_zero_points(NoZeroPoints, float*, int64_t,
                                                                int64_t, int)
+{
+    return {};
+}
+
+__device__ __forceinline__ NoZeroPoints stage_tile_zero_points(GroupScales, float*, int64_t, int64_t,
+                                                               int)
 {
     return {};
 }

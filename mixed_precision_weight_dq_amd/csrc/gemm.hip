@@ -214,6 +214,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 {
     using T = MfmaTile<kMT, kNT>;
     constexpr bool kSplit = B >= 10;
+    constexpr bool kGroup = is_group_scales<ZP>::value;
     constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
     __shared__ __attribute__((aligned(16))) uint4 As[T::kStages][T::kPieces];
 
@@ -266,12 +267,22 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     for (int t = 0; t < 4; ++t) abase[t] = c * 8 + ((4 * h + t) ^ xswz(c));
 
     f32x16_t acc[kMT][kNT];
+    // group-wise scales: the current group's MFMAs accumulate here
+    f32x16_t part[kGroup ? kMT : 1][kGroup ? kNT : 1];
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    if constexpr (kGroup) {
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+    }
 
     // codes, ping-pong by step parity: stage st holds step ks (loaded during
     // step ks-1) and is expanded to MFMA operands at the top of step ks while
@@ -298,6 +309,16 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     auto step = [&](auto S, int64_t ks) {  // MFMAs of step ks from stage S
         constexpr int st = decltype(S)::value;
         __syncthreads();  // step ks in LDS for every wave; stage st^1 free again
+        // this step's group scales, loaded every step (unconditional loads
+        // keep the compiler's waits counted) before the next step's prefetch
+        float sg[kNT];
+        if constexpr (kGroup) {
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
+                sg[j] = zp.scales[(n < N ? n : N - 1) * zp.G + ks / zp.steps];
+            }
+        }
         bf16x8_t bh[4][kNT], bl[4][kNT];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -325,12 +346,26 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
                 for (int j = 0; j < kNT; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[t][j], acc[i][j], 0, 0, 0);
+                    f32x16_t& d = kGroup ? part[kGroup ? i : 0][kGroup ? j : 0] : acc[i][j];
+                    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[t][j], d, 0, 0, 0);
                     if constexpr (kSplit)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bl[t][j], acc[i][j], 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bl[t][j], d, 0, 0, 0);
                 }
         }
         store_x(std::integral_constant<int, st ^ 1>{});
+        if constexpr (kGroup) {  // the group ends with this step: fold it in
+            if ((ks + 1) % zp.steps == 0 || ks + 1 == nk) {
+#pragma unroll
+                for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                    for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            acc[i][j][r] = fmaf(sg[j], part[i][j][r], acc[i][j][r]);
+                            part[i][j][r] = 0.0f;
+                        }
+            }
+        }
     };
 
     load_x(0);
@@ -351,7 +386,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
-            const float s = scales[n];
+            const float s = kGroup ? 1.0f : scales[n];
             const float zc = zt.template coef<B>(n);
 #pragma unroll
             for (int i = 0; i < kMT; ++i) {
@@ -359,7 +394,8 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     __builtin_nontemporal_store(
-                        s * zt.apply(acc[i][j][r] * kUnscale, zc, m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                        s * zt.apply(acc[i][j][r] * kUnscale, zc,
+                                     m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
                         yp + (8 * (r >> 2) + (r & 3)) * N);
             }
         }
@@ -369,7 +405,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     for (int j = 0; j < kNT; ++j) {
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
-        const float s = scales[n];
+        const float s = kGroup ? 1.0f : scales[n];
         const float zc = zt.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
@@ -630,7 +666,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     buf_store_f32_nt(yb,
-                                     s * zt.apply(acc[i][j][r] * kUnscale, zc, m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
+                                     s * zt.apply(acc[i][j][r] * kUnscale, zc,
+                                                  m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
                                      voff,
                                      (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * row4);
         }
@@ -867,6 +904,12 @@ hipError_t launch_gemm_group_b(const uint16_t* x, int64_t M, const uint32_t* pac
                                const float* scales, int64_t N, int64_t K, int64_t group, float* y,
                                hipStream_t stream)
 {
+    // groups of whole 64-wide K steps: the pipelined 128-row kernel, whose
+    // MFMAs take codes from two neighbouring 32-code chunks at once
+    if (K % 64 == 0 && group % 64 == 0)
+        return launch_gemm_mfma<B, 4, 1, 2>(x, M, packed, scales, N, K, y,
+                                            GroupScales{scales, ceil_div(K, group), group / 64},
+                                            stream);
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, kBN) * ceil_div(M, kBM);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
