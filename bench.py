@@ -395,7 +395,10 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     for per in (256, 512, 1024):
         outs = [torch.empty((max(1, min(65536, b.numel() * b.element_size() // 16 // per)),),
                             dtype=torch.int32, device=dev) for b in read_bufs]
-        parts[per] = (outs, timed(lambda: [dq.stream_read(b, o.shape[0], o) for b, o in zip(read_bufs, outs)]))
+        lib = dq.load()
+        calls = [(lib.dq_stream_read, (b.data_ptr(), b.numel() * b.element_size(), o.data_ptr(),
+                                       o.shape[0], stream.cuda_stream)) for b, o in zip(read_bufs, outs)]
+        parts[per] = (outs, timed(lambda calls=calls: [fn(*a) for fn, a in calls]))
     per, (outs, read_ms) = min(parts.items(), key=lambda kv: kv[1][1])
     gemv_ms = timed(gemv_group)
     big = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
@@ -589,9 +592,22 @@ def main():
     for b in W4:  # one event group per GEMM (each runs for hundreds of microseconds)
         ops.append(("gemm_2048_b%d" % b, b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
     decode = [(X1t[t], P2t[t][b], S2[b], b, Y1[b]) for t in range(DECODE["tokens"]) for b in W2]
-    for xt, pt, st, b, yt in decode:
-        ops.append(("gemv_m1", b, lambda xt=xt, pt=pt, st=st, b=b, yt=yt:
-                    dq.gemv(xt, pt, st, DECODE["K"], b, yt)))
+    # the decode launches go through the C entry point with their arguments
+    # taken beforehand: the tensor wrapper's checks cost the host more time
+    # than a 4096^2 GEMV takes on the GPU, and a host-bound loop would time the
+    # host (the submission cost is measured and reported below)
+    lib = dq.load()
+    decode_calls = [(lib.dq_gemv, (xt.data_ptr(), 1, pt.data_ptr(), st.data_ptr(), DECODE["N"],
+                                   DECODE["K"], b, yt.data_ptr(), stream.cuda_stream))
+                    for xt, pt, st, b, yt in decode]
+
+    def launch(fn, a):
+        status = fn(*a)
+        if status:
+            raise dq.DQError(status, fn.__name__)
+
+    for (fn, a), (_, _, _, b, _) in zip(decode_calls, decode):
+        ops.append(("gemv_m1", b, lambda fn=fn, a=a: launch(fn, a)))
 
     # one HIP event at every group boundary (events between every launch would
     # add their own dispatch gaps to the tiny GEMV launches)
@@ -628,6 +644,18 @@ def main():
     group_ms = {kind: float(np.mean([ev[s][g].elapsed_time(ev[s][g + 1]) for s in range(args.steps)]))
                 for g, kind in enumerate(kinds)}
     count = {kind: sum(1 for k, _, _ in ops if k == kind) for kind in kinds}
+
+    # host time to issue the decode launches, taken while a GEMM keeps the GPU
+    # busy: below the GPU's per-launch time, the decode group is not host-bound
+    b6 = PREFILL["bits"][1]
+    host_us = []
+    for _ in range(5):
+        dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4)
+        t0 = time.perf_counter()
+        for fn, a in decode_calls:
+            launch(fn, a)
+        host_us.append((time.perf_counter() - t0) / len(decode_calls) * 1e6)
+        torch.cuda.synchronize()
 
     Nd, Kd = DECODE["N"], DECODE["K"]
     Np, Kp, Mp = PREFILL["N"], PREFILL["K"], PREFILL["M"]
@@ -687,7 +715,8 @@ def main():
             "step": "quantize+pack(5 decode) -> unpack(5) -> quantize+pack(4 prefill) -> "
                     "gemm(4) -> decode 8 tokens x gemv(5), token t on copy t of the packed weights",
             "timing": "HIP events at group boundaries on the launch stream; per-launch "
-                      "figures are group time / launches (inter-launch gaps included)",
+                      "figures are group time / launches (inter-launch gaps included); decode "
+                      "launches through the C entry point with prepared arguments",
         },
         "roofline": {
             "kernel": "dq_gemv M=1 N=K=4096 (40 launches back to back: 8 tokens x b=4..8, "
@@ -699,6 +728,7 @@ def main():
             "frac": round(value / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "per_launch_us": round(gemv_ms / count["gemv_m1"] * 1e3, 3),
+            "host_submit_us_per_launch": round(float(np.median(host_us)), 3),
         },
         "roofline_gemm": {
             "kernel": "dq_gemm M=2048 N=K=8192, b=5,6,8 (b=12 listed in per_bits)",
@@ -738,7 +768,7 @@ def main():
     b6 = PREFILL["bits"][1]
     out["roofline"]["attainable_read"] = attainable_read(
         torch, dq, dev, stream,
-        lambda: [dq.gemv(xt, pt, st, DECODE["K"], b, yt) for xt, pt, st, b, yt in decode],
+        lambda: [launch(fn, a) for fn, a in decode_calls],
         [pt for _, pt, _, _, _ in decode],
         lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
     out["allocation"] = {"row_sumsq": row_sumsq_context(torch, dq, stream, list(W4.values()),
