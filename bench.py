@@ -459,6 +459,20 @@ def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
         el = time.perf_counter() - t0
         if el >= target_s:
             break
+    # the oracle's asymmetric and group-wise products on one decode matrix
+    # (b = 6), beside the GPU figures of the same variants
+    variants = {}
+    w6 = decode_w[6]
+    N, K = DECODE["N"], DECODE["K"]
+    for name, prep, run in (
+            ("asymmetric", lambda: oracle.quantize_pack_asym(w6, 6)[:3],
+             lambda q: oracle.matmul_asym(x1, q[0], q[1], q[2], N, K, 6)),
+            ("group_scales_128", lambda: oracle.quantize_pack_group(w6, 6, 128)[:2],
+             lambda q: oracle.matmul_group(x1, q[0], q[1], N, K, 6, 128))):
+        q = prep()
+        t0 = time.perf_counter()
+        run(q)
+        variants[name + "_gemv_gbs"] = round(N * K * 6 / 8 / (time.perf_counter() - t0) / 1e9, 4)
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -469,7 +483,7 @@ def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
             "kind": "oracle",
             "sample": "fp64 GEMV M=1 over the five 4096x4096 decode matrices (b=4..8), "
                       "%d passes, %.1f s" % (reps, el),
-            "cpu": cpu, "allocation_oracle": alloc}
+            "cpu": cpu, "allocation_oracle": alloc, "variants_oracle": variants}
 
 
 def device_info(torch, dev) -> dict:
