@@ -204,14 +204,22 @@ struct TileZeroPoints {
     }
 };
 
-// Group-wise scales for the pipelined 128-row GEMM: one scale per row and
-// group of `steps` 64-wide K steps (scales [N, G]).  The kernel accumulates a
-// group's MFMAs apart and folds them in, scaled, when the group ends, so the
-// epilogue applies no row scale.  No zero points.
+// Group-wise scales for the pipelined 128-row GEMM and the resident-x GEMV:
+// one scale per row and group of `group` codes (scales [N, G]).  The kernels
+// accumulate a group's (or a chunk's) products apart and add them in scaled,
+// so the epilogue applies no row scale.
 struct GroupScales {
     const float* scales;
     int64_t G;
-    int64_t steps;
+    int64_t group;  // codes per group, a power of two >= 32
+
+    // no zero points: the epilogue adds nothing
+    template <int B>
+    __device__ __forceinline__ float coef(int64_t) const
+    {
+        return 0.0f;
+    }
+    __device__ __forceinline__ float apply(float v, float, int64_t) const { return v; }
 };
 
 template <class P>

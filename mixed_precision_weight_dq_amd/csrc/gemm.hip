@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
-                sg[j] = zp.scales[(n < N ? n : N - 1) * zp.G + ks / zp.steps];
+                sg[j] = zp.scales[(n < N ? n : N - 1) * zp.G + ks / (zp.group / 64)];
             }
         }
         bf16x8_t bh[4][kNT], bl[4][kNT];
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
         }
         store_x(std::integral_constant<int, st ^ 1>{});
         if constexpr (kGroup) {  // the group ends with this step: fold it in
-            if ((ks + 1) % zp.steps == 0 || ks + 1 == nk) {
+            if ((ks + 1) % (zp.group / 64) == 0 || ks + 1 == nk) {
 #pragma unroll
                 for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -908,7 +908,7 @@ hipError_t launch_gemm_group_b(const uint16_t* x, int64_t M, const uint32_t* pac
     // MFMAs take codes from two neighbouring 32-code chunks at once
     if (K % 64 == 0 && group % 64 == 0)
         return launch_gemm_mfma<B, 4, 1, 2>(x, M, packed, scales, N, K, y,
-                                            GroupScales{scales, ceil_div(K, group), group / 64},
+                                            GroupScales{scales, ceil_div(K, group), group},
                                             stream);
     const int64_t rw = packed_row_words(K, B);
     const int64_t tiles = ceil_div(N, kBN) * ceil_div(M, kBM);

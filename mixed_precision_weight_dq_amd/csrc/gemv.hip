@@ -17,6 +17,8 @@
 //     and x copied through LDS; else gemv_mfma_kernel): codes expanded to
 //     exact bf16 operands of v_mfma_f32_16x16x32_bf16, so the VALU cost per
 //     code no longer grows with M.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "gemm_tiles.hpp"
@@ -739,7 +741,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 template <int B, int kNT, class ZP>
 hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* packed,
                                const float* scales, int64_t N, int64_t K, float* y, ZP zp,
-                hipStream_t stream)
+                            hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 16 * kNT)), block(kGemvMfmaWaves * kWave);
@@ -760,7 +762,7 @@ hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* pac
 template <int B, class ZP>
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, ZP zp,
-                hipStream_t stream)
+                            hipStream_t stream)
 {
 #ifndef DQ_GEMV_MFMA_NT2_MIN
 #define DQ_GEMV_MFMA_NT2_MIN (1LL << 24)
@@ -788,7 +790,7 @@ hipError_t launch_gemv_mfma(const uint16_t* x, int64_t M, const uint32_t* packed
 // (waiting only for x), then the slice loop.
 constexpr int kXResMax = 48 * 1024;
 
-template <int B, int MT, int kWaves, int kR, class ZP>
+template <int B, int MT, int kWaves, int kR, class ZP, int kRW>
 __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
@@ -799,10 +801,17 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+    // kRW rows per wave (1 or 2): their chunks form one stream of kRW * nchunks
+    // chunks, so a row whose chunk count fills its last 64-chunk slice poorly
+    // shares that slice with the next row
+    static_assert(kRW == 1 || (kRW == 2 && !is_group_scales<ZP>::value), "two rows: per-row scales");
+    const int64_t n = ((int64_t)blockIdx.x * kWaves + wave) * kRW;
     const int64_t nchunks = K / kChunk;
-    const int64_t nslices = ceil_div(nchunks, kSlice);
-    const BufRef wbuf = uniform_buf(packed + (n < N ? n : N - 1) * row_words, (uint32_t)(row_words * 4));
+    const int64_t tchunks = kRW * nchunks;
+    const int64_t nslices = ceil_div(tchunks, kSlice);
+    const int64_t wrows = n < N ? (N - n < kRW ? N - n : kRW) : 1;
+    const BufRef wbuf = uniform_buf(packed + (n < N ? n : N - 1) * row_words,
+                                    (uint32_t)(wrows * row_words * 4));
     const BufRef xall = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
 
     // x piece p (8 elements) = piece p % 4 of chunk slot p / 4 (slot = m * nchunks + chunk)
@@ -820,8 +829,25 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
         xv[r] = make_uint4(d.x, d.y, d.z, d.w);
     }
     uint32_t w[3][B];
+    // group-wise scales: each chunk's scale, loaded (a fixed count) with its codes
+    constexpr bool kGroup = is_group_scales<ZP>::value;
+    uint32_t gsc[3];
+    [[maybe_unused]] BufRef sbuf{};
+    [[maybe_unused]] int gshift = 0;  // log2 of the chunks per group
+    if constexpr (kGroup) {
+        sbuf = uniform_buf(zp.scales + (n < N ? n : N - 1) * zp.G, (uint32_t)(zp.G * 4));
+        gshift = __builtin_ctzll((unsigned long long)(zp.group / kChunk));
+    }
     auto load_w = [&](auto S, int64_t sl) {  // past the last slice: zeros
-        buf_load_words<B>(wbuf, (uint32_t)((sl * kSlice + lane) * B * 4), 0u, w[decltype(S)::value]);
+        const int64_t gc = sl * kSlice + lane;
+        const int64_t r = (kRW == 2 && gc >= nchunks) ? 1 : 0;
+        buf_load_words<B>(wbuf, (uint32_t)((r * row_words + (gc - r * nchunks) * B) * 4), 0u,
+                          w[decltype(S)::value]);
+        if constexpr (kGroup) {
+            uint32_t t[1];
+            buf_load_words<1>(sbuf, (uint32_t)(((sl * kSlice + lane) >> gshift) * 4), 0u, t);
+            gsc[decltype(S)::value] = t[0];
+        }
     };
     load_w(std::integral_constant<int, 0>{}, 0);
     load_w(std::integral_constant<int, 1>{}, 1);
@@ -830,14 +856,20 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     for (int r = 0; r < kR; ++r) *reinterpret_cast<uint4*>(xs_dyn + xdst[r]) = xv[r];
     __syncthreads();
 
-    float acc[MT];
+    float acc[MT], acc2[kRW == 2 ? MT : 1];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    if constexpr (kRW == 2) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc2[m] = 0.0f;
+    }
     auto step = [&](auto S, int64_t sl) {
         constexpr int st = decltype(S)::value;
         load_w(std::integral_constant<int, (st + 2) % 3>{}, sl + 2);
-        const int64_t c = sl * kSlice + lane;
-        if (c < nchunks) {
+        const int64_t gc = sl * kSlice + lane;
+        if (gc < tchunks) {
+            const int64_t r = (kRW == 2 && gc >= nchunks) ? 1 : 0;
+            const int64_t c = gc - r * nchunks;
             uint32_t xw[MT][16];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -851,10 +883,35 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
                     xw[m][4 * i + 3] = d.w;
                 }
             }
-            if constexpr (B <= 9)
+            if constexpr (kGroup) {  // the chunk's sum, scaled by its group's scale
+                float part[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) part[m] = 0.0f;
+                if constexpr (B <= 9)
+                    chunk_dot<B, MT>(w[st], xw, part);
+                else
+                    chunk_fma<B, MT>(w[st], xw, part);
+                const float sg = __uint_as_float(gsc[st]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = fmaf(part[m], sg, acc[m]);
+            } else if constexpr (kRW == 2) {  // the chunk's sum goes to its row
+                float part[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) part[m] = 0.0f;
+                if constexpr (B <= 9)
+                    chunk_dot<B, MT>(w[st], xw, part);
+                else
+                    chunk_fma<B, MT>(w[st], xw, part);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    acc[m] += r ? 0.0f : part[m];
+                    acc2[kRW == 2 ? m : 0] += r ? part[m] : 0.0f;
+                }
+            } else if constexpr (B <= 9) {
                 chunk_dot<B, MT>(w[st], xw, acc);
-            else
+            } else {
                 chunk_fma<B, MT>(w[st], xw, acc);
+            }
         }
     };
     int64_t sl = 0;
@@ -868,13 +925,27 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
 
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = wave_sum(acc[m]);
+    if constexpr (kRW == 2) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc2[m] = wave_sum(acc2[m]);
+    }
     if (lane == 0 && n < N) {
         constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
-        const float s = scales[n];
+        const float s = kGroup ? 1.0f : scales[n];
         const float zc = zp.template coef<B>(n);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             if (m < M) y[(int64_t)m * N + n] = s * zp.apply(acc[m] * kUnscale, zc, m);
+        if constexpr (kRW == 2) {
+            if (n + 1 < N) {
+                const float s2 = scales[n + 1];
+                const float zc2 = zp.template coef<B>(n + 1);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (m < M)
+                        y[(int64_t)m * N + n + 1] = s2 * zp.apply(acc2[m] * kUnscale, zc2, m);
+            }
+        }
     }
 }
 
@@ -885,7 +956,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
 template <int B, int MT, class ZP>
 hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed,
                             const float* scales, int64_t N, int64_t K, float* y, ZP zp,
-                hipStream_t stream)
+                            hipStream_t stream)
 {
     constexpr int kWaves = DQ_GEMV_XRES_WAVES;
     constexpr int kThreads = kWaves * kWave;
@@ -893,23 +964,43 @@ hipError_t launch_gemv_xres(const uint16_t* x, int64_t M, const uint32_t* packed
     const int64_t nchunks = K / kChunk;
     const size_t lds = (size_t)MT * nchunks * kXPitch * 2;
     const int64_t pieces = MT * nchunks * 4;
-    const dim3 grid((unsigned)ceil_div(N, kWaves)), block(kThreads);
-#define DQ_XRES(R) gemv_xres_kernel<B, MT, kWaves, R><<<grid, block, lds, stream>>>(x, (int)M, packed, scales, N, K, rw, y, zp)
+    const dim3 block(kThreads);
+    // two rows per wave when a row's chunks fill their last 64-chunk slice
+    // poorly and two rows' chunks fill theirs clearly better (per-row scales
+    // only).  Measured: 160 chunks per row (83 % -> 100 % full) gains 5-14 %,
+    // 544 chunks (94 % -> 100 %) loses 3 %, hence the 10-point margin.
+    auto fill = [](int64_t c) { return (double)c / (double)(ceil_div(c, kSlice) * kSlice); };
+    const bool two = std::is_same<ZP, NoZeroPoints>::value && fill(2 * nchunks) > fill(nchunks) + 0.1;
     // pieces per thread: every piece of x must be covered
     static_assert(10 * kThreads >= kXResMax / (kXPitch * 2) * 4, "x staging covers the largest x");
+#define DQ_XRES_RW(R, RW)                                                                         \
+    gemv_xres_kernel<B, MT, kWaves, R, ZP, RW>                                                    \
+        <<<dim3((unsigned)ceil_div(N, kWaves * RW)), block, lds, stream>>>(x, (int)M, packed,     \
+                                                                          scales, N, K, rw, y, zp)
+#define DQ_XRES(R)                                                                                \
+    do {                                                                                          \
+        if constexpr (std::is_same<ZP, NoZeroPoints>::value) {                                   \
+            if (two) {                                                                            \
+                DQ_XRES_RW(R, 2);                                                                 \
+                break;                                                                            \
+            }                                                                                     \
+        }                                                                                         \
+        DQ_XRES_RW(R, 1);                                                                         \
+    } while (0)
     if (pieces <= kThreads) DQ_XRES(1);
     else if (pieces <= 2 * kThreads) DQ_XRES(2);
     else if (pieces <= 3 * kThreads) DQ_XRES(3);
     else if (pieces <= 5 * kThreads) DQ_XRES(5);
     else DQ_XRES(10);
 #undef DQ_XRES
+#undef DQ_XRES_RW
     return hipGetLastError();
 }
 
 template <int B, int MT, class ZP>
 hipError_t launch_gemv_lds(const uint16_t* x, int64_t M, const uint32_t* packed,
                            const float* scales, int64_t N, int64_t K, float* y, ZP zp,
-                hipStream_t stream)
+                            hipStream_t stream)
 {
     constexpr int kRows = B <= 8 ? DQ_GEMV_ROWS_NARROW : DQ_GEMV_ROWS_WIDE;
     constexpr int kWaves = DQ_GEMV_WAVES;
@@ -946,9 +1037,11 @@ hipError_t launch_gemv_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
 // Group-wise scales ("量化" tutorial, exercise 1 of its exercises: one scale
 // per group of g = 32 gpc consecutive codes of a row, scales [N, G]): each
 // chunk's partial dot product is multiplied by its group's scale before it
-// joins the row's sum, so no scale is left for the epilogue.  Four waves, one
-// row per wave; lanes take chunks lane, lane + 64, ...; x is read straight
-// from global memory (at most 16 rows, cached).
+// joins the row's sum, so no scale is left for the epilogue.  M <= 2 with x
+// small enough for LDS takes the resident-x kernel above with a GroupScales
+// policy; otherwise this kernel: four waves, one row per wave; lanes take
+// chunks lane, lane + 64, ...; x read straight from global memory (at most 16
+// rows, cached).
 template <int B, int MT>
 __global__ __launch_bounds__(4 * kWave) void gemv_group_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
@@ -1013,6 +1106,13 @@ hipError_t launch_gemv_group_b(const uint16_t* x, int64_t M, const uint32_t* pac
                                const float* scales, int64_t N, int64_t K, int64_t group, float* y,
                                hipStream_t stream)
 {
+    // M <= 2 with x resident in LDS: the per-row kernel with a scale per chunk
+    if (M <= 2 && K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax &&
+        N * K <= (1LL << 27)) {
+        const GroupScales gs{scales, ceil_div(K, group), group};
+        if (M <= 1) return launch_gemv_xres<B, 1>(x, M, packed, scales, N, K, y, gs, stream);
+        return launch_gemv_xres<B, 2>(x, M, packed, scales, N, K, y, gs, stream);
+    }
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 4)), block(4 * kWave);
     const int gpc = (int)(group / kChunk);

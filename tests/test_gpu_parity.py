@@ -258,3 +258,16 @@ def test_random_shapes_whole_path():
         y_ref, bound = oracle.matmul(x, o_packed, o_scales, N, K, bits)
         ok = within_tolerance(y.cpu().numpy(), y_ref, bound)
         assert ok.all(), "case %d: %d outputs out of tolerance" % (case, int((~ok).sum()))
+
+
+# K whose chunk count fills the last 64-chunk slice of a row poorly (160 and
+# 65 chunks): the resident-x GEMV then takes two rows per wave; odd N leaves
+# the last wave a single row (544 chunks stays at one row per wave)
+TWO_ROW_SHAPES = [(37, 5120), (300, 5120), (1, 5120), (9, 17408), (33, 2080), (2, 2080)]
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemv_two_rows_per_wave(bits):
+    for M in (1, 2):
+        for i, (N, K) in enumerate(TWO_ROW_SHAPES):
+            assert_matmul_parity("gemv", M, N, K, bits, seed=bits * 2000 + M * 10 + i)
