@@ -382,7 +382,7 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     launches of a step against a plain streaming read (dq_stream_read) of the
     same packed buffers in the same order, each group timed after the same
     cache-flushing GEMM; plus the read rate of a 1 GiB buffer.  The read's
-    share count is the best of three."""
+    share count is the best of four."""
     nbytes = sum(b.numel() * b.element_size() for b in read_bufs)
     n = len(read_bufs)
 
@@ -399,7 +399,7 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
         return float(np.median(ts))
 
     parts = {}
-    for per in (256, 512, 1024):
+    for per in (256, 512, 1024, 2048):
         outs = [torch.empty((max(1, min(65536, b.numel() * b.element_size() // 16 // per)),),
                             dtype=torch.int32, device=dev) for b in read_bufs]
         lib = dq.load()
