@@ -14,7 +14,12 @@
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile of y; the K loop
 // stages a 128 x 64 slice of x and the matching 128 x 64 slice of expanded
 // codes in LDS (k contiguous for both), and each wave issues
-// v_mfma_f32_16x16x32_bf16 over its 64 x 64 sub-tile.
+// v_mfma_f32_16x16x32_bf16 over its 64 x 64 sub-tile.  That is the simple
+// fallback (K not a multiple of 64); the main kernels below pipeline the
+// codes through registers and x through LDS.  Variants: asymmetric codes add
+// a zero-point term in the epilogues (ZeroPoints / TileZeroPoints policies);
+// group-wise scales fold each group's sum in as it ends (GroupScales in the
+// 128-row kernel; gemm_group_kernel for groups of 32 codes).
 #include <type_traits>
 
 #include "common.hpp"

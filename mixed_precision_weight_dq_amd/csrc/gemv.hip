@@ -6,9 +6,10 @@
 // bound by the bytes of the packed weights (decode is memory-bound, as the
 // Quantization tutorial's closing remark on prefill vs decode puts it).
 //
-// Three kernels by M (the row scale always multiplies the reduced sum once):
+// Kernels by M (the row scale always multiplies the reduced sum once):
 //   * M <= 2 (gemv_xres_kernel when K is a multiple of 32 and x fits in LDS
-//     whole, else gemv_lds_kernel): a wave owns a row; lane l walks the chunks
+//     whole, else gemv_lds_kernel): a wave owns a row (or two, when a row's
+//     chunks fill their last slice poorly); lane l walks the chunks
 //     l, l+64, ... of it (a chunk = 32 codes = B whole words, so a wave's
 //     loads of one row cover 64*B contiguous words); x sits in LDS; codes
 //     become signed integers with one XOR per word plus a signed bit-field
@@ -17,6 +18,11 @@
 //     and x copied through LDS; else gemv_mfma_kernel): codes expanded to
 //     exact bf16 operands of v_mfma_f32_16x16x32_bf16, so the VALU cost per
 //     code no longer grows with M.
+// The product kernels take a policy type for the variants: NoZeroPoints (the
+// scheme above), ZeroPoints (asymmetric codes: a zero-point term in the
+// epilogue) and, in the resident-x kernel, GroupScales (a scale per group of
+// codes, applied per chunk).  gemv_group_kernel serves group-wise scales for
+// the other shapes.
 #include <type_traits>
 
 #include "common.hpp"
