@@ -157,4 +157,13 @@ __device__ __forceinline__ void buf_load_lds16(BufRef buf, void* lds, uint32_t v
                                              soff, 0, 0);
 }
 
+// 4 bytes per lane from byte offset voff + soff of a buffer straight into LDS
+// at lds + 4 * lane (buffer_load_dword ... lds).
+__device__ __forceinline__ void buf_load_lds4(BufRef buf, void* lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(buf.base, buf.bytes),
+                                             (__attribute__((address_space(3))) void*)lds, 4, voff,
+                                             soff, 0, 0);
+}
+
 }  // namespace dq

@@ -573,7 +573,10 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     constexpr int kXCopies = kMR / 4;
     constexpr int kCodeSlots = (16 * kNT * B + 63) / 64 * 64;  // 16-byte code pieces of one step
     constexpr int kCodeCopies = kCodeSlots / 64;
-    constexpr int kPerStage = kCodeCopies + kXCopies;
+    // group-wise scales (groups of whole 128-code steps): each step's scales of
+    // the tile's rows come into LDS with the step's codes, one more copy
+    constexpr bool kGroup = is_group_scales<ZP>::value;
+    constexpr int kPerStage = kCodeCopies + kXCopies + (kGroup ? 1 : 0);
     constexpr int kSlots = kMR * 16;  // 16-byte x pieces of one step
     static_assert(kDepth >= 1 && kDepth <= 2, "one or two steps ahead");
     static_assert(kMR == 8 || kMR == 16, "x rows staged: 8 or 16");
@@ -587,6 +590,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     __shared__ __attribute__((aligned(16))) uint4 cs0[kGemvMfmaWaves][kCodeSlots];
     __shared__ __attribute__((aligned(16))) uint4 cs1[kGemvMfmaWaves][kCodeSlots];
     __shared__ __attribute__((aligned(16))) uint4 cs2[kStages > 2 ? kGemvMfmaWaves : 1][kStages > 2 ? kCodeSlots : 1];
+    __shared__ float ss[kGroup ? kStages : 1][kGroup ? kGemvMfmaWaves : 1][kGroup ? kWave : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -642,7 +646,19 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
         const int r = sl / B, pc = sl % B;
         cbase[q] = r < 16 * kNT ? (uint32_t)(r * row_words * 4 + pc * 16) : kOutside;
     }
+    [[maybe_unused]] BufRef sb{};
+    [[maybe_unused]] int64_t steps_per_group = 1;
+    if constexpr (kGroup) {
+        sb = uniform_buf(zp.scales + n0 * zp.G, (uint32_t)(nrows * zp.G * 4));
+        steps_per_group = zp.group / 128;
+    }
     auto load = [&](auto P, int64_t ks) {
+        if constexpr (kGroup) {  // lane r < 16 kNT: the scale of row r for step ks's group
+            const int64_t gi = ks / steps_per_group;
+            const bool in = lane < 16 * kNT && lane < nrows && gi < zp.G;
+            buf_load_lds4(sb, &ss[kGroup ? decltype(P)::value : 0][kGroup ? wave : 0][0],
+                          in ? (uint32_t)((lane * zp.G + gi) * 4) : kOutside, 0u);
+        }
         uint4* cdst = cring(P);
 #pragma unroll
         for (int q = 0; q < kCodeCopies; ++q)
@@ -669,6 +685,9 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int i = 0; i < B; ++i) wl[j][i] = cw[(16 * j + c) * 4 * B + g * B + i];
+        f32x4m_t part[kNT];  // group-wise scales: this step's sums, scaled below
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) part[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const bf16x8m_t a = __builtin_bit_cast(bf16x8m_t, src[aslot[t]]);
@@ -676,8 +695,17 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
             for (int j = 0; j < kNT; ++j) {
                 bf16x8_t bh, bl;
                 expand8<B>(wl[j], t, bh, bl);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
-                if constexpr (kSplit) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
+                f32x4m_t& d = kGroup ? part[j] : acc[j];
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, d, 0, 0, 0);
+                if constexpr (kSplit) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, d, 0, 0, 0);
+            }
+        }
+        if constexpr (kGroup) {
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                const float sg = ss[kGroup ? decltype(P)::value : 0][kGroup ? wave : 0][16 * j + c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sg, part[j][r], acc[j][r]);
             }
         }
     };
@@ -726,7 +754,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + 16 * j + c;
             if (n >= N) continue;
-            const float s = scales[n];
+            const float s = kGroup ? 1.0f : scales[n];
             const float zc = zp.template coef<B>(n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -757,7 +785,7 @@ hipError_t launch_gemv_mfma_nt(const uint16_t* x, int64_t M, const uint32_t* pac
     else if (K % kChunk == 0)  // twice the x per stage: one step ahead, so two workgroups fit per CU
         gemv_mfma_xlds_kernel<B, kNT, 1, 16><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y, zp);
-    else
+    else if constexpr (!is_group_scales<ZP>::value)  // group scales come here with K % 32 == 0 only
         gemv_mfma_kernel<B, kNT, DQ_GEMV_MFMA_DEPTH><<<grid, block, 0, stream>>>(
             x, (int)M, packed, scales, N, K, rw, y, zp);
     return hipGetLastError();
@@ -1119,6 +1147,11 @@ hipError_t launch_gemv_group_b(const uint16_t* x, int64_t M, const uint32_t* pac
         if (M <= 1) return launch_gemv_xres<B, 1>(x, M, packed, scales, N, K, y, gs, stream);
         return launch_gemv_xres<B, 2>(x, M, packed, scales, N, K, y, gs, stream);
     }
+    // 3 <= M <= 16, groups of whole 128-code steps: the matrix-core kernel,
+    // each step's sums scaled by the step's group scales
+    if (M >= 3 && K % kChunk == 0 && group % 128 == 0)
+        return launch_gemv_mfma<B>(x, M, packed, scales, N, K, y,
+                                   GroupScales{scales, ceil_div(K, group), group}, stream);
     const int64_t rw = packed_row_words(K, B);
     const dim3 grid((unsigned)ceil_div(N, 4)), block(4 * kWave);
     const int gpc = (int)(group / kChunk);

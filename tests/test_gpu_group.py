@@ -94,6 +94,15 @@ def test_gemv_group_parity(bits):
                 assert_group_product("gemv", M, N, K, bits, g, bits * 1000 + M * 10 + i + g)
 
 
+@pytest.mark.parametrize("bits", [2, 4, 7, 9, 10, 13, 15])
+def test_gemv_group_matrix_core_tiles(bits):
+    """3 <= M <= 16 with groups of whole 128-code steps: the matrix-core GEMV
+    with 32-row tiles (N * K > 2^24), a ragged last tile, a last step of half
+    its codes, and groups of one, two and four steps."""
+    for M, N, K, g in ((3, 4100, 4224, 128), (9, 4100, 4160, 256), (16, 4100, 4160, 512)):
+        assert_group_product("gemv", M, N, K, bits, g, bits * 100 + M)
+
+
 @pytest.mark.parametrize("bits", range(2, 16))
 def test_gemm_group_parity(bits):
     for g in (32, 64, 128, 2048):
@@ -107,17 +116,17 @@ def test_gemm_group_parity(bits):
 def test_group_one_hot_is_exact(kind, bits):
     """x = e_k: the group's partial sum is q[n, k] exactly and it is scaled
     once, so y[k, n] = fl32(q[n, k] * s[n, k / g])."""
-    N, K, g = 70, 96, 32
-    w = group_weights(bits + 77, N, K, g)
-    w[2] = w[0]
-    o_packed, o_scales, _ = oracle.quantize_pack_group(w, bits, g)
-    _, w_hat = oracle.unpack_group(o_packed, o_scales, N, K, bits, g)
-    eye = workload.bf16_from_f32(np.eye(K, dtype=np.float32))
-    P = torch().from_numpy(o_packed.view(np.int32)).cuda()
-    S = torch().from_numpy(o_scales).cuda()
-    fn = dq.gemv_group if kind == "gemv" else dq.gemm_group
-    report("%s_group one-hot b=%d" % (kind, bits))
-    for k0 in range(0, K, 16):
-        y = fn(bf16_gpu(eye[k0:k0 + 16]), P, S, K, bits, g)
-        torch().cuda.synchronize()
-        assert np.array_equal(f32_bits(y), w_hat.T[k0:k0 + 16].copy().view(np.uint32))
+    for N, K, g in ((70, 96, 32), (70, 384, 128)):  # g = 128: the matrix-core GEMV
+        w = group_weights(bits + 77, N, K, g)
+        w[2] = w[0]
+        o_packed, o_scales, _ = oracle.quantize_pack_group(w, bits, g)
+        _, w_hat = oracle.unpack_group(o_packed, o_scales, N, K, bits, g)
+        eye = workload.bf16_from_f32(np.eye(K, dtype=np.float32))
+        P = torch().from_numpy(o_packed.view(np.int32)).cuda()
+        S = torch().from_numpy(o_scales).cuda()
+        fn = dq.gemv_group if kind == "gemv" else dq.gemm_group
+        report("%s_group one-hot b=%d g=%d" % (kind, bits, g))
+        for k0 in range(0, K, 16):
+            y = fn(bf16_gpu(eye[k0:k0 + 16]), P, S, K, bits, g)
+            torch().cuda.synchronize()
+            assert np.array_equal(f32_bits(y), w_hat.T[k0:k0 + 16].copy().view(np.uint32))
