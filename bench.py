@@ -459,6 +459,16 @@ def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
         el = time.perf_counter() - t0
         if el >= target_s:
             break
+    # one host thread, one pass over the b = 6 decode matrix
+    cores = oracle.max_threads()
+    b6p = next((p, s) for b, p, s in packs if b == 6)
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.matmul(x1, b6p[0], b6p[1], DECODE["N"], DECODE["K"], 6)
+        one_thread = DECODE["N"] * DECODE["K"] * 6 / 8 / (time.perf_counter() - t1) / 1e9
+    finally:
+        oracle.set_threads(cores)
     # the oracle's asymmetric and group-wise products on one decode matrix
     # (b = 6), beside the GPU figures of the same variants
     variants = {}
@@ -479,8 +489,8 @@ def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "one_thread_b6_gbs": round(one_thread, 4),
             "sample": "fp64 GEMV M=1 over the five 4096x4096 decode matrices (b=4..8), "
                       "%d passes, %.1f s" % (reps, el),
             "cpu": cpu, "allocation_oracle": alloc, "variants_oracle": variants}

@@ -20,9 +20,10 @@
 //     code no longer grows with M.
 // The product kernels take a policy type for the variants: NoZeroPoints (the
 // scheme above), ZeroPoints (asymmetric codes: a zero-point term in the
-// epilogue) and, in the resident-x kernel, GroupScales (a scale per group of
-// codes, applied per chunk).  gemv_group_kernel serves group-wise scales for
-// the other shapes.
+// epilogue) and GroupScales (a scale per group of codes): the resident-x
+// kernel applies it per chunk; gemv_mfma_xlds_kernel, for groups of whole
+// 128-code steps, scales each step's MFMA sums before adding them in.
+// gemv_group_kernel serves group-wise scales for the other shapes.
 #include <type_traits>
 
 #include "common.hpp"

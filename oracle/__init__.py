@@ -89,11 +89,17 @@ class Oracle:
         lib.oracle_matmul_group.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         self.lib = lib
         self.path = path
 
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Thread count of the OpenMP loops from now on (for timing)."""
+        self.lib.oracle_set_threads(int(n))
 
     def row_bytes(self, K: int, bits: int) -> int:
         """Bytes of one packed row: ceil(K*bits/8) rounded up to a multiple of 128."""
@@ -277,6 +283,10 @@ def default() -> Oracle:
 
 def max_threads() -> int:
     return default().max_threads()
+
+
+def set_threads(n: int) -> None:
+    default().set_threads(n)
 
 
 def row_bytes(K: int, bits: int) -> int:

@@ -542,3 +542,13 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops that follow (n < 1 means 1); timing only. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
