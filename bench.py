@@ -257,6 +257,18 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
     calls = [(lib.dq_gemv_group, (X.data_ptr(), 1, P.data_ptr(), S.data_ptr(), Nd, Kd, b, group,
                                   ys[b].data_ptr(), cs))
              for t, X in enumerate(X1t) for b, (P, S) in copies[t].items()]
+    # M = 16 (the token activations stacked twice): group-wise scales in the
+    # matrix-core GEMV, and the per-row scheme on the same matrices beside it
+    X16 = torch.cat([X1t[i % len(X1t)] for i in range(16)], 0).contiguous()
+    y16 = torch.empty((16, Nd), dtype=torch.float32, device=X16.device)
+    sym = {b: dq.quantize_pack(W, b) for b, W in W2.items()}
+    sym_copies = [sym] + [{b: (P.clone(), S) for b, (P, S) in sym.items()} for _ in range(len(X1t) - 1)]
+    calls16 = [(lib.dq_gemv_group, (X16.data_ptr(), 16, P.data_ptr(), S.data_ptr(), Nd, Kd, b, group,
+                                    y16.data_ptr(), cs))
+               for t in range(len(X1t)) for b, (P, S) in copies[t].items()]
+    calls16_sym = [(lib.dq_gemv, (X16.data_ptr(), 16, P.data_ptr(), S.data_ptr(), Nd, Kd, b,
+                                  y16.data_ptr(), cs))
+                   for t in range(len(X1t)) for b, (P, S) in sym_copies[t].items()]
 
     def timed(fn):
         fn()
@@ -279,6 +291,14 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
         for fn, a in calls:
             fn(*a)
 
+    def decode16():
+        for fn, a in calls16:
+            fn(*a)
+
+    def decode16_sym():
+        for fn, a in calls16_sym:
+            fn(*a)
+
     P6, S6 = dq.quantize_pack_group(W4[6], 6, group)
     Y = torch.empty((X4.shape[0], P6.shape[0]), dtype=torch.float32, device=X4.device)
 
@@ -286,8 +306,10 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
         dq.gemm_group(X4, P6, S6, X4.shape[1], 6, group, Y)
 
     t_q, t_d, t_g = timed(quant), timed(decode), timed(gemm)
+    t_16, t_16s = timed(decode16), timed(decode16_sym)
     G = -(-Kd // group)
     dec_bytes = len(X1t) * sum(Nd * (Kd * b // 8 + G * 4) for b in W2)
+    payload = len(X1t) * sum(Nd * Kd * b // 8 for b in W2)
     q_bytes = sum(Nd * (Kd * (16 + b) // 8 + G * 4) for b in W2)
     M, K = X4.shape
     N = P6.shape[0]
@@ -295,10 +317,13 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
             "quantize_pack_4096_gbs": round(q_bytes / (t_q * 1e-3) / 1e9, 1),
             "gemv_m1_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
             "gemv_m1_per_launch_us": round(t_d / len(calls) * 1e3, 3),
+            "gemv_m16_packed_gbs": round(payload / (t_16 * 1e-3) / 1e9, 1),
+            "gemv_m16_per_row_scales_packed_gbs": round(payload / (t_16s * 1e-3) / 1e9, 1),
             "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
             "what": "group-wise scales (g=128) on the step's inputs: quantize+pack (read + write "
                     "bytes), decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed "
-                    "words + group scales per second), prefill GEMM M=2048 b=6 (pipelined 128-row tiles, each group folded in as it ends); "
+                    "words + group scales per second), the same at M=16 (packed words per second; "
+                    "beside it the per-row scheme on the same matrices), prefill GEMM M=2048 b=6 (pipelined 128-row tiles, each group folded in as it ends); "
                     "median of the step count, outside the timed steps"}
 
 
