@@ -123,6 +123,16 @@ def test_gemm_asym_parity(bits):
         assert_asym_product("gemm", M, N, K, bits, seed=bits * 1000 + 500 + i)
 
 
+@pytest.mark.parametrize("bits", [3, 9, 15])
+def test_asym_largest_k(bits):
+    """K at the library's maximum (2^22): bit-exact quantize + pack, GEMV at
+    M = 1 and M = 5, GEMM, every output."""
+    N, K = 3, 1 << 22
+    assert_quantize_asym(shifted_weights(bits + 4000, N, K), bits)
+    for kind, M in (("gemv", 1), ("gemv", 5), ("gemm", 2)):
+        assert_asym_product(kind, M, N, K, bits, seed=bits * 10 + M + 4000)
+
+
 @pytest.mark.parametrize("bits", [2, 6, 9, 12])
 def test_gemm_asym_wide_tiles(bits):
     """Shapes that take the 256 x 256 and the 256 x 128 wide kernels."""

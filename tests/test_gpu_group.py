@@ -103,6 +103,24 @@ def test_gemv_group_matrix_core_tiles(bits):
         assert_group_product("gemv", M, N, K, bits, g, bits * 100 + M)
 
 
+@pytest.mark.parametrize("bits", [3, 9, 15])
+def test_group_largest_k(bits):
+    """K at the library's maximum (2^22) with the largest and a mid group size:
+    bit-exact quantize + pack, GEMV at M = 1 (VALU kernel, x too large for LDS)
+    and M = 5 (matrix-core kernel with the per-step fold), GEMM, every output."""
+    N, K = 3, 1 << 22
+    for g in (2048, 256):
+        w = group_weights(bits + g, N, K, g)
+        report("quantize_pack_group largest K g=%d b=%d" % (g, bits))
+        P, S = dq.quantize_pack_group(weights_gpu(w), bits, g)
+        torch().cuda.synchronize()
+        o_packed, o_scales, _ = oracle.quantize_pack_group(w, bits, g)
+        assert np.array_equal(f32_bits(S), o_scales.view(np.uint32))
+        assert np.array_equal(u32(P), o_packed)
+        for kind, M in (("gemv", 1), ("gemv", 5), ("gemm", 2)):
+            assert_group_product(kind, M, N, K, bits, g, bits * 10 + M + g)
+
+
 @pytest.mark.parametrize("bits", range(2, 16))
 def test_gemm_group_parity(bits):
     for g in (32, 64, 128, 2048):
