@@ -529,6 +529,21 @@ def device_info(torch, dev) -> dict:
     arch = getattr(p, "gcnArchName", None)
     if arch:
         info["arch"] = arch
+    # peak engine clock as the runtime reports it (hipDeviceAttributeClockRate,
+    # enum value 5, in kHz; looked up through the library's handle, so it is the
+    # HIP runtime the library runs on), and the dense bf16 matrix peak scaled to
+    # it from 2.5 PFLOP/s at 2.4 GHz on 256 CUs
+    try:
+        import ctypes
+        import mixed_precision_weight_dq_amd as dq
+        khz = ctypes.c_int(0)
+        if dq.load().hipDeviceGetAttribute(ctypes.byref(khz), 5, ctypes.c_int(dev.index or 0)) == 0 \
+                and khz.value > 0:
+            info["peak_clock_mhz"] = round(khz.value / 1e3)
+            info["bf16_peak_at_that_clock_tflops"] = round(
+                MFMA_BF16_PEAK_TFLOPS * khz.value / 2.4e6 * p.multi_processor_count / 256, 1)
+    except (OSError, AttributeError):
+        pass
     return info
 
 
