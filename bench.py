@@ -842,6 +842,26 @@ def main():
         lambda: [launch(fn, a) for fn, a in decode_calls],
         [pt for _, pt, _, _, _ in decode],
         lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
+    # cache-hot figure, labelled as such: the same 40 launches with every token
+    # reading copy 0 (63 MB, inside the 256 MB last-level cache after the first token)
+    hot_calls = [(fn, (a[0], a[1], P2t[0][a[6]].data_ptr()) + a[3:])
+                 for fn, a in decode_calls]
+    hot_ms = []
+    for _ in range(max(5, args.steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for fn, a in hot_calls:
+            launch(fn, a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hot_ms.append(e0.elapsed_time(e1))
+    hot = float(np.median(hot_ms))
+    out["roofline"]["cache_hot"] = {
+        "gbs": round(gemv_bytes / (hot * 1e-3) / 1e9, 1),
+        "per_launch_us": round(hot / len(hot_calls) * 1e3, 3),
+        "what": "cache-hot: the 40 decode launches all on copy 0 of the five packed matrices "
+                "(63 MB, re-read from the last-level cache), median of the step count; "
+                "context, not the value"}
     out["allocation"] = {"row_sumsq": row_sumsq_context(torch, dq, stream, list(W4.values()),
                                                         reps=max(5, args.steps))}
     out["asymmetric"] = asym_context(torch, dq, stream, W2, X1t, W4, X4, reps=max(5, args.steps))
