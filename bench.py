@@ -438,6 +438,9 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     dq.stream_read(big, 65536, big_out)
     torch.cuda.synchronize()
     big_ms = timed(lambda: dq.stream_read(big, 65536, big_out))
+    # launch floor: n back-to-back reads of 16 KB (1024 workgroups) from the same buffer
+    tiny = (lib.dq_stream_read, (big.data_ptr(), 16384, big_out.data_ptr(), 1024, stream.cuda_stream))
+    floor_ms = timed(lambda: [tiny[0](*tiny[1]) for _ in range(n)])
     del big
     read_gbs = nbytes / (read_ms * 1e-3) / 1e9
     gemv_gbs = nbytes / (gemv_ms * 1e-3) / 1e9
@@ -453,6 +456,9 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
         "gemv_per_launch_us": round(gemv_ms / n * 1e3, 3),
         "gemv_frac_of_read": round(gemv_gbs / read_gbs, 4),
         "read_1gib_gbs": round((1 << 30) / (big_ms * 1e-3) / 1e9, 1),
+        "launch_floor_us": round(floor_ms / n * 1e3, 3),
+        "launch_floor_what": "per-launch time of %d back-to-back 16 KB plain reads: no kernel "
+                             "launched once per matrix finishes faster here" % n,
     }
 
 
