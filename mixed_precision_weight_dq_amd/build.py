@@ -36,13 +36,23 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source in csrc/ and link libdq.so; returns its path."""
+def headers():
+    return [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + \
+        [os.path.join(ROOT, "include", "dq.h")]
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source in csrc/ and link libdq.so; returns its path.
+    incremental=True reuses an object newer than its source and every header."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
+    newest_header = max(os.path.getmtime(h) for h in headers())
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src + ".o")
+        if incremental and os.path.exists(obj) and os.path.getmtime(obj) > max(
+                newest_header, os.path.getmtime(os.path.join(CSRC, src))):
+            return obj
         cmd = [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd = [cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -67,4 +77,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, incremental="-i" in sys.argv[1:]))

@@ -1,7 +1,8 @@
 // C ABI of the library (declared in include/dq.h): argument validation on the
 // host, then the kernel launches on the caller's stream.  No allocation, no
 // synchronisation, no state beyond the per-thread text of the last HIP error.
-// (The host-only allocation entry points live in recipe.cpp.)
+// (The host-only allocation entry points live in recipe.cpp, the file format's
+// writer and parser in packfile.cpp.)
 #include "../../include/dq.h"
 
 #include <hip/hip_runtime.h>
@@ -243,6 +244,26 @@ dq_status dq_gemm_asym(const uint16_t* x, int64_t M, const uint32_t* packed, con
         return DQ_ERR_ALIGN;
     return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, zeros, xsum,
                                       static_cast<hipStream_t>(stream)));
+}
+
+dq_status dq_file_load(const dq_file* f, int64_t i, void* data, float* scales, void* stream)
+{
+    if (!f || !data) return DQ_ERR_NULL;
+    dq_file_matrix m;
+    const dq_status st = dq_file_matrix_info(f, i, &m);
+    if (st != DQ_OK) return st;
+    if (m.scales && !scales) return DQ_ERR_NULL;
+    if (!aligned(data, 16) || !aligned(scales, 4)) return DQ_ERR_ALIGN;
+    // region sizes follow from the entry's shape, which dq_file_open checked
+    // against the file's extent
+    const uint64_t db = m.bits == DQ_TOP_BITS
+                            ? (uint64_t)m.N * (uint64_t)m.K * 2
+                            : (uint64_t)m.N * (uint64_t)dq::packed_row_words(m.K, m.bits) * 4;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = hipMemcpyAsync(data, m.data, db, hipMemcpyHostToDevice, s);
+    if (err == hipSuccess && m.scales)
+        err = hipMemcpyAsync(scales, m.scales, (uint64_t)m.N * 4, hipMemcpyHostToDevice, s);
+    return hip_status(err);
 }
 
 dq_status dq_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,

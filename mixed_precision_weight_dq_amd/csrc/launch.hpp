@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.hpp"
+
 namespace dq {
 
 hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
@@ -47,11 +49,6 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial,
 // DQ_OK for hipSuccess; otherwise keeps the HIP message for dq_last_error on
 // this thread and returns DQ_ERR_HIP (defined with the C ABI in api.cpp).
 int32_t record_hip_error(hipError_t e);
-
-inline int64_t packed_row_words(int64_t K, int bits)
-{
-    return ((K * bits + 7) / 8 + 127) / 128 * 128 / 4;
-}
 
 // Expands CALL(B) for the run-time bit width, one template instance per width.
 #define DQ_BITS_SWITCH(bits, CALL)                                                                \

@@ -18,9 +18,9 @@
 //   checksum    64-bit FNV-1a over the data bytes then the scale bytes:
 //               h = 0xcbf29ce484222325; for each byte: h = (h ^ byte) * 0x100000001b3
 //               (mod 2^64).
+// This file is host-only C++ (no HIP): the copy of an entry to the device,
+// dq_file_load, sits with the other HIP entry points in api.cpp.
 #include "../../include/dq.h"
-
-#include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstring>
@@ -31,7 +31,7 @@
 #include <sys/stat.h>
 #include <unistd.h>
 
-#include "launch.hpp"
+#include "layout.hpp"
 
 namespace {
 
@@ -235,11 +235,14 @@ dq_status dq_file_open(const char* path, dq_file** out)
              region_bytes(N, K, bits, &db, &sb);
         if (!ok) break;
         const uint64_t doff = get_u64(e + 88), soff = get_u64(e + 104);
-        ok = get_u64(e + 96) == db && doff % kAlign == 0 && doff >= prev_end && doff + db <= size;
-        prev_end = doff + db;
+        // offsets are untrusted: compare without forming doff + db (which
+        // could wrap past 2^64 and pass)
+        ok = get_u64(e + 96) == db && doff % kAlign == 0 && doff >= prev_end && doff <= size &&
+             db <= size - doff;
+        prev_end = ok ? doff + db : prev_end;
         if (ok && sb > 0) {
-            ok = soff % kAlign == 0 && soff >= prev_end && soff + sb <= size;
-            prev_end = soff + sb;
+            ok = soff % kAlign == 0 && soff >= prev_end && soff <= size && sb <= size - soff;
+            prev_end = ok ? soff + sb : prev_end;
         } else if (ok) {
             ok = soff == 0;
         }
@@ -288,23 +291,6 @@ dq_status dq_file_verify(const dq_file* f, int64_t i)
     const uint64_t soff = get_u64(e + 104);
     if (soff) h.bytes(f->base + soff, get_u64(e + 64) * 4);
     return h.done() == get_u64(e + 112) ? DQ_OK : DQ_ERR_FORMAT;
-}
-
-dq_status dq_file_load(const dq_file* f, int64_t i, void* data, float* scales, void* stream)
-{
-    if (!f || !data) return DQ_ERR_NULL;
-    if (i < 0 || i >= f->count) return DQ_ERR_SHAPE;
-    const unsigned char* e = f->base + kHeaderBytes + kEntryBytes * (uint64_t)i;
-    const uint64_t soff = get_u64(e + 104);
-    if (soff && !scales) return DQ_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(data) & 15) || (reinterpret_cast<uintptr_t>(scales) & 3))
-        return DQ_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = hipMemcpyAsync(data, f->base + get_u64(e + 88), get_u64(e + 96),
-                                    hipMemcpyHostToDevice, s);
-    if (err == hipSuccess && soff)
-        err = hipMemcpyAsync(scales, f->base + soff, get_u64(e + 64) * 4, hipMemcpyHostToDevice, s);
-    return dq::record_hip_error(err);
 }
 
 void dq_file_close(dq_file* f)

@@ -152,6 +152,12 @@ def test_corruption_and_bad_files_refused(tmp_path):
         "misaligned": (64 + 88, struct.pack("<Q", doff + 8)),
         "overlap": (64 + 128 + 88, struct.pack("<Q", doff)),
         "name_no_nul": (64, b"n" * 64),
+        # offsets near 2^64: offset + size wraps to a small number, which a
+        # check that adds them would let through
+        "data_offset_wraps": (64 + 88, struct.pack("<Q", 2 ** 64 - 4096)),
+        "scale_offset_wraps": (64 + 104, struct.pack("<Q", 2 ** 64 - 4096)),
+        "last_data_offset_wraps": (64 + 128 * (len(mats) - 1) + 88,
+                                   struct.pack("<Q", 2 ** 64 - 4096)),
     }
     for what, (off, patch) in cases.items():
         blob = bytearray(good)
