@@ -82,6 +82,70 @@ def check_nonpositive_rows(orc) -> list[str]:
     return bad
 
 
+def f32_nearest(q: Fraction) -> float:
+    """The fp32 value nearest to the rational q, ties to the even significand
+    (IEEE round to nearest; subnormals kept, overflow to infinity), computed
+    with exact integers only."""
+    if q == 0:
+        return 0.0
+    sign, a = (-1.0 if q < 0 else 1.0), abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)  # 24 significant bits, or the subnormal step
+    m = a / ulp
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * ulp
+    if v >= Fraction(2) ** 128 - Fraction(2) ** 103:
+        return sign * float("inf")
+    return sign * float(v)  # exact: v has at most 24 significant bits
+
+
+def rint_even(q: Fraction) -> int:
+    n = q.numerator // q.denominator
+    r = q - n
+    return n + 1 if (r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1)) else n
+
+
+def check_mixed_sign_scale(orc) -> list[str]:
+    """Rows with both signs (reading of "量化怎么工作" taken by the oracle: the
+    range [lo, hi] is widened to hold 0, s = fl32(fl32(hi - lo) / L) with both
+    operations rounded in fp32, z = clip(rint(fl32(-lo / s)), 0, L)).  The
+    expected s and z come from exact rationals rounded by f32_nearest, so a
+    range formed in fp64, a divide split as hi/L - lo/L, or a zero point from
+    an unrounded quotient disagree on some rows.  Invariants: the smallest
+    element gets code 0 (rint(lo/s) + rint(-lo/s) = 0, rint being odd), the
+    largest code L - 1 or L."""
+    bad = []
+    rng = np.random.default_rng(23)
+    for bits in range(2, 16):
+        L = (1 << bits) - 1
+        # mixed-sign rows of varied skew and magnitude: N(mu, 1) * 2^e
+        mu = rng.uniform(-1.5, 1.5, 40)
+        ex = rng.integers(-20, 20, 40).astype(np.float64)
+        w = ((rng.standard_normal((40, 33)) + mu[:, None]) * 2.0 ** ex[:, None]).astype(np.float32)
+        w[:, 0] = -np.abs(w[:, 0]) - np.float32(2.0 ** ex[0] * 1e-3)  # a negative element
+        w[:, 1] = np.abs(w[:, 1]) + np.float32(2.0 ** ex[0] * 1e-3)   # and a positive one
+        _, s, z, u = orc.quantize_pack_asym(w, bits)
+        for n in range(40):
+            lo, hi = Fraction(float(w[n].min())), Fraction(float(w[n].max()))
+            want_s = f32_nearest(Fraction(f32_nearest(hi - lo)) / L)
+            if np.float32(s[n]).view(np.uint32) != np.float32(want_s).view(np.uint32):
+                bad.append("b=%d mixed row %d: scale %r, want %r" % (bits, n, s[n], want_s))
+                continue
+            want_z = min(max(rint_even(Fraction(f32_nearest(-lo / Fraction(want_s)))), 0), L)
+            if z[n] != want_z:
+                bad.append("b=%d mixed row %d: zero point %d, want %d" % (bits, n, z[n], want_z))
+            if u[n, int(np.argmin(w[n]))] != 0 or u[n, int(np.argmax(w[n]))] < L - 1:
+                bad.append("b=%d mixed row %d: extreme codes" % (bits, n))
+    return bad
+
+
 def check_error_bound(orc) -> list[str]:
     """|w - (u - z) s| <= s (1 + 2^-20): half a step from rounding w / s and half
     a step from rounding the zero point, plus the fp32 roundings."""
@@ -151,8 +215,8 @@ def check_unpack_and_matmul(orc) -> list[str]:
     return bad
 
 
-CHECKS = [check_nonnegative_rows, check_nonpositive_rows, check_error_bound, check_special_rows,
-          check_unpack_and_matmul]
+CHECKS = [check_nonnegative_rows, check_nonpositive_rows, check_mixed_sign_scale,
+          check_error_bound, check_special_rows, check_unpack_and_matmul]
 
 
 def run_all(orc) -> list[str]:
@@ -171,6 +235,10 @@ MUTANTS = [
     ("levels_minus_one", "const int32_t L = (1 << bits) - 1;", "const int32_t L = (1 << bits) - 2;"),
     ("range_without_zero", "float lo = 0.0f, hi = 0.0f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;",
      "float lo = 1e30f, hi = -1e30f;\n    int nonfinite = 0;\n    for (int64_t k = 0; k < K; k++) {\n        float v = load_weight(w, dtype, row * K + k);\n        if (!isfinite(v))\n            nonfinite = 1;"),
+    ("range_in_fp64", "float s = (range == 0.0f ? 1.0f : range) / (float)L;",
+     "float s = range == 0.0f ? 1.0f / (float)L : (float)(((double)hi - (double)lo) / (double)L);"),
+    ("scale_divide_split", "float s = (range == 0.0f ? 1.0f : range) / (float)L;",
+     "float s = range == 0.0f ? 1.0f / (float)L : hi / (float)L - lo / (float)L;"),
     ("zero_point_truncated", "float zf = rintf(-lo / s);", "float zf = truncf(-lo / s);"),
     ("zero_point_subtracted", "float c = rintf(quot) + zf;", "float c = rintf(quot) - zf;"),
     ("codes_round_half_up", "float c = rintf(quot) + zf;", "float c = roundf(quot) + zf;"),
@@ -198,3 +266,17 @@ def test_asym_pins_reject_mutant(tmp_path, name, old, new):
     except Exception as e:  # a mutant may also crash a check outright
         bad = ["raised %r" % e]
     assert bad, "mutant %s passed every pin" % name
+
+
+def test_f32_nearest_is_ieee_rounding():
+    """The rounding helper of the mixed-sign pin agrees with the IEEE fp64 ->
+    fp32 conversion (one correct rounding of an exact double) on normal,
+    subnormal, tie and overflowing values."""
+    rng = np.random.default_rng(5)
+    d = np.concatenate([rng.standard_normal(2000) * 2.0 ** rng.integers(-160, 130, 2000),
+                        (rng.integers(1, 1 << 24, 200) + 0.5) * 2.0 ** -20,  # ties
+                        [1.5 * 2.0 ** -149, 2.0 ** -150, 3.4e38, 3.403e38, -7e-46, 1e-300]])
+    with np.errstate(over="ignore"):
+        want = d.astype(np.float32)
+    for v, wv in zip(d, want):
+        assert np.float32(f32_nearest(Fraction(float(v)))).view(np.uint32) == wv.view(np.uint32), v
