@@ -36,22 +36,29 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def headers():
-    return [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + \
-        [os.path.join(ROOT, "include", "dq.h")]
+def local_deps(path: str, seen=None) -> set:
+    """The file and every local header it includes (#include "..."), recursively."""
+    import re
+    seen = set() if seen is None else seen
+    path = os.path.normpath(path)
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    for inc in re.findall(r'^\s*#include\s+"([^"]+)"', open(path, encoding="utf-8").read(), re.M):
+        local_deps(os.path.join(os.path.dirname(path), inc), seen)
+    return seen
 
 
 def build(verbose: bool = False, incremental: bool = False) -> str:
     """Compile every source in csrc/ and link libdq.so; returns its path.
-    incremental=True reuses an object newer than its source and every header."""
+    incremental=True reuses an object newer than its source and the headers it includes."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    newest_header = max(os.path.getmtime(h) for h in headers())
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src + ".o")
         if incremental and os.path.exists(obj) and os.path.getmtime(obj) > max(
-                newest_header, os.path.getmtime(os.path.join(CSRC, src))):
+                os.path.getmtime(d) for d in local_deps(os.path.join(CSRC, src))):
             return obj
         cmd = [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):

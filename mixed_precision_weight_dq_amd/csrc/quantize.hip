@@ -18,6 +18,7 @@
 // squares per row, and optionally one more launch that adds the rows up.
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_rule.hpp"
 
 namespace dq {
 
@@ -70,13 +71,8 @@ __device__ __forceinline__ void load_row_chunk(const void* __restrict__ w, int64
 
 // q = clip(rint(fl32(w / s))) for the 32 elements of a chunk, as offset-binary
 // codes packed into B words (elements at or past K give code 0 = zero bits).
-//
-// The divide: with r = fl32(1/s) (one IEEE divide per row), t' = fl32(w * r)
-// differs from w/s by at most 2^-23 |w/s|, and fl32(w/s) by at most 2^-24 |w/s|,
-// so |t' - fl32(w/s)| <= 1.5 * 2^-23 |w/s| <= 2^-22 (qmax + 1) for every element
-// of the row (|w/s| <= qmax (1 + 2^-23)).  rint gives the same integer for both
-// unless a half-integer lies within that distance of t'; only those elements
-// (and any non-finite t', e.g. when 1/s overflows) take the IEEE divide.
+// The divide: rounded_quotient (quant_rule.hpp) multiplies by r = fl32(1/s)
+// and takes the IEEE divide only near a rounding tie.
 template <int B>
 __device__ __forceinline__ void quantize_chunk(const float (&v)[kChunk], float s, float r,
                                                float margin, bool zero_codes, int64_t k0,
@@ -90,9 +86,7 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[kChunk], float s
     for (int i = 0; i < B; ++i) out[i] = 0;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-        float t = v[j] * r;
-        float q = rintf(t);
-        if (!(fabsf(t - q) < margin)) q = rintf(v[j] / s);  // near a tie, or not finite
+        float q = rounded_quotient(v[j], s, r, margin);
         q = fminf(fmaxf(q, kLo), kHi);
         // code u = q + 2^(B-1) in [0, 2^B): exact in fp32, converted once
         const uint32_t u = (zero_codes || k0 + j >= K) ? (k0 + j >= K ? 0u : (uint32_t)kBias)
@@ -138,10 +132,12 @@ __device__ __forceinline__ double chunk_sumsq(const float (&v)[kChunk], double a
 // kSumsq: pass 1 also sums w^2 over the row in fp64 (per lane in chunk order,
 // then across the wave by a fixed butterfly, then over the waves in order) and
 // writes it to row_sumsq[n]; the codes and scales are unchanged.
+// nonfinite (may be null): a counter, zeroed before the launch, that gains one
+// for every row holding a NaN or an infinity.
 template <int B, bool BF16, bool kAligned, bool kSumsq>
 __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t K, int64_t row_words, uint32_t* __restrict__ packed,
-    float* __restrict__ scales, double* __restrict__ row_sumsq)
+    float* __restrict__ scales, double* __restrict__ row_sumsq, uint32_t* __restrict__ nonfinite)
 {
     constexpr int32_t kQmax = (1 << (B - 1)) - 1;
     __shared__ uint32_t red[kQuantThreads / kWave];
@@ -202,6 +198,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     if (amax >= 0x7f800000u) {  // a NaN or an infinity in the row
         s = __uint_as_float(0x7fc00000u);
         zero_codes = true;
+        if (tid == 0 && nonfinite) atomicAdd(nonfinite, 1u);
     } else {
         const float a = __uint_as_float(amax);
         s = (a == 0.0f ? 1.0f : a) / qmaxf;
@@ -213,7 +210,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(
     }
     if (tid == 0) scales[n] = s;
     const float r = 1.0f / s;
-    const float margin = 0.5f - ldexpf(qmaxf + 1.0f, -21);
+    const float margin = quotient_margin(qmaxf + 1.0f);
 
     // ---- pass 2: quantize, offset, pack 32 codes into B whole words
     uint32_t* __restrict__ prow = packed + n * row_words;
@@ -254,7 +251,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_group_kernel(
     const int esize = BF16 ? 2 : 4;
     const bool vec_ok = ((K * esize) & 15) == 0;
     const float qmaxf = (float)kQmax;
-    const float margin = 0.5f - ldexpf(qmaxf + 1.0f, -21);
+    const float margin = quotient_margin(qmaxf + 1.0f);
     uint32_t* __restrict__ prow = packed + n * row_words;
 
     // every lane of a wave takes part in each round (the butterfly needs them)
@@ -317,9 +314,7 @@ __device__ __forceinline__ void quantize_chunk_asym(const float (&v)[kChunk], fl
     for (int i = 0; i < B; ++i) out[i] = 0;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-        float t = v[j] * r;
-        float q = rintf(t);
-        if (!(fabsf(t - q) < margin)) q = rintf(v[j] / s);  // near a tie, or not finite
+        float q = rounded_quotient(v[j], s, r, margin);
         const float c = fminf(fmaxf(q + zf, 0.0f), kL);
         uint32_t u = mode == 0 ? (uint32_t)c : (mode == 1 ? (1u << (B - 1)) : 0u);
         if (k0 + j >= K) u = 0;
@@ -414,7 +409,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_asym_kernel(
     const float r = 1.0f / s;
     // |w / s| <= L (1 + 2^-22): the reciprocal product stays within
     // 2^-22 (L + 1) of fl32(w / s), so rint agrees outside that margin
-    const float margin = 0.5f - ldexpf(Lf + 1.0f, -21);
+    const float margin = quotient_margin(Lf + 1.0f);
 
     // ---- pass 2: codes, packed 32 to B whole words
     uint32_t* __restrict__ prow = packed + n * row_words;
@@ -431,53 +426,6 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_pack_asym_kernel(
         store_chunk<B>(prow, c, row_words, out);
     }
     for (int64_t i = nchunks * B + tid; i < row_words; i += threads) prow[i] = 0u;
-}
-
-// sum_k x[m, k] for the asymmetric products: one workgroup per row of x, fp64
-// partial sums in a fixed order, rounded once to fp32.  When rows are 16-byte
-// aligned, thread t adds the 8-element pieces t, t + 256, ... (four loads in
-// flight per round); otherwise elements t, t + 256, ...; then a fixed tree.
-constexpr int kXSumThreads = 256;
-
-template <bool kVec>
-__global__ __launch_bounds__(kXSumThreads) void x_sum_kernel(const uint16_t* __restrict__ x,
-                                                             int64_t K, float* __restrict__ xsum)
-{
-    __shared__ double part[kXSumThreads];
-    const int64_t m = blockIdx.x;
-    const int tid = threadIdx.x;
-    double acc = 0.0;
-    if (kVec) {
-        const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
-        const int64_t npieces = K / 8;
-        for (int64_t p0 = tid; p0 < npieces; p0 += 4 * kXSumThreads) {
-            uint4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t p = p0 + (int64_t)u * kXSumThreads;
-                v[u] = p < npieces ? row[p] : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc += (double)__uint_as_float(e[j] << 16);
-                    acc += (double)__uint_as_float(e[j] & 0xffff0000u);
-                }
-            }
-        }
-    } else {
-        for (int64_t k = tid; k < K; k += kXSumThreads)
-            acc += (double)bf16_bits_to_float(x[m * K + k]);
-    }
-    part[tid] = acc;
-    __syncthreads();
-    for (int d = kXSumThreads / 2; d >= 1; d >>= 1) {
-        if (tid < d) part[tid] += part[tid + d];
-        __syncthreads();
-    }
-    if (tid == 0) xsum[m] = (float)part[0];
 }
 
 // One workgroup per row; thread t turns codes 4t .. 4t+3 (then + 1024, ...)
@@ -633,11 +581,22 @@ __global__ __launch_bounds__(kSumThreads) void sum_rows_kernel(const double* __r
     if (threadIdx.x == 0) out[0] = part[0];
 }
 
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p)
+{
+    if (threadIdx.x == 0) *p = 0u;
+}
+
 template <int B, bool kSumsq>
 hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K, uint32_t* packed,
-                                  float* scales, double* row_sumsq, hipStream_t stream)
+                                  float* scales, double* row_sumsq, uint32_t* nonfinite,
+                                  hipStream_t stream)
 {
     const int64_t rw = packed_row_words(K, B);
+    if (nonfinite) {  // a fill kernel rather than a memset node (graph-capture safe)
+        zero_u32_kernel<<<dim3(1), dim3(kWave), 0, stream>>>(nonfinite);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // one chunk per thread where the row allows, in whole waves, 64..256 threads
     const int64_t nchunks = ceil_div(K, kChunk);
     const int threads = (int)(nchunks >= kQuantThreads ? kQuantThreads
@@ -646,16 +605,16 @@ hipError_t launch_quantize_pack_b(const void* w, bool bf16, int64_t N, int64_t K
     const bool aligned = K % kChunk == 0;
     if (bf16 && aligned)
         quantize_pack_kernel<B, true, true, kSumsq>
-            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq, nonfinite);
     else if (bf16)
         quantize_pack_kernel<B, true, false, kSumsq>
-            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq, nonfinite);
     else if (aligned)
         quantize_pack_kernel<B, false, true, kSumsq>
-            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq, nonfinite);
     else
         quantize_pack_kernel<B, false, false, kSumsq>
-            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq);
+            <<<grid, block, 0, stream>>>(w, K, rw, packed, scales, row_sumsq, nonfinite);
     return hipGetLastError();
 }
 
@@ -673,9 +632,10 @@ hipError_t launch_unpack_b(const uint32_t* packed, const float* scales, const in
 }  // namespace
 
 hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
-                                uint32_t* packed, float* scales, hipStream_t stream)
+                                uint32_t* packed, float* scales, uint32_t* nonfinite,
+                                hipStream_t stream)
 {
-#define CALL(B) launch_quantize_pack_b<B, false>(w, bf16, N, K, packed, scales, nullptr, stream)
+#define CALL(B) launch_quantize_pack_b<B, false>(w, bf16, N, K, packed, scales, nullptr, nonfinite, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
 }
@@ -685,7 +645,7 @@ hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64
                                       double* matrix_sumsq, hipStream_t stream)
 {
     hipError_t e;
-#define CALL(B) launch_quantize_pack_b<B, true>(w, bf16, N, K, packed, scales, row_sumsq, stream)
+#define CALL(B) launch_quantize_pack_b<B, true>(w, bf16, N, K, packed, scales, row_sumsq, nullptr, stream)
     e = [&]() -> hipError_t { DQ_BITS_SWITCH(bits, CALL) }();
 #undef CALL
     if (e != hipSuccess || !matrix_sumsq) return e;
@@ -782,15 +742,6 @@ hipError_t launch_quantize_pack_group(const void* w, bool bf16, int64_t N, int64
 #define CALL(B) launch_quantize_pack_group_b<B>(w, bf16, N, K, group, packed, scales, stream)
     DQ_BITS_SWITCH(bits, CALL)
 #undef CALL
-}
-
-hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hipStream_t stream)
-{
-    if (K % 8 == 0)  // 16-byte rows (x itself is 16-byte aligned)
-        x_sum_kernel<true><<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
-    else
-        x_sum_kernel<false><<<dim3((unsigned)M), dim3(kXSumThreads), 0, stream>>>(x, K, xsum);
-    return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint32_t* packed, const float* scales, const int32_t* zeros,
