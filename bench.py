@@ -174,14 +174,12 @@ def allocation_context(dq, workload, sumsq, reps: int = 20):
 def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
     """The asymmetric (zero-point) variant, outside the timed steps, on the
     step's own inputs: quantize + pack of the five 4096^2 decode matrices, the
-    decode group (8 tokens x 5 GEMVs on 8 rotated copies, one dq_x_sum per
-    token included) and the b = 6 prefill GEMM (with its dq_x_sum), each
-    beside the symmetric figure of the same run."""
+    decode group (8 tokens x 5 GEMVs on 8 rotated copies) and the b = 6
+    prefill GEMM, each beside the symmetric figure of the same run."""
     Nd, Kd = next(iter(W2.values())).shape
     q = {b: dq.quantize_pack_asym(W, b) for b, W in W2.items()}
     copies = [q] + [{b: (P.clone(), S, Z) for b, (P, S, Z) in q.items()} for _ in range(len(X1t) - 1)]
     ys = {b: torch.empty((1, Nd), dtype=torch.float32, device=W.device) for b, W in W2.items()}
-    xs = [torch.empty((1,), dtype=torch.float32, device=X.device) for X in X1t]
 
     def timed(fn):
         fn()
@@ -206,11 +204,9 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
     lib = dq.load()
     calls = []
     for t, X in enumerate(X1t):
-        calls.append((lib.dq_x_sum, (X.data_ptr(), 1, Kd, xs[t].data_ptr(), cs)))
         for b, (P, S, Z) in copies[t].items():
             calls.append((lib.dq_gemv_asym, (X.data_ptr(), 1, P.data_ptr(), S.data_ptr(),
-                                             Z.data_ptr(), xs[t].data_ptr(), Nd, Kd, b,
-                                             ys[b].data_ptr(), cs)))
+                                             Z.data_ptr(), Nd, Kd, b, ys[b].data_ptr(), cs)))
 
     def decode():
         for fn, a in calls:
@@ -219,16 +215,11 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
     b6 = 6
     P6, S6, Z6 = dq.quantize_pack_asym(W4[b6], b6)
     Y = torch.empty((X4.shape[0], P6.shape[0]), dtype=torch.float32, device=X4.device)
-    xs4 = torch.empty((X4.shape[0],), dtype=torch.float32, device=X4.device)
-
-    def xsum4():
-        dq.x_sum(X4, xs4)
 
     def gemm():
-        dq.gemm_asym(X4, P6, S6, Z6, X4.shape[1], b6, xsum=xs4, y=Y)
+        dq.gemm_asym(X4, P6, S6, Z6, X4.shape[1], b6, y=Y)
 
-    t_q, t_d, t_x, t_g = timed(quant), timed(decode), timed(xsum4), timed(gemm)
-    t_g += t_x
+    t_q, t_d, t_g = timed(quant), timed(decode), timed(gemm)
     dec_bytes = len(X1t) * sum(Nd * Kd * b // 8 for b in W2)
     q_bytes = sum(Nd * Kd * (16 + b) // 8 for b in W2)
     M, K = X4.shape
@@ -237,11 +228,10 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
             "gemv_m1_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
             "gemv_m1_per_launch_us": round(t_d / (len(X1t) * len(W2)) * 1e3, 3),
             "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
-            "x_sum_2048x8192_us": round(t_x * 1e3, 2),
             "what": "asymmetric scheme on the step's inputs: quantize+pack (read + write bytes), "
-                    "decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies with one dq_x_sum "
-                    "per token (packed-weight GB/s), prefill GEMM M=2048 b=6 with its dq_x_sum; "
-                    "median of the step count, outside the timed steps"}
+                    "decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed-weight "
+                    "GB/s), prefill GEMM M=2048 b=6; the products subtract each row's zero "
+                    "point from its codes; median of the step count, outside the timed steps"}
 
 
 def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 128):

@@ -95,14 +95,18 @@ typedef int32_t dq_status;
 size_t dq_packed_row_bytes(int64_t K, int32_t bits);
 
 /* Quantize W[N, K] row by row to `bits` bits and pack it.
- *   w       in   device, [N, K], dtype w_dtype (DQ_F32 or DQ_BF16)
- *   packed  out  device, [N, row_words] uint32, fully written (padding = 0)
- *   scales  out  device, [N] fp32
+ *   w              in   device, [N, K], dtype w_dtype (DQ_F32 or DQ_BF16)
+ *   packed         out  device, [N, row_words] uint32, fully written (padding = 0)
+ *   scales         out  device, [N] fp32
+ *   nonfinite_rows out  device, [1] uint32, 4-byte aligned, may be NULL: the
+ *                       number of rows holding a NaN or +-Inf (the pages take
+ *                       finite weights; this reports where that fails)
  * A row holding a NaN or +-Inf gets scale = quiet NaN (bits 0x7FC00000) and
  * every code = 2^(b-1) (q = 0).  A row whose max|W| / qmax underflows to 0 is
  * treated like an all-zero row: scale = fl32(1/qmax), q = 0. */
 dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
-                           uint32_t* packed, float* scales, void* stream);
+                           uint32_t* packed, float* scales, uint32_t* nonfinite_rows,
+                           void* stream);
 
 /* Group-wise scales ("量化" tutorial, exercise 1 of its exercises: one scale
  * per group of weights instead of per channel, groups of 32 to 256 as
@@ -147,22 +151,19 @@ dq_status dq_unpack_asym(const uint32_t* packed, const float* scales, const int3
                          int64_t N, int64_t K, int32_t bits, int32_t* q_out, float* w_out,
                          void* stream);
 
-/* xsum[m] = sum_k x[m, k] (device, fp32 [M]; summed in fp64 in a fixed order
- * and rounded once), the activation term the asymmetric products need; one
- * call serves every matrix that multiplies the same x. */
-dq_status dq_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, void* stream);
-
-/* Asymmetric products: y[m,n] = s[n] * sum_k x[m,k] (u[n,k] - z[n]), computed
- * as s[n] * (sum_k x (u - 2^(b-1)) + (2^(b-1) - z[n]) * xsum[m]) with the
- * kernels of dq_gemv / dq_gemm (same M ranges and layouts; zeros [N] int32
- * and xsum [M] fp32 from dq_x_sum of the same x, both device, 4-byte
- * aligned). */
+/* Asymmetric products: y[m,n] = s[n] * sum_k x[m,k] (u[n,k] - z[n]), with the
+ * kernels of dq_gemv / dq_gemm (same M ranges and layouts; zeros [N] int32,
+ * device, 4-byte aligned).  Each code has the row's zero point subtracted
+ * before it meets x, so every product x * (u - z) is exact (|u - z| < 2^b:
+ * for b >= 9 the codes go through fp32 FMAs on the vector units, or as two
+ * exact bf16 halves on the matrix cores); accumulation is fp32 and the scale
+ * is applied once per output, as in the symmetric products. */
 dq_status dq_gemv_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
-                       float* y, void* stream);
+                       const int32_t* zeros, int64_t N, int64_t K, int32_t bits, float* y,
+                       void* stream);
 dq_status dq_gemm_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
-                       float* y, void* stream);
+                       const int32_t* zeros, int64_t N, int64_t K, int32_t bits, float* y,
+                       void* stream);
 
 /* The statistic a matrix's sensitivity needs (DynaQuant page, "第一步：敏感度
  * 测量": mean(w^2) of the matrix), measured before any width is chosen: one

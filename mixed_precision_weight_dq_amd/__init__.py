@@ -13,8 +13,8 @@ kernels behind the C ABI declared in ``include/dq.h``):
   ``stream_read`` -- the same calls on torch tensors (torch provides device
   memory and the current stream); they check device, dtype and contiguity,
   allocate outputs with torch and raise ``DQError`` on a non-zero status.
-* ``quantize_pack_asym``, ``unpack_asym``, ``x_sum``, ``gemv_asym``,
-  ``gemm_asym`` -- the asymmetric (zero-point) variant on torch tensors.
+* ``quantize_pack_asym``, ``unpack_asym``, ``gemv_asym``, ``gemm_asym`` --
+  the asymmetric (zero-point) variant on torch tensors.
 * ``quantize_pack_group``, ``unpack_group``, ``gemv_group``, ``gemm_group``
   -- group-wise scales (one per g codes of a row) on torch tensors.
 * ``sensitivity``, ``allocate_bits`` -- the host-side allocation calls on
@@ -40,8 +40,8 @@ __all__ = [
     "packed_row_bytes", "quantize_pack", "unpack", "gemv", "gemm", "stream_read", "load",
     "dq_row_sumsq", "row_sumsq", "dq_quantize_pack_sumsq", "dq_sensitivity", "dq_allocate_bits", "quantize_pack_sumsq",
     "sensitivity", "allocate_bits", "NATIVE_LEVELS", "FULL_LEVELS", "DQFileMatrix",
-    "write_packed_file", "PackedFile", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
-    "dq_gemv_asym", "dq_gemm_asym", "quantize_pack_asym", "unpack_asym", "x_sum", "gemv_asym",
+    "write_packed_file", "PackedFile", "dq_quantize_pack_asym", "dq_unpack_asym",
+    "dq_gemv_asym", "dq_gemm_asym", "quantize_pack_asym", "unpack_asym", "gemv_asym",
     "gemm_asym", "dq_quantize_pack_group", "dq_unpack_group", "dq_gemv_group", "dq_gemm_group",
     "quantize_pack_group", "unpack_group", "gemv_group", "gemm_group",
 ]
@@ -85,7 +85,7 @@ def load():
     i64, i32, vp, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32
     lib.dq_packed_row_bytes.argtypes = [i64, i32]
     lib.dq_packed_row_bytes.restype = ctypes.c_size_t
-    lib.dq_quantize_pack.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+    lib.dq_quantize_pack.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
     lib.dq_quantize_pack.restype = st
     lib.dq_unpack.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
     lib.dq_unpack.restype = st
@@ -101,11 +101,9 @@ def load():
     lib.dq_quantize_pack_asym.restype = st
     lib.dq_unpack_asym.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp]
     lib.dq_unpack_asym.restype = st
-    lib.dq_x_sum.argtypes = [vp, i64, i64, vp, vp]
-    lib.dq_x_sum.restype = st
-    lib.dq_gemv_asym.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemv_asym.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, vp, vp]
     lib.dq_gemv_asym.restype = st
-    lib.dq_gemm_asym.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.dq_gemm_asym.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, vp, vp]
     lib.dq_gemm_asym.restype = st
     lib.dq_quantize_pack_group.argtypes = [vp, i32, i64, i64, i32, i64, vp, vp, vp]
     lib.dq_quantize_pack_group.restype = st
@@ -151,8 +149,9 @@ def dq_packed_row_bytes(K: int, bits: int) -> int:
 
 
 def dq_quantize_pack(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int, scales: int,
-                     stream: int = 0) -> int:
-    return int(load().dq_quantize_pack(w, w_dtype, N, K, bits, packed, scales, stream))
+                     nonfinite_rows: int = 0, stream: int = 0) -> int:
+    return int(load().dq_quantize_pack(w, w_dtype, N, K, bits, packed, scales, nonfinite_rows,
+                                       stream))
 
 
 def dq_quantize_pack_asym(w: int, w_dtype: int, N: int, K: int, bits: int, packed: int,
@@ -165,18 +164,14 @@ def dq_unpack_asym(packed: int, scales: int, zeros: int, N: int, K: int, bits: i
     return int(load().dq_unpack_asym(packed, scales, zeros, N, K, bits, q_out, w_out, stream))
 
 
-def dq_x_sum(x: int, M: int, K: int, xsum: int, stream: int = 0) -> int:
-    return int(load().dq_x_sum(x, M, K, xsum, stream))
-
-
-def dq_gemv_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int, N: int, K: int,
+def dq_gemv_asym(x: int, M: int, packed: int, scales: int, zeros: int, N: int, K: int,
                  bits: int, y: int, stream: int = 0) -> int:
-    return int(load().dq_gemv_asym(x, M, packed, scales, zeros, xsum, N, K, bits, y, stream))
+    return int(load().dq_gemv_asym(x, M, packed, scales, zeros, N, K, bits, y, stream))
 
 
-def dq_gemm_asym(x: int, M: int, packed: int, scales: int, zeros: int, xsum: int, N: int, K: int,
+def dq_gemm_asym(x: int, M: int, packed: int, scales: int, zeros: int, N: int, K: int,
                  bits: int, y: int, stream: int = 0) -> int:
-    return int(load().dq_gemm_asym(x, M, packed, scales, zeros, xsum, N, K, bits, y, stream))
+    return int(load().dq_gemm_asym(x, M, packed, scales, zeros, N, K, bits, y, stream))
 
 
 def dq_quantize_pack_group(w: int, w_dtype: int, N: int, K: int, bits: int, group: int,
@@ -285,9 +280,10 @@ def _check(status: int, where: str):
         raise DQError(status, where)
 
 
-def quantize_pack(w, bits: int, packed=None, scales=None):
+def quantize_pack(w, bits: int, packed=None, scales=None, nonfinite=None):
     """W[N, K] (float32 or bfloat16, on the GPU) -> (packed int32 [N, row_bytes/4] holding
-    the uint32 words, scales float32 [N])."""
+    the uint32 words, scales float32 [N]).  nonfinite: optional int32 [1] tensor
+    that receives the number of rows holding a NaN or an infinity."""
     torch = _torch()
     _need(w, "w", (torch.float32, torch.bfloat16), 2)
     N, K = w.shape
@@ -300,9 +296,14 @@ def quantize_pack(w, bits: int, packed=None, scales=None):
     _need(scales, "scales", (torch.float32,), 1)
     if tuple(packed.shape) != (N, rw) or tuple(scales.shape) != (N,):
         raise ValueError("packed/scales shape mismatch")
+    if nonfinite is not None:
+        _need(nonfinite, "nonfinite", (torch.int32,), 1)
+        if nonfinite.shape[0] != 1:
+            raise ValueError("nonfinite must be [1]")
     dt = DQ_BF16 if w.dtype == torch.bfloat16 else DQ_F32
     _check(dq_quantize_pack(w.data_ptr(), dt, N, K, bits, packed.data_ptr(), scales.data_ptr(),
-                            _stream(w)), "dq_quantize_pack")
+                            nonfinite.data_ptr() if nonfinite is not None else 0, _stream(w)),
+           "dq_quantize_pack")
     return packed, scales
 
 
@@ -341,52 +342,34 @@ def unpack_asym(packed, scales, zeros, K: int, bits: int, want_q: bool = True,
     return q, w
 
 
-def x_sum(x, xsum=None):
-    """sum_k x[m, k] for bf16 x [M, K] on the GPU -> float32 [M]."""
-    torch = _torch()
-    _need(x, "x", (torch.bfloat16,), 2)
-    M, K = x.shape
-    if xsum is None:
-        xsum = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _need(xsum, "xsum", (torch.float32,), 1)
-    if xsum.shape[0] != M:
-        raise ValueError("xsum must be [M]")
-    _check(dq_x_sum(x.data_ptr(), M, K, xsum.data_ptr(), _stream(x)), "dq_x_sum")
-    return xsum
-
-
-def _matmul_asym(fn, name, x, packed, scales, zeros, xsum, K: int, bits: int, y=None):
+def _matmul_asym(fn, name, x, packed, scales, zeros, K: int, bits: int, y=None):
     torch = _torch()
     _need(x, "x", (torch.bfloat16,), 2)
     _need(packed, "packed", (torch.int32,), 2)
     _need(scales, "scales", (torch.float32,), 1)
     _need(zeros, "zeros", (torch.int32,), 1)
     M, N = x.shape[0], packed.shape[0]
-    if xsum is None:
-        xsum = x_sum(x)
-    _need(xsum, "xsum", (torch.float32,), 1)
     if (x.shape[1] != K or packed.shape[1] != packed_row_bytes(K, bits) // 4
-            or scales.shape[0] != N or zeros.shape[0] != N or xsum.shape[0] != M):
-        raise ValueError("shape mismatch between x, packed, scales, zeros, xsum, K and bits")
+            or scales.shape[0] != N or zeros.shape[0] != N):
+        raise ValueError("shape mismatch between x, packed, scales, zeros, K and bits")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _need(y, "y", (torch.float32,), 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(fn(x.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-              xsum.data_ptr(), N, K, bits, y.data_ptr(), _stream(x)), name)
+    _check(fn(x.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, bits,
+              y.data_ptr(), _stream(x)), name)
     return y
 
 
-def gemv_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
-    """y = s * x . (u - z)^T for 1 <= M <= 16; xsum (from ``x_sum``) is computed
-    when not given."""
-    return _matmul_asym(dq_gemv_asym, "dq_gemv_asym", x, packed, scales, zeros, xsum, K, bits, y)
+def gemv_asym(x, packed, scales, zeros, K: int, bits: int, y=None):
+    """y = s * x . (u - z)^T for 1 <= M <= 16."""
+    return _matmul_asym(dq_gemv_asym, "dq_gemv_asym", x, packed, scales, zeros, K, bits, y)
 
 
-def gemm_asym(x, packed, scales, zeros, K: int, bits: int, xsum=None, y=None):
+def gemm_asym(x, packed, scales, zeros, K: int, bits: int, y=None):
     """y = s * x . (u - z)^T on the matrix cores (any M >= 1)."""
-    return _matmul_asym(dq_gemm_asym, "dq_gemm_asym", x, packed, scales, zeros, xsum, K, bits, y)
+    return _matmul_asym(dq_gemm_asym, "dq_gemm_asym", x, packed, scales, zeros, K, bits, y)
 
 
 def quantize_pack_group(w, bits: int, group: int):

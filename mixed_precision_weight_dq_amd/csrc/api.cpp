@@ -49,15 +49,18 @@ size_t dq_packed_row_bytes(int64_t K, int32_t bits)
 }
 
 dq_status dq_quantize_pack(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
-                           uint32_t* packed, float* scales, void* stream)
+                           uint32_t* packed, float* scales, uint32_t* nonfinite_rows,
+                           void* stream)
 {
     if (!w || !packed || !scales) return DQ_ERR_NULL;
     dq_status st = check_common(N, K, bits);
     if (st != DQ_OK) return st;
     if (w_dtype != DQ_F32 && w_dtype != DQ_BF16) return DQ_ERR_DTYPE;
-    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DQ_ERR_ALIGN;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4) ||
+        !aligned(nonfinite_rows, 4))
+        return DQ_ERR_ALIGN;
     return hip_status(dq::launch_quantize_pack(w, w_dtype == DQ_BF16, N, K, bits, packed, scales,
-                                               static_cast<hipStream_t>(stream)));
+                                               nonfinite_rows, static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_quantize_pack_sumsq(const void* w, int32_t w_dtype, int64_t N, int64_t K,
@@ -182,14 +185,6 @@ dq_status dq_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed, co
                                             static_cast<hipStream_t>(stream)));
 }
 
-dq_status dq_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, void* stream)
-{
-    if (!x || !xsum) return DQ_ERR_NULL;
-    if (M < 1 || M > 0x7fffffffLL || K < 1 || K > DQ_MAX_K) return DQ_ERR_SHAPE;
-    if (!aligned(x, 16) || !aligned(xsum, 4)) return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_x_sum(x, M, K, xsum, static_cast<hipStream_t>(stream)));
-}
-
 dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                   int64_t N, int64_t K, int32_t bits, float* y, void* stream)
 {
@@ -199,22 +194,22 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
     if (M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, nullptr, nullptr,
+    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_gemv_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
-                       float* y, void* stream)
+                       const int32_t* zeros, int64_t N, int64_t K, int32_t bits, float* y,
+                       void* stream)
 {
-    if (!x || !packed || !scales || !zeros || !xsum || !y) return DQ_ERR_NULL;
+    if (!x || !packed || !scales || !zeros || !y) return DQ_ERR_NULL;
     dq_status st = check_common(N, K, bits);
     if (st != DQ_OK) return st;
     if (M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4) ||
-        !aligned(zeros, 4) || !aligned(xsum, 4))
+        !aligned(zeros, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, zeros, xsum,
+    return hip_status(dq::launch_gemv(x, M, packed, scales, N, K, bits, y, zeros,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -227,22 +222,22 @@ dq_status dq_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
     if (M < 1 || M > 0x7fffffffLL) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, nullptr, nullptr,
+    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
 
 dq_status dq_gemm_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
-                       const int32_t* zeros, const float* xsum, int64_t N, int64_t K, int32_t bits,
-                       float* y, void* stream)
+                       const int32_t* zeros, int64_t N, int64_t K, int32_t bits, float* y,
+                       void* stream)
 {
-    if (!x || !packed || !scales || !zeros || !xsum || !y) return DQ_ERR_NULL;
+    if (!x || !packed || !scales || !zeros || !y) return DQ_ERR_NULL;
     dq_status st = check_common(N, K, bits);
     if (st != DQ_OK) return st;
     if (M < 1 || M > 0x7fffffffLL) return DQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4) ||
-        !aligned(zeros, 4) || !aligned(xsum, 4))
+        !aligned(zeros, 4))
         return DQ_ERR_ALIGN;
-    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, zeros, xsum,
+    return hip_status(dq::launch_gemm(x, M, packed, scales, N, K, bits, y, zeros,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -153,55 +153,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
-// Zero points of the asymmetric scheme, for the products' epilogues.  Codes
-// are stored unsigned, u = rint(w / s) + z[n]; every product kernel sums
-// x * (u - 2^(b-1)) (the two's-complement view of the code), so adding
-// (2^(b-1) - z[n]) * sum_k x[m, k] gives sum_k x * (u - z[n]).  The product
-// kernels take the type as a template parameter: NoZeroPoints (the symmetric
-// scheme) adds nothing and compiles to the plain epilogue.
-// Each type gives coef<B>(n), read once per output column before any store
-// (a load issued after the stores would wait for all of them), and
-// apply(v, coef, m) = v + coef * sum_k x[m, k].
+// Zero points of the asymmetric scheme.  Codes are stored unsigned,
+// u = rint(w / s) + z[n], and dequantize as q = u - z[n].  The product kernels
+// take the scheme as a template type and, for ZeroPoints, subtract the row's
+// zero point from every code before it meets x, so each product x * (u - z)
+// is formed exactly, as in the symmetric scheme (where q = u - 2^(b-1)).
+// Nothing is folded into an activation-sum term afterwards: such a fold adds
+// two large terms that cancel when most codes equal z.
+//
+// |u - z| < 2^b, one bit more than a symmetric code, so the asymmetric
+// kernels treat b = 9 like the wide codes (fp32 FMAs, or two exact bf16
+// halves on the matrix cores).
 struct NoZeroPoints {
-    template <int B>
-    __device__ __forceinline__ float coef(int64_t) const
-    {
-        return 0.0f;
-    }
-    __device__ __forceinline__ float apply(float v, float, int64_t) const { return v; }
+    static constexpr bool kAsym = false;
+    __device__ __forceinline__ int32_t zero(int64_t) const { return 0; }
 };
 
 struct ZeroPoints {
+    static constexpr bool kAsym = true;
     const int32_t* zeros;  // [N]
-    const float* xsum;     // [M]: sum_k x[m, k]
-
-    template <int B>
-    __device__ __forceinline__ float coef(int64_t n) const
-    {
-        return (float)((1 << (B - 1)) - zeros[n]);
-    }
-    __device__ __forceinline__ float apply(float v, float c, int64_t m) const
-    {
-        return fmaf(c, xsum[m], v);
-    }
-};
-
-// ZeroPoints with one tile's activation sums staged in LDS (row m at
-// xs[m - m0]), for epilogues that read each row's sum many times.
-struct TileZeroPoints {
-    const int32_t* zeros;
-    const float* xs;
-    int64_t m0;
-
-    template <int B>
-    __device__ __forceinline__ float coef(int64_t n) const
-    {
-        return (float)((1 << (B - 1)) - zeros[n]);
-    }
-    __device__ __forceinline__ float apply(float v, float c, int64_t m) const
-    {
-        return fmaf(c, xs[m - m0], v);
-    }
+    __device__ __forceinline__ int32_t zero(int64_t n) const { return zeros[n]; }
 };
 
 // Group-wise scales for the pipelined 128-row GEMM and the resident-x GEMV:
@@ -213,13 +184,8 @@ struct GroupScales {
     int64_t G;
     int64_t group;  // codes per group, a power of two >= 32
 
-    // no zero points: the epilogue adds nothing
-    template <int B>
-    __device__ __forceinline__ float coef(int64_t) const
-    {
-        return 0.0f;
-    }
-    __device__ __forceinline__ float apply(float v, float, int64_t) const { return v; }
+    static constexpr bool kAsym = false;
+    __device__ __forceinline__ int32_t zero(int64_t) const { return 0; }
 };
 
 template <class P>
@@ -230,30 +196,5 @@ template <>
 struct is_group_scales<GroupScales> {
     static constexpr bool value = true;
 };
-
-// Stage rows [m0, m0 + rows) of the activation sums into `lds` (a buffer the
-// workgroup no longer uses) between two barriers; every thread of the
-// workgroup must call it.  The symmetric scheme stages nothing.
-__device__ __forceinline__ NoZeroPoints stage_tile_zero_points(NoZeroPoints, float*, int64_t,
-                                                               int64_t, int)
-{
-    return {};
-}
-
-__device__ __forceinline__ NoZeroPoints stage_tile_zero_points(GroupScales, float*, int64_t, int64_t,
-                                                               int)
-{
-    return {};
-}
-
-__device__ __forceinline__ TileZeroPoints stage_tile_zero_points(ZeroPoints zp, float* lds,
-                                                                 int64_t m0, int64_t M, int rows)
-{
-    __syncthreads();
-    for (int i = threadIdx.x; i < rows; i += blockDim.x)
-        lds[i] = m0 + i < M ? zp.xsum[m0 + i] : 0.0f;
-    __syncthreads();
-    return {zp.zeros, lds, m0};
-}
 
 }  // namespace dq

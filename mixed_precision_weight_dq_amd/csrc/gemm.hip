@@ -52,7 +52,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
     float* __restrict__ y, ZP zp)
 {
-    constexpr bool kSplit = B >= 10;
+    constexpr bool kAsym = ZP::kAsym;
+    constexpr bool kSplit = split_codes<B, kAsym>();
+    // two exact bf16 halves: q = 2^kShift * (q >> kShift) + (q & (2^kShift - 1))
+    constexpr int kShift = kAsym ? B - 8 : 6;
     constexpr int kPlanes = kSplit ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLd];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[kPlanes][kBN * kLd];
@@ -77,6 +80,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 
     const int sr = tid >> 1;  // staging row within the tile
     const int sh = tid & 1;   // which 32-wide half of the k slice
+    const int32_t zs = zp.zero(n0 + sr < N ? n0 + sr : N - 1);  // the staging row's zero point
 
     for (int64_t k0 = 0; k0 < K; k0 += kBK) {
         // ---- x slice -> LDS
@@ -106,17 +110,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
                 for (int i = 0; i < B; ++i) wd[i] = 0;
             }
+            if constexpr (!kAsym) {
 #pragma unroll
-            for (int i = 0; i < B; ++i) wd[i] ^= code_msb_mask<B>(i);
+                for (int i = 0; i < B; ++i) wd[i] ^= code_msb_mask<B>(i);
+            }
             uint16_t* d0 = &Bs[0][sr * kLd + kChunk * sh];
             uint16_t* d1 = &Bs[kPlanes - 1][sr * kLd + kChunk * sh];
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) {
-                int32_t q = chunk_code_signed<B>(wd, j);
+                int32_t q = kAsym ? (int32_t)chunk_code_unsigned<B>(wd, j) - zs
+                                  : chunk_code_signed<B>(wd, j);
                 if (!live || c * kChunk + j >= K) q = 0;
                 if (kSplit) {
-                    d0[j] = exact_bf16_bits((q >> 6) * 64);
-                    d1[j] = exact_bf16_bits(q & 63);
+                    d0[j] = exact_bf16_bits((q >> kShift) * (1 << kShift));
+                    d1[j] = exact_bf16_bits(q & ((1 << kShift) - 1));
                 } else {
                     d0[j] = exact_bf16_bits(q);
                 }
@@ -156,13 +163,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
         if (n >= N) continue;
         const float s = scales[n];
-        const float zc = zp.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-                if (m < M) y[m * N + n] = s * zp.apply(acc[i][j][r], zc, m);
+                if (m < M) y[m * N + n] = s * acc[i][j][r];
             }
         }
     }
@@ -218,7 +224,8 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     float* __restrict__ y, ZP zp)
 {
     using T = MfmaTile<kMT, kNT>;
-    constexpr bool kSplit = B >= 10;
+    constexpr bool kAsym = ZP::kAsym;
+    constexpr bool kSplit = split_codes<B, kAsym>();
     constexpr bool kGroup = is_group_scales<ZP>::value;
     constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
     __shared__ __attribute__((aligned(16))) uint4 As[T::kStages][T::kPieces];
@@ -260,10 +267,12 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     const int64_t nrows = N - n0 < T::BN ? N - n0 : T::BN;
     const BufRef wbuf = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
     uint32_t woff[kNT];
+    int32_t zr[kNT];  // zero point of this lane's weight row in each column tile
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
         const int64_t nl = wave * 32 * kNT + j * 32 + c;
         woff[j] = (uint32_t)((nl < nrows ? nl : nrows - 1) * row_words * 4 + h * B * 4);
+        zr[j] = zp.zero(n0 + (nl < nrows ? nl : nrows - 1));
     }
     // LDS slot of this lane's x fragment for tile i, substep t: row r = 32i + c,
     // and xswz(32i + c) = xswz(c), so the slot is 256 i + a constant per t
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int j = 0; j < kNT; ++j) expand8<B>(w[st][j], t, bh[t][j], bl[t][j]);
+            for (int j = 0; j < kNT; ++j) expand8z<B, kAsym>(w[st][j], zr[j], t, bh[t][j], bl[t][j]);
         // step ks+1 (after the last step, the last step again: loads stay
         // inside the buffers and the data is never used)
         const int64_t kn = ks + 1 < nk ? ks + 1 : nk - 1;
@@ -385,23 +394,19 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 
     // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4;
     // whole tiles store without bounds checks, as streaming stores
-    constexpr float kUnscale = 1.0f / expand8_scale<B>();
-    const auto zt = stage_tile_zero_points(zp, reinterpret_cast<float*>(&As[0][0]), m0, M, T::BM);
+    constexpr float kUnscale = 1.0f / expand8_scale<B, kAsym>();
     if (m0 + T::BM <= M && n0 + T::BN <= N) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
             const float s = kGroup ? 1.0f : scales[n];
-            const float zc = zt.template coef<B>(n);
 #pragma unroll
             for (int i = 0; i < kMT; ++i) {
                 float* yp = y + (m0 + i * 32 + 4 * h) * N + n;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    __builtin_nontemporal_store(
-                        s * zt.apply(acc[i][j][r] * kUnscale, zc,
-                                     m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
-                        yp + (8 * (r >> 2) + (r & 3)) * N);
+                    __builtin_nontemporal_store(s * (acc[i][j][r] * kUnscale),
+                                                yp + (8 * (r >> 2) + (r & 3)) * N);
             }
         }
         return;
@@ -411,13 +416,12 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
         const float s = kGroup ? 1.0f : scales[n];
-        const float zc = zt.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * zt.apply(acc[i][j][r] * kUnscale, zc, m);
+                if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
             }
         }
     }
@@ -461,7 +465,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     using T = WideTile<kNT>;
     constexpr int kStages = kDepth + 1;  // x (LDS) and code (register) stages
     constexpr int kMT = T::BM / 32;
-    constexpr bool kSplit = B >= 10;
+    constexpr bool kAsym = ZP::kAsym;
+    constexpr bool kSplit = split_codes<B, kAsym>();
     constexpr int kCopyInstr = T::BM / 32;  // 16-byte x pieces per thread per step
     __shared__ __attribute__((aligned(16))) uint4 As[kStages][T::kPieces];
 
@@ -500,10 +505,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const int64_t nrows = N - n0 < T::BN ? N - n0 : T::BN;
     const BufRef wbuf = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
     uint32_t woff[kNT];
+    int32_t zr[kNT];  // zero point of this lane's weight row in each column tile
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
         const int64_t nl = wave * 32 * kNT + j * 32 + c;
         woff[j] = (uint32_t)((nl < nrows ? nl : nrows - 1) * row_words * 4 + h * B * 4);
+        zr[j] = zp.zero(n0 + (nl < nrows ? nl : nrows - 1));
     }
     int abase[4];
 #pragma unroll
@@ -592,9 +599,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 if (t < 3)
-                    expand8<B>(w[st][j], t + 1, nh[j], nl[j]);
+                    expand8z<B, kAsym>(w[st][j], zr[j], t + 1, nh[j], nl[j]);
                 else
-                    expand8<B>(w[s1][j], 0, nh[j], nl[j]);
+                    expand8z<B, kAsym>(w[s1][j], zr[j], 0, nh[j], nl[j]);
             }
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
@@ -630,7 +637,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     __syncthreads();
     read_a(std::integral_constant<int, 0>{}, 0, a[0]);
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) expand8<B>(w[0][j], 0, bh[j], bl[j]);
+    for (int j = 0; j < kNT; ++j) expand8z<B, kAsym>(w[0][j], zr[j], 0, bh[j], bl[j]);
     int64_t ks = 0;
     for (; ks + kStages <= nk; ks += kStages) {
         step(std::integral_constant<int, 0>{}, ks);
@@ -654,9 +661,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     // offset is a scalar (the same for every lane), so no per-store address
     // arithmetic runs on the vector units; the tile's 256 rows of y must span
     // less than 4 GiB (N < 2^22), else the checked stores below serve.
-    constexpr float kUnscale = 1.0f / expand8_scale<B>();
-    // the x staging buffer is free now: the tile's activation sums go there
-    const auto zt = stage_tile_zero_points(zp, reinterpret_cast<float*>(&As[0][0]), m0, M, T::BM);
+    constexpr float kUnscale = 1.0f / expand8_scale<B, kAsym>();
     if (m0 + T::BM <= M && n0 + T::BN <= N && (int64_t)T::BM * N * 4 <= 0xffffffffLL) {
         const BufRef yb = uniform_buf(y + m0 * N, (uint32_t)(T::BM * N * 4));
         const uint32_t row4 = (uint32_t)(N * 4);
@@ -664,16 +669,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
             const float s = scales[n];
-            const float zc = zt.template coef<B>(n);
             const uint32_t voff = (uint32_t)(4 * h) * row4 + (uint32_t)n * 4;
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    buf_store_f32_nt(yb,
-                                     s * zt.apply(acc[i][j][r] * kUnscale, zc,
-                                                  m0 + i * 32 + 4 * h + 8 * (r >> 2) + (r & 3)),
-                                     voff,
+                    buf_store_f32_nt(yb, s * (acc[i][j][r] * kUnscale), voff,
                                      (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * row4);
         }
         return;
@@ -683,13 +684,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
         const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
         if (n >= N) continue;
         const float s = scales[n];
-        const float zc = zt.template coef<B>(n);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) y[m * N + n] = s * zt.apply(acc[i][j][r] * kUnscale, zc, m);
+                if (m < M) y[m * N + n] = s * (acc[i][j][r] * kUnscale);
             }
         }
     }
@@ -936,10 +936,10 @@ hipError_t launch_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packe
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
-                       const float* xsum, hipStream_t stream)
+                       hipStream_t stream)
 {
     if (zeros) {
-        const ZeroPoints zp{zeros, xsum};
+        const ZeroPoints zp{zeros};
 #define CALL(B) launch_gemm_b<B>(x, M, packed, scales, N, K, y, zp, stream)
         DQ_BITS_SWITCH(bits, CALL)
 #undef CALL

@@ -24,9 +24,14 @@ __device__ __forceinline__ bf16x8_t bf16x8_from_words(uint32_t a, uint32_t b, ui
 __device__ __forceinline__ float sbyte_f(uint32_t w, int j) { return (float)(int8_t)(w >> (8 * j)); }
 
 // Factor by which expand8<B> scales the codes (converted from the top bits of a
-// byte): 16 for B = 4, else 1.  The GEMM divides its sums by it.
-template <int B>
-__host__ __device__ constexpr float expand8_scale() { return B == 4 ? 16.0f : 1.0f; }
+// byte): 16 for symmetric B = 4, else 1.  The kernels divide their sums by it.
+template <int B, bool kAsym = false>
+__host__ __device__ constexpr float expand8_scale() { return (!kAsym && B == 4) ? 16.0f : 1.0f; }
+
+// Whether a code needs two bf16 operands: symmetric |q| <= 2^(B-1) - 1 is exact
+// in bf16 up to B = 9, asymmetric |u - z| <= 2^B - 1 up to B = 8.
+template <int B, bool kAsym>
+__host__ __device__ constexpr bool split_codes() { return kAsym ? B >= 9 : B >= 10; }
 
 // Codes 8t .. 8t+7 of a chunk (raw words w) as exact bf16: for B <= 9 one
 // operand (q, or 16q for B = 4); for B >= 10 two operands, bf16(q & ~63) =
@@ -71,6 +76,46 @@ __device__ __forceinline__ void expand8(const uint32_t (&w)[B], int t, bf16x8_t&
                                    bf16x2_bits((float)(q[6] & 63), (float)(q[7] & 63)));
         }
     }
+}
+
+// Asymmetric codes: q = u - z for codes 8t .. 8t+7 of a chunk (raw unsigned
+// words w), |q| <= 2^B - 1.  B <= 8: one exact operand.  B >= 9: with
+// S = B - 8, bf16(q & ~(2^S - 1)) = bf16(2^S * (q >> S)), q >> S in
+// [-256, 255], and bf16(q & (2^S - 1)) in [0, 127]; both exact, summing to q.
+template <int B>
+__device__ __forceinline__ void expand8_asym(const uint32_t (&w)[B], int32_t z, int t, bf16x8_t& hi,
+                                             bf16x8_t& lo)
+{
+    int32_t q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = (int32_t)chunk_code_unsigned<B>(w, 8 * t + e) - z;
+    if constexpr (B <= 8) {
+        hi = bf16x8_from_words(bf16x2_bits((float)q[0], (float)q[1]),
+                               bf16x2_bits((float)q[2], (float)q[3]),
+                               bf16x2_bits((float)q[4], (float)q[5]),
+                               bf16x2_bits((float)q[6], (float)q[7]));
+    } else {
+        constexpr int32_t kLo = (1 << (B - 8)) - 1;
+        hi = bf16x8_from_words(bf16x2_bits((float)(q[0] & ~kLo), (float)(q[1] & ~kLo)),
+                               bf16x2_bits((float)(q[2] & ~kLo), (float)(q[3] & ~kLo)),
+                               bf16x2_bits((float)(q[4] & ~kLo), (float)(q[5] & ~kLo)),
+                               bf16x2_bits((float)(q[6] & ~kLo), (float)(q[7] & ~kLo)));
+        lo = bf16x8_from_words(bf16x2_bits((float)(q[0] & kLo), (float)(q[1] & kLo)),
+                               bf16x2_bits((float)(q[2] & kLo), (float)(q[3] & kLo)),
+                               bf16x2_bits((float)(q[4] & kLo), (float)(q[5] & kLo)),
+                               bf16x2_bits((float)(q[6] & kLo), (float)(q[7] & kLo)));
+    }
+}
+
+// expand8 for either scheme: z is the row's zero point (ignored when symmetric).
+template <int B, bool kAsym>
+__device__ __forceinline__ void expand8z(const uint32_t (&w)[B], int32_t z, int t, bf16x8_t& hi,
+                                         bf16x8_t& lo)
+{
+    if constexpr (kAsym)
+        expand8_asym<B>(w, z, t, hi, lo);
+    else
+        expand8<B>(w, t, hi, lo);
 }
 
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));

@@ -211,6 +211,55 @@ __device__ __forceinline__ void chunk_fma(const uint32_t (&w)[B], const uint32_t
     }
 }
 
+// Asymmetric codes (q = u - z, |q| <= 2^B - 1), same contract as chunk_dot
+// (no pre-shift): B <= 8 as exact bf16 pairs through v_dot2c_f32_bf16; B >= 9
+// as fp32 FMAs on x widened exactly (x has 8 significant bits and q at most
+// 15, so every product is exact in fp32).  Codes are extracted unsigned and
+// the zero point subtracted in fp32 (both are integers below 2^15: exact).
+template <int B, int MT>
+__device__ __forceinline__ void chunk_dot_asym(const uint32_t (&w)[B], int32_t z,
+                                               const uint32_t (&xw)[MT][16], float (&acc)[MT])
+{
+    const float zf = (float)z;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const float q0 = (float)chunk_code_unsigned<B>(w, 2 * p) - zf;
+        const float q1 = (float)chunk_code_unsigned<B>(w, 2 * p + 1) - zf;
+        if constexpr (B <= 8) {
+            const bf16x2_t q = bf16_pair(q0, q1);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = dot2(q, xw[m][p], acc[m]);
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                acc[m] = fmaf(__uint_as_float(xw[m][p] << 16), q0, acc[m]);
+                acc[m] = fmaf(__uint_as_float(xw[m][p] & 0xffff0000u), q1, acc[m]);
+            }
+        }
+    }
+}
+
+// acc[m] += (scaled) sum over one chunk of x[m][j] * q[j] for either scheme; z
+// is the row's zero point (ignored when symmetric).  product_unscale undoes
+// the pre-shift of the symmetric byte paths.
+template <int B, int MT, bool kAsym>
+__device__ __forceinline__ void chunk_product(const uint32_t (&w)[B], int32_t z,
+                                              const uint32_t (&xw)[MT][16], float (&acc)[MT])
+{
+    if constexpr (kAsym)
+        chunk_dot_asym<B, MT>(w, z, xw, acc);
+    else if constexpr (B <= 9)
+        chunk_dot<B, MT>(w, xw, acc);
+    else
+        chunk_fma<B, MT>(w, xw, acc);
+}
+
+template <int B, bool kAsym>
+__host__ __device__ constexpr float product_unscale()
+{
+    return (kAsym || B > 9) ? 1.0f : 1.0f / (float)(1 << chunk_dot_shift<B>());
+}
+
 template <int B, int MT, int kRows, int kWaves, bool kAligned, class ZP>
 __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
@@ -238,6 +287,9 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
         rowp_[r] = packed + n * row_words;
     }
     const uint32_t* const(&rowp)[kRows] = rowp_;
+    int32_t zr[kRows];  // zero points of the wave's rows (asymmetric codes)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) zr[r] = zp.zero(n0 + r < N ? n0 + r : N - 1);
 
     // x staging: thread t moves kXPerThread elements of each x row per slice
     const int xc = tid * kXPerThread / kChunk;                 // chunk within the slice
@@ -306,12 +358,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
                 }
             }
 #pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                if constexpr (B <= 9)
-                    chunk_dot<B, MT>(w[r], xw, acc[r]);
-                else
-                    chunk_fma<B, MT>(w[r], xw, acc[r]);
-            }
+            for (int r = 0; r < kRows; ++r) chunk_product<B, MT, ZP::kAsym>(w[r], zr[r], xw, acc[r]);
         }
     };
     uint4 xnxt[MT];
@@ -367,16 +414,15 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_lds_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
     if (lane == 0) {
-        constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
+        constexpr float kUnscale = product_unscale<B, ZP::kAsym>();
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int64_t n = n0 + r;
             if (n < N) {
                 const float s = scales[n];
-                const float zc = zp.template coef<B>(n);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    if (m < M) y[(int64_t)m * N + n] = s * zp.apply(acc[r][m] * kUnscale, zc, m);
+                    if (m < M) y[(int64_t)m * N + n] = s * (acc[r][m] * kUnscale);
             }
         }
     }
@@ -412,7 +458,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
 {
     typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
     typedef float f32x4m_t __attribute__((ext_vector_type(4)));
-    constexpr bool kSplit = B >= 10;
+    constexpr bool kSplit = split_codes<B, ZP::kAsym>();
     constexpr int kStages = kDepth + 1;
     static_assert(kDepth >= 1 && kDepth <= 3, "one to three steps ahead");
     __shared__ float red[kGemvMfmaWaves - 1][kNT][4][kWave];
@@ -424,10 +470,12 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     const int g = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * kNT;
     const uint32_t* rowp[kNT];
+    int32_t zr[kNT];  // zero point of this lane's row in each row tile
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
         const int64_t n = n0 + 16 * j + c;
         rowp[j] = packed + (n < N ? n : N - 1) * row_words;
+        zr[j] = zp.zero(n < N ? n : N - 1);
     }
     const int64_t nchunks = ceil_div(K, kChunk);
     const int64_t nsteps = ceil_div(nchunks, 4);
@@ -480,7 +528,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 bf16x8_t bh, bl;
-                expand8<B>(w[p][j], t, bh, bl);
+                expand8z<B, ZP::kAsym>(w[p][j], zr[j], t, bh, bl);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
                 if constexpr (kSplit) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
             }
@@ -520,20 +568,19 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-        constexpr float kUnscale = 1.0f / expand8_scale<B>();
+        constexpr float kUnscale = 1.0f / expand8_scale<B, ZP::kAsym>();
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + 16 * j + c;
             if (n >= N) continue;
             const float s = scales[n];
-            const float zc = zp.template coef<B>(n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = acc[j][r];
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * zp.apply(v * kUnscale, zc, m);
+                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
             }
         }
     }
@@ -569,15 +616,18 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 {
     typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
     typedef float f32x4m_t __attribute__((ext_vector_type(4)));
-    constexpr bool kSplit = B >= 10;
+    constexpr bool kSplit = split_codes<B, ZP::kAsym>();
     constexpr int kStages = kDepth + 1;
     constexpr int kXCopies = kMR / 4;
     constexpr int kCodeSlots = (16 * kNT * B + 63) / 64 * 64;  // 16-byte code pieces of one step
     constexpr int kCodeCopies = kCodeSlots / 64;
     // group-wise scales (groups of whole 128-code steps): each step's scales of
-    // the tile's rows come into LDS with the step's codes, one more copy
+    // this lane's rows come into registers with the step's codes (kNT more
+    // loads).  Not through the LDS ring: the fold that reads them is plain
+    // arithmetic the compiler may sink past the next step's copies, and a copy
+    // into a slot whose read is still in flight would race with it.
     constexpr bool kGroup = is_group_scales<ZP>::value;
-    constexpr int kPerStage = kCodeCopies + kXCopies + (kGroup ? 1 : 0);
+    constexpr int kPerStage = kCodeCopies + kXCopies + (kGroup ? kNT : 0);
     constexpr int kSlots = kMR * 16;  // 16-byte x pieces of one step
     static_assert(kDepth >= 1 && kDepth <= 2, "one or two steps ahead");
     static_assert(kMR == 8 || kMR == 16, "x rows staged: 8 or 16");
@@ -591,7 +641,6 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     __shared__ __attribute__((aligned(16))) uint4 cs0[kGemvMfmaWaves][kCodeSlots];
     __shared__ __attribute__((aligned(16))) uint4 cs1[kGemvMfmaWaves][kCodeSlots];
     __shared__ __attribute__((aligned(16))) uint4 cs2[kStages > 2 ? kGemvMfmaWaves : 1][kStages > 2 ? kCodeSlots : 1];
-    __shared__ float ss[kGroup ? kStages : 1][kGroup ? kGemvMfmaWaves : 1][kGroup ? kWave : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -647,18 +696,26 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
         const int r = sl / B, pc = sl % B;
         cbase[q] = r < 16 * kNT ? (uint32_t)(r * row_words * 4 + pc * 16) : kOutside;
     }
+    int32_t zr[kNT];  // zero point of this lane's row in each row tile
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) zr[j] = zp.zero(n0 + 16 * j + c < N ? n0 + 16 * j + c : N - 1);
     [[maybe_unused]] BufRef sb{};
-    [[maybe_unused]] int64_t steps_per_group = 1;
+    [[maybe_unused]] int gshift = 0;  // log2 of the 128-code steps per group
     if constexpr (kGroup) {
         sb = uniform_buf(zp.scales + n0 * zp.G, (uint32_t)(nrows * zp.G * 4));
-        steps_per_group = zp.group / 128;
+        gshift = __builtin_ctzll((unsigned long long)(zp.group / 128));
     }
+    float gsc[kGroup ? kStages : 1][kGroup ? kNT : 1];  // group scales by stage
     auto load = [&](auto P, int64_t ks) {
-        if constexpr (kGroup) {  // lane r < 16 kNT: the scale of row r for step ks's group
-            const int64_t gi = ks / steps_per_group;
-            const bool in = lane < 16 * kNT && lane < nrows && gi < zp.G;
-            buf_load_lds4(sb, &ss[kGroup ? decltype(P)::value : 0][kGroup ? wave : 0][0],
-                          in ? (uint32_t)((lane * zp.G + gi) * 4) : kOutside, 0u);
+        if constexpr (kGroup) {  // the scale of row 16 j + c for step ks's group
+            const int64_t gi = ks >> gshift;
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                const bool in = 16 * j + c < nrows && gi < zp.G;
+                uint32_t t[1];
+                buf_load_words<1>(sb, in ? (uint32_t)(((16 * j + c) * zp.G + gi) * 4) : kOutside, 0u, t);
+                gsc[kGroup ? decltype(P)::value : 0][kGroup ? j : 0] = __uint_as_float(t[0]);
+            }
         }
         uint4* cdst = cring(P);
 #pragma unroll
@@ -695,7 +752,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 bf16x8_t bh, bl;
-                expand8<B>(wl[j], t, bh, bl);
+                expand8z<B, ZP::kAsym>(wl[j], zr[j], t, bh, bl);
                 f32x4m_t& d = kGroup ? part[j] : acc[j];
                 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, d, 0, 0, 0);
                 if constexpr (kSplit) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, d, 0, 0, 0);
@@ -704,7 +761,7 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
         if constexpr (kGroup) {
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
-                const float sg = ss[kGroup ? decltype(P)::value : 0][kGroup ? wave : 0][16 * j + c];
+                const float sg = gsc[kGroup ? decltype(P)::value : 0][kGroup ? j : 0];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sg, part[j][r], acc[j][r]);
             }
@@ -750,20 +807,19 @@ __global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_xlds_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-        constexpr float kUnscale = 1.0f / expand8_scale<B>();
+        constexpr float kUnscale = 1.0f / expand8_scale<B, ZP::kAsym>();
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
             const int64_t n = n0 + 16 * j + c;
             if (n >= N) continue;
             const float s = kGroup ? 1.0f : scales[n];
-            const float zc = zp.template coef<B>(n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = acc[j][r];
 #pragma unroll
                 for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red[q][j][r][lane];
                 const int m = 4 * g + r;
-                if (m < M) y[(int64_t)m * N + n] = s * zp.apply(v * kUnscale, zc, m);
+                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
             }
         }
     }
@@ -839,7 +895,8 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     // kRW rows per wave (1 or 2): their chunks form one stream of kRW * nchunks
     // chunks, so a row whose chunk count fills its last 64-chunk slice poorly
     // shares that slice with the next row
-    static_assert(kRW == 1 || (kRW == 2 && !is_group_scales<ZP>::value), "two rows: per-row scales");
+    static_assert(kRW == 1 || (kRW == 2 && !is_group_scales<ZP>::value && !ZP::kAsym),
+                  "two rows: symmetric per-row scales");
     const int64_t n = ((int64_t)blockIdx.x * kWaves + wave) * kRW;
     const int64_t nchunks = K / kChunk;
     const int64_t tchunks = kRW * nchunks;
@@ -848,6 +905,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
     const BufRef wbuf = uniform_buf(packed + (n < N ? n : N - 1) * row_words,
                                     (uint32_t)(wrows * row_words * 4));
     const BufRef xall = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+    const int32_t z = zp.zero(n < N ? n : N - 1);  // the row's zero point (asymmetric codes)
 
     // x piece p (8 elements) = piece p % 4 of chunk slot p / 4 (slot = m * nchunks + chunk)
     const int pieces = (int)(MT * nchunks * 4);
@@ -922,10 +980,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
                 float part[MT];
 #pragma unroll
                 for (int m = 0; m < MT; ++m) part[m] = 0.0f;
-                if constexpr (B <= 9)
-                    chunk_dot<B, MT>(w[st], xw, part);
-                else
-                    chunk_fma<B, MT>(w[st], xw, part);
+                chunk_product<B, MT, false>(w[st], 0, xw, part);
                 const float sg = __uint_as_float(gsc[st]);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) acc[m] = fmaf(part[m], sg, acc[m]);
@@ -933,19 +988,14 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
                 float part[MT];
 #pragma unroll
                 for (int m = 0; m < MT; ++m) part[m] = 0.0f;
-                if constexpr (B <= 9)
-                    chunk_dot<B, MT>(w[st], xw, part);
-                else
-                    chunk_fma<B, MT>(w[st], xw, part);
+                chunk_product<B, MT, false>(w[st], 0, xw, part);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     acc[m] += r ? 0.0f : part[m];
                     acc2[kRW == 2 ? m : 0] += r ? part[m] : 0.0f;
                 }
-            } else if constexpr (B <= 9) {
-                chunk_dot<B, MT>(w[st], xw, acc);
             } else {
-                chunk_fma<B, MT>(w[st], xw, acc);
+                chunk_product<B, MT, ZP::kAsym>(w[st], z, xw, acc);
             }
         }
     };
@@ -965,20 +1015,17 @@ __global__ __launch_bounds__(kWaves * kWave) void gemv_xres_kernel(
         for (int m = 0; m < MT; ++m) acc2[m] = wave_sum(acc2[m]);
     }
     if (lane == 0 && n < N) {
-        constexpr float kUnscale = 1.0f / (float)(1 << (B <= 9 ? chunk_dot_shift<B>() : 0));
+        constexpr float kUnscale = product_unscale<B, ZP::kAsym>();
         const float s = kGroup ? 1.0f : scales[n];
-        const float zc = zp.template coef<B>(n);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            if (m < M) y[(int64_t)m * N + n] = s * zp.apply(acc[m] * kUnscale, zc, m);
+            if (m < M) y[(int64_t)m * N + n] = s * (acc[m] * kUnscale);
         if constexpr (kRW == 2) {
             if (n + 1 < N) {
                 const float s2 = scales[n + 1];
-                const float zc2 = zp.template coef<B>(n + 1);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    if (m < M)
-                        y[(int64_t)m * N + n + 1] = s2 * zp.apply(acc2[m] * kUnscale, zc2, m);
+                    if (m < M) y[(int64_t)m * N + n + 1] = s2 * (acc2[m] * kUnscale);
             }
         }
     }
@@ -1181,10 +1228,10 @@ hipError_t launch_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packe
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
-                       const float* xsum, hipStream_t stream)
+                       hipStream_t stream)
 {
     if (zeros) {
-        const ZeroPoints zp{zeros, xsum};
+        const ZeroPoints zp{zeros};
 #define CALL(B) launch_gemv_b<B>(x, M, packed, scales, N, K, y, zp, stream)
         DQ_BITS_SWITCH(bits, CALL)
 #undef CALL

@@ -10,8 +10,10 @@
 
 namespace dq {
 
+// nonfinite: optional count of rows holding a NaN or an infinity (zeroed first)
 hipError_t launch_quantize_pack(const void* w, bool bf16, int64_t N, int64_t K, int bits,
-                                uint32_t* packed, float* scales, hipStream_t stream);
+                                uint32_t* packed, float* scales, uint32_t* nonfinite,
+                                hipStream_t stream);
 hipError_t launch_quantize_pack_sumsq(const void* w, bool bf16, int64_t N, int64_t K, int bits,
                                       uint32_t* packed, float* scales, double* row_sumsq,
                                       double* matrix_sumsq, hipStream_t stream);
@@ -31,18 +33,17 @@ hipError_t launch_gemv_group(const uint16_t* x, int64_t M, const uint32_t* packe
 hipError_t launch_gemm_group(const uint16_t* x, int64_t M, const uint32_t* packed,
                              const float* scales, int64_t N, int64_t K, int bits, int64_t group,
                              float* y, hipStream_t stream);
-// zeros / xsum: the asymmetric scheme's zero points [N] and sum_k x[m, k]
-// [M]; both null for the symmetric scheme.
+// zeros: the asymmetric scheme's zero points [N] (q = u - zeros[n]); null for
+// the symmetric scheme (q = u - 2^(b-1)).
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
-                       const float* xsum, hipStream_t stream);
+                       hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
-                       const float* xsum, hipStream_t stream);
+                       hipStream_t stream);
 hipError_t launch_quantize_pack_asym(const void* w, bool bf16, int64_t N, int64_t K, int bits,
                                      uint32_t* packed, float* scales, int32_t* zeros,
                                      hipStream_t stream);
-hipError_t launch_x_sum(const uint16_t* x, int64_t M, int64_t K, float* xsum, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int64_t nparts,
                               hipStream_t stream);
 

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("dq_packed_row_bytes", "dq_quantize_pack", "dq_unpack", "dq_gemv", "dq_gemm",
                  "dq_status_string", "dq_last_error", "dq_quantize_pack_sumsq", "dq_sensitivity",
-                 "dq_row_sumsq", "dq_quantize_pack_asym", "dq_unpack_asym", "dq_x_sum",
+                 "dq_row_sumsq", "dq_quantize_pack_asym", "dq_unpack_asym",
                  "dq_gemv_asym", "dq_gemm_asym", "dq_quantize_pack_group", "dq_unpack_group",
                  "dq_gemv_group", "dq_gemm_group", "dq_file_write", "dq_file_open", "dq_file_count",
                  "dq_file_matrix_info", "dq_file_verify", "dq_file_load", "dq_file_close",
@@ -111,6 +111,7 @@ def test_alignment_rejected():
     assert dq.dq_quantize_pack(MIS, dq.DQ_F32, 4, 64, 6, A, A) == dq.DQ_ERR_ALIGN
     assert dq.dq_quantize_pack(A, dq.DQ_F32, 4, 64, 6, MIS, A) == dq.DQ_ERR_ALIGN
     assert dq.dq_quantize_pack(A, dq.DQ_F32, 4, 64, 6, A, A + 2) == dq.DQ_ERR_ALIGN
+    assert dq.dq_quantize_pack(A, dq.DQ_F32, 4, 64, 6, A, A, A + 2) == dq.DQ_ERR_ALIGN
     assert dq.dq_unpack(MIS, A, 4, 64, 6, A, 0) == dq.DQ_ERR_ALIGN
     assert dq.dq_unpack(A, A, 4, 64, 6, A + 1, 0) == dq.DQ_ERR_ALIGN
     for fn in (dq.dq_gemv, dq.dq_gemm):
@@ -175,18 +176,13 @@ def test_asym_arguments_rejected():
     assert u(A, A, 0, 4, 64, 6, A, 0) == dq.DQ_ERR_NULL
     assert u(A, 0, A, 4, 64, 6, 0, A) == dq.DQ_ERR_NULL  # w_out needs scales
     assert u(A, A, A + 1, 4, 64, 6, A, 0) == dq.DQ_ERR_ALIGN
-    x = dq.dq_x_sum
-    assert x(0, 1, 64, A) == dq.DQ_ERR_NULL
-    assert x(A, 0, 64, A) == dq.DQ_ERR_SHAPE
-    assert x(A, 1, (1 << 22) + 1, A) == dq.DQ_ERR_SHAPE
-    assert x(MIS, 1, 64, A) == dq.DQ_ERR_ALIGN
     for fn, bad_m in ((dq.dq_gemv_asym, 17), (dq.dq_gemm_asym, 0)):
-        assert fn(A, 1, A, A, 0, A, 4, 64, 6, A) == dq.DQ_ERR_NULL
-        assert fn(A, 1, A, A, A, 0, 4, 64, 6, A) == dq.DQ_ERR_NULL
-        assert fn(A, bad_m, A, A, A, A, 4, 64, 6, A) == dq.DQ_ERR_SHAPE
-        assert fn(A, 1, A, A, A, A, 4, 64, 1, A) == dq.DQ_ERR_BITS
-        assert fn(A, 1, A, A, A + 2, A, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
-        assert fn(A, 1, A, A, A, A + 2, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, A, A, 0, 4, 64, 6, A) == dq.DQ_ERR_NULL
+        assert fn(A, 1, A, A, A, 4, 64, 6, 0) == dq.DQ_ERR_NULL
+        assert fn(A, bad_m, A, A, A, 4, 64, 6, A) == dq.DQ_ERR_SHAPE
+        assert fn(A, 1, A, A, A, 4, 64, 1, A) == dq.DQ_ERR_BITS
+        assert fn(A, 1, A, A, A + 2, 4, 64, 6, A) == dq.DQ_ERR_ALIGN
+        assert fn(A, 1, A, A, A, 4, 64, 6, A + 2) == dq.DQ_ERR_ALIGN
 
 
 @pytest.mark.parametrize("group", [0, 16, 31, 48, 96, 4096, -32])

@@ -1,10 +1,10 @@
 """Parity of the asymmetric (zero-point) variant with the oracle: quantize +
-pack and unpack bit-exact, the activation sums within their fp64-then-fp32
-rounding, GEMV / GEMM within 1e-4 * sum_k |x * w_hat| of the fp64 reference,
-one-hot activations exact, on rows shifted off zero, non-negative and
-non-positive rows and the special rows, through every product kernel (the
-resident-x and sliced GEMVs, the matrix-core GEMVs, the 128-row, wide and
-fallback GEMMs).
+pack and unpack bit-exact, GEMV / GEMM within 1e-4 * sum_k |x * w_hat| of the
+fp64 reference, one-hot activations exact, on rows shifted off zero,
+non-negative and non-positive rows, sparse rows (one non-zero, 90 % zeros,
+all zeros) with small activations at their non-zeros, and the special rows,
+through every product kernel (the resident-x and sliced GEMVs, the
+matrix-core GEMVs, the 128-row, wide and fallback GEMMs).
 
 Source: "量化" tutorial (aiknowledge.cn), "量化怎么工作" (a zero point added to
 the rounded quotient for distributions not centred on zero)."""
@@ -79,23 +79,52 @@ def test_unpack_asym_bitexact(bits):
         assert np.array_equal(f32_bits(w_hat), w_ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("M,K", [(1, 1), (3, 1000), (16, 4133), (2048, 8192)])
-def test_x_sum(M, K):
-    x = workload.activations(32, K, M, K)
-    report("x_sum M=%d K=%d" % (M, K))
-    got = dq.x_sum(bf16_gpu(x)).cpu().numpy().astype(np.float64)
-    xf = workload.bf16_to_f32(x).astype(np.float64)
-    exact = np.array([np.sum(xf[m]) for m in range(M)])  # every partial sum exact in fp64 here
-    mag = np.abs(xf).sum(axis=1)
-    assert (np.abs(got - exact) <= 2.0 ** -24 * np.abs(exact) + K * 2.0 ** -52 * mag).all()
+def sparse_weights(seed: int, N: int, K: int):
+    """Rows the zero point is for ("量化怎么工作": distributions not centred on
+    zero, such as non-negative ReLU outputs), made sparse, by row n % 5:
+    0 one positive element (z = 0, every other code 0), 1 non-negative with
+    90 % zeros, 2 non-positive with 90 % zeros (z = L), 3 all zeros, 4 one
+    negative element.  Returns (bf16 weights, the positions of the one-element
+    rows' non-zeros)."""
+    rng = np.random.default_rng(seed)
+    w = np.abs(workload.bf16_to_f32(workload.weights(35, seed, N, K, dtype="bf16")))
+    keep = rng.random((N, K)) < 0.1
+    keep[:, 0] = True  # at least one non-zero in the 90 %-zero rows
+    kind = np.arange(N) % 5
+    w[kind == 1] *= keep[kind == 1]
+    w[kind == 2] *= -keep[kind == 2].astype(np.float32)
+    w[kind == 3] = 0.0
+    pos = rng.integers(0, K, N)
+    for n in np.flatnonzero((kind == 0) | (kind == 4)):
+        v = w[n, pos[n]] + 0.01
+        w[n] = 0.0
+        w[n, pos[n]] = v if kind[n] == 0 else -v
+    return workload.bf16_from_f32(w.astype(np.float32)), pos[(kind == 0) | (kind == 4)]
 
 
-def assert_asym_product(kind: str, M: int, N: int, K: int, bits: int, seed: int):
-    w = shifted_weights(seed, N, K)
-    x = workload.activations(33, seed, M, K)
+def small_at(x: np.ndarray, cols: np.ndarray, seed: int) -> np.ndarray:
+    """x (bf16 bits) with the columns `cols` replaced by small values of either
+    sign, |x| in [0.005, 0.05], while the rest stays N(0, 1): the product is
+    then small next to sum_k |x_k|, which is where a fold through sum_k x loses
+    it."""
+    xf = workload.bf16_to_f32(x)
+    rng = np.random.default_rng(seed)
+    v = rng.uniform(0.005, 0.05, (x.shape[0], len(cols))) * rng.choice([-1.0, 1.0], (x.shape[0], len(cols)))
+    xf[:, cols] = v.astype(np.float32)
+    return workload.bf16_from_f32(xf)
+
+
+def assert_asym_product(kind: str, M: int, N: int, K: int, bits: int, seed: int,
+                        sparse: bool = False):
+    if sparse:
+        w, cols = sparse_weights(seed, N, K)
+        x = small_at(workload.activations(33, seed, M, K), cols, seed)
+    else:
+        w = shifted_weights(seed, N, K)
+        x = workload.activations(33, seed, M, K)
     o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
     y_ref, bound = oracle.matmul_asym(x, o_packed, o_scales, o_zeros, N, K, bits)
-    report("%s_asym M=%d N=%d K=%d bits=%d" % (kind, M, N, K, bits))
+    report("%s_asym M=%d N=%d K=%d bits=%d sparse=%d" % (kind, M, N, K, bits, sparse))
     P = torch().from_numpy(o_packed.view(np.int32)).cuda()
     S = torch().from_numpy(o_scales).cuda()
     Z = torch().from_numpy(o_zeros).cuda()
@@ -103,6 +132,9 @@ def assert_asym_product(kind: str, M: int, N: int, K: int, bits: int, seed: int)
     y = fn(bf16_gpu(x), P, S, Z, K, bits)
     torch().cuda.synchronize()
     y = y.cpu().numpy()
+    if sparse:  # the sparse rows really are the hard case: most codes equal z
+        assert (o_zeros[1::5] == 0).all() and (o_zeros[2::5] == (1 << bits) - 1).all()
+        assert (bound[:, 3::5] == 0).all()
     ok = within_tolerance(y, y_ref, bound)
     if not ok.all():
         m, n = np.argwhere(~ok)[0]
@@ -115,6 +147,28 @@ def test_gemv_asym_parity(bits):
     for M in (1, 2, 3, 8, 16):
         for i, (N, K) in enumerate(GEMV_SHAPES):
             assert_asym_product("gemv", M, N, K, bits, seed=bits * 1000 + M * 10 + i)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemv_asym_sparse_rows(bits):
+    """Sparse non-negative, non-positive and all-zero rows with small
+    activations at the non-zero weights, through every GEMV kernel (M <= 2:
+    resident-x and sliced; 3 <= M <= 16: matrix-core, codes through LDS or
+    registers)."""
+    for M in (1, 2, 3, 8, 16):
+        for i, (N, K) in enumerate(GEMV_SHAPES + [(45, 4096)]):
+            assert_asym_product("gemv", M, N, K, bits, seed=bits * 1000 + M * 10 + i + 70000,
+                                sparse=True)
+
+
+@pytest.mark.parametrize("bits", range(2, 16))
+def test_gemm_asym_sparse_rows(bits):
+    """The sparse rows through every GEMM kernel: the LDS-staged fallback
+    (K % 64 != 0), the 128-row pipelined kernel and the 256 x 256 and
+    256 x 128 wide kernels."""
+    shapes = GEMM_SHAPES + [(2000, 8100, 448), (300, 30000, 448)]
+    for i, (M, N, K) in enumerate(shapes):
+        assert_asym_product("gemm", M, N, K, bits, seed=bits * 1000 + 500 + i + 70000, sparse=True)
 
 
 @pytest.mark.parametrize("bits", range(2, 16))
@@ -143,8 +197,8 @@ def test_gemm_asym_wide_tiles(bits):
 @pytest.mark.parametrize("kind", ["gemv", "gemm"])
 @pytest.mark.parametrize("bits", [2, 6, 9, 10, 15])
 def test_asym_one_hot_is_exact(kind, bits):
-    """x = e_k: the kernels' sum is u - 2^(b-1) exactly and the zero-point term
-    (2^(b-1) - z) * 1 makes it u - z exactly, so y[k, n] = fl32(s[n] (u - z))."""
+    """x = e_k: the kernels' sum is the one product 1 * (u - z), exact, so
+    y[k, n] = fl32(s[n] (u - z))."""
     N, K = 70, 16 if kind == "gemv" else 40
     w = shifted_weights(bits + 900, N, K)
     o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
@@ -163,15 +217,14 @@ def test_asym_one_hot_is_exact(kind, bits):
 
 
 def test_quantize_asym_then_products_end_to_end():
-    """GPU quantize -> GPU x_sum -> GPU GEMV and GEMM, against the oracle's flow."""
+    """GPU quantize -> GPU GEMV and GEMM, against the oracle's flow."""
     N, K, bits = 640, 2048, 5
     w = shifted_weights(4242, N, K)
     P, S, Z = dq.quantize_pack_asym(weights_gpu(w), bits)
     x = workload.activations(34, 1, 300, K)
     X = bf16_gpu(x)
-    xs = dq.x_sum(X)
-    yv = dq.gemv_asym(X[:4], P, S, Z, K, bits, xsum=xs[:4])
-    yg = dq.gemm_asym(X, P, S, Z, K, bits, xsum=xs)
+    yv = dq.gemv_asym(X[:4], P, S, Z, K, bits)
+    yg = dq.gemm_asym(X, P, S, Z, K, bits)
     torch().cuda.synchronize()
     o_packed, o_scales, o_zeros, _ = oracle.quantize_pack_asym(w, bits)
     y_ref, bound = oracle.matmul_asym(x, o_packed, o_scales, o_zeros, N, K, bits)

@@ -271,3 +271,30 @@ def test_gemv_two_rows_per_wave(bits):
     for M in (1, 2):
         for i, (N, K) in enumerate(TWO_ROW_SHAPES):
             assert_matmul_parity("gemv", M, N, K, bits, seed=bits * 2000 + M * 10 + i)
+
+
+@pytest.mark.parametrize("bits", [2, 6, 15])
+def test_nonfinite_rows_counted(bits):
+    """dq_quantize_pack's optional output counts the rows holding a NaN or an
+    infinity (the rows whose scale is NaN), counting from zero on every call;
+    the codes and scales are those of the call without it."""
+    rng = np.random.default_rng(bits)
+    cases = []
+    for N, K in ((10, 33), (300, 4096), (7, 1), (1000, 96)):
+        w = workload.weights(36, N + K, N, K, dtype="f32")
+        hit = rng.random(N) < 0.2
+        for n in np.flatnonzero(hit):
+            w[n, rng.integers(0, K)] = rng.choice([np.nan, np.inf, -np.inf])
+        cases.append(w)
+    cases.append(special_rows(300, bits))
+    cases.append(np.zeros((5, 64), np.float32))
+    nf = torch().zeros(1, dtype=torch().int32, device="cuda")
+    for w in cases:
+        want = int((~np.isfinite(w)).any(axis=1).sum())
+        report("nonfinite_rows shape=%s bits=%d want=%d" % (w.shape, bits, want))
+        P, S = dq.quantize_pack(weights_gpu(w), bits, nonfinite=nf)
+        P0, S0 = dq.quantize_pack(weights_gpu(w), bits)
+        torch().cuda.synchronize()
+        assert int(nf.item()) == want
+        assert int(np.isnan(S.cpu().numpy()).sum()) == want
+        assert np.array_equal(u32(P), u32(P0)) and np.array_equal(f32_bits(S), f32_bits(S0))
