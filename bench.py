@@ -24,6 +24,7 @@ decode matrices, timed on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -68,7 +69,7 @@ def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_dq_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f in ("gemv.hip", "common.hpp"):
+        if f in ("gemv_batch.hip", "gemv_kernels.hpp", "gemm_tiles.hpp", "common.hpp"):
             # code only: whole-line comments do not change the kernel
             for line in open(os.path.join(csrc, f), "rb"):
                 if not line.lstrip().startswith(b"//"):
@@ -77,8 +78,8 @@ def kernel_source_digest() -> str:
 
 
 def recorded_traffic():
-    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary,
-    if it was taken on the current GEMV source; else None."""
+    """HBM bytes per batched decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current source of that kernel; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -136,10 +137,54 @@ def stack_context(torch, dq, workload, dev, stream):
         ms = float(np.median(ts))
         out["m%d" % M] = {"ms_per_pass": round(ms, 3), "gbs": round(total / (ms * 1e-3) / 1e9, 1),
                           "frac_of_hbm_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del packs
+    # batched: one dq_gemv_batched per layer (its 7 matrices), and one per
+    # group of matrices a layer can multiply at once (q/k/v on one activation,
+    # o, gate/up on one activation, down); every item its own output
+    per_layer = 7
+    yl = {M: [torch.empty((M, N), dtype=torch.float32, device=dev) for N, _ in shapes[:per_layer]]
+          for M in (1, 8)}
+    groupings = {"layer": [list(range(per_layer))], "dependency_groups": [[0, 1, 2], [3], [4, 5], [6]]}
+    keep = []
+    for M in (1, 8):
+        for gname, groups in groupings.items():
+            calls = []
+            for l0 in range(0, len(packs), per_layer):
+                for grp in groups:
+                    arr = (dq.DQGemvItem * len(grp))()
+                    for i, j in enumerate(grp):
+                        P, S, K, b, N = packs[l0 + j]
+                        arr[i] = dq.DQGemvItem(xs[K].data_ptr(), P.data_ptr(), S.data_ptr(),
+                                               yl[M][j].data_ptr(), N, K, b)
+                    keep.append(arr)
+                    calls.append((ctypes.addressof(arr), len(grp), M, stream.cuda_stream))
+
+            def one_pass(calls=calls):
+                for a in calls:
+                    if lib.dq_gemv_batched(*a):
+                        raise RuntimeError("dq_gemv_batched failed")
+            one_pass()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                one_pass()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = float(np.median(ts))
+            out["m%d_batched_per_%s" % (M, gname)] = {
+                "ms_per_pass": round(ms, 3), "launches_per_pass": len(calls),
+                "gbs": round(total / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del packs, keep
     out["packed_gb"] = round(total / 1e9, 3)
     out["what"] = ("decode GEMV over the 448-matrix layer stack (17.8 GB packed, mostly 6-bit), "
-                   "every matrix in layer order per pass; packed-weight GB/s; context, not the value")
+                   "every matrix in layer order per pass: m1/m8 one dq_gemv launch per matrix; "
+                   "*_batched_per_layer one dq_gemv_batched launch per layer (7 matrices); "
+                   "*_batched_per_dependency_groups one per group a layer multiplies at once "
+                   "(q/k/v, o, gate/up, down: 4 per layer); packed-weight GB/s; context, not "
+                   "the value")
     return out, sumsq
 
 
@@ -392,12 +437,15 @@ def row_sumsq_context(torch, dq, stream, mats, reps: int):
             "bytes": "N*K*2 read + N*8 written per matrix"}
 
 
-def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: int):
+def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: int,
+                    per_matrix_group=None, per_matrix_launches: int = 0):
     """Context for the GEMV figure, outside the timed steps: the decode GEMV
-    launches of a step against a plain streaming read (dq_stream_read) of the
-    same packed buffers in the same order, each group timed after the same
-    cache-flushing GEMM; plus the read rate of a 1 GiB buffer.  The read's
-    share count is the best of four."""
+    launches of a step (one batched launch per token) against a plain
+    streaming read (dq_stream_read) of the same packed bytes in as many
+    launches (each token's buffer), each group timed after the same
+    cache-flushing GEMM; the same matrices with one dq_gemv launch each; plus
+    the read rate of a 1 GiB buffer and the back-to-back launch floor.  The
+    read's share count is the best of four."""
     nbytes = sum(b.numel() * b.element_size() for b in read_bufs)
     n = len(read_bufs)
 
@@ -423,6 +471,7 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
         parts[per] = (outs, timed(lambda calls=calls: [fn(*a) for fn, a in calls]))
     per, (outs, read_ms) = min(parts.items(), key=lambda kv: kv[1][1])
     gemv_ms = timed(gemv_group)
+    single_ms = timed(per_matrix_group) if per_matrix_group is not None else None
     big = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
     big_out = torch.empty((65536,), dtype=torch.int32, device=dev)
     dq.stream_read(big, 65536, big_out)
@@ -434,11 +483,11 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
     del big
     read_gbs = nbytes / (read_ms * 1e-3) / 1e9
     gemv_gbs = nbytes / (gemv_ms * 1e-3) / 1e9
-    return {
-        "what": "plain streaming read (dq_stream_read) of the step's %d packed 4096x4096 buffers "
-                "(8 tokens x b=4..8, one copy per token), back to back, vs the %d GEMV launches on "
-                "them; each group after the same b=6 prefill GEMM, median of %d; bytes = packed "
-                "buffers; context, not the value" % (n, n, reps),
+    out = {
+        "what": "plain streaming read (dq_stream_read) of the step's %d token buffers (each the "
+                "five packed 4096x4096 matrices b=4..8 of one token, 63 MB), one launch each, vs "
+                "the %d batched GEMV launches on them; each group after the same b=6 prefill "
+                "GEMM, median of %d; bytes = packed words; context, not the value" % (n, n, reps),
         "read_gbs": round(read_gbs, 1),
         "read_per_launch_us": round(read_ms / n * 1e3, 3),
         "read_shares": sorted({o.shape[0] for o in outs}),
@@ -447,9 +496,17 @@ def attainable_read(torch, dq, dev, stream, gemv_group, read_bufs, flush, reps: 
         "gemv_frac_of_read": round(gemv_gbs / read_gbs, 4),
         "read_1gib_gbs": round((1 << 30) / (big_ms * 1e-3) / 1e9, 1),
         "launch_floor_us": round(floor_ms / n * 1e3, 3),
-        "launch_floor_what": "per-launch time of %d back-to-back 16 KB plain reads: no kernel "
-                             "launched once per matrix finishes faster here" % n,
+        "launch_floor_what": "per-launch time of %d back-to-back 16 KB plain reads: the fixed "
+                             "cost every launch pays here" % n,
     }
+    if single_ms is not None:
+        out["per_matrix"] = {
+            "gbs": round(nbytes / (single_ms * 1e-3) / 1e9, 1),
+            "per_launch_us": round(single_ms / per_matrix_launches * 1e3, 3),
+            "frac_of_hbm_peak": round(nbytes / (single_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "what": "the same 40 matrix products as one dq_gemv launch each (the per-matrix "
+                    "figure), same flush and timing"}
+    return out
 
 
 def cpu_baseline(decode_w, x1, target_s: float, allocation=None):
@@ -636,13 +693,27 @@ def main():
     def rw(K, b):
         return dq.packed_row_bytes(K, b) // 4
 
-    P2 = {b: torch.empty((DECODE["N"], rw(DECODE["K"], b)), dtype=torch.int32, device=dev) for b in W2}
+    # each token's five packed matrices lie back to back in one buffer (token t
+    # reads copy t), so a plain read of exactly those bytes is one launch too
+    words = {b: DECODE["N"] * rw(DECODE["K"], b) for b in W2}
+    tok_bufs = [torch.empty((sum(words.values()),), dtype=torch.int32, device=dev)
+                for _ in range(DECODE["tokens"])]
+
+    def token_views(buf):
+        out, off = {}, 0
+        for b in W2:
+            out[b] = buf[off:off + words[b]].view(DECODE["N"], rw(DECODE["K"], b))
+            off += words[b]
+        return out
+    P2t = [token_views(buf) for buf in tok_bufs]
+    P2 = P2t[0]
     S2 = {b: torch.empty((DECODE["N"],), dtype=torch.float32, device=dev) for b in W2}
     Q2 = {b: torch.empty((DECODE["N"], DECODE["K"]), dtype=torch.int32, device=dev) for b in W2}
     Y1 = {b: torch.empty((1, DECODE["N"]), dtype=torch.float32, device=dev) for b in W2}
     for b in W2:
         dq.quantize_pack(W2[b], b, P2[b], S2[b])
-    P2t = [P2] + [{b: P2[b].clone() for b in W2} for _ in range(1, DECODE["tokens"])]
+    for t in range(1, DECODE["tokens"]):
+        tok_bufs[t].copy_(tok_bufs[0])
     P4 = {b: torch.empty((PREFILL["N"], rw(PREFILL["K"], b)), dtype=torch.int32, device=dev) for b in W4}
     S4 = {b: torch.empty((PREFILL["N"],), dtype=torch.float32, device=dev) for b in W4}
     Y4 = torch.empty((PREFILL["M"], PREFILL["N"]), dtype=torch.float32, device=dev)
@@ -659,22 +730,32 @@ def main():
     for b in W4:  # one event group per GEMM (each runs for hundreds of microseconds)
         ops.append(("gemm_2048_b%d" % b, b, lambda b=b: dq.gemm(X4, P4[b], S4[b], PREFILL["K"], b, Y4)))
     decode = [(X1t[t], P2t[t][b], S2[b], b, Y1[b]) for t in range(DECODE["tokens"]) for b in W2]
-    # the decode launches go through the C entry point with their arguments
-    # taken beforehand: the tensor wrapper's checks cost the host more time
-    # than a 4096^2 GEMV takes on the GPU, and a host-bound loop would time the
-    # host (the submission cost is measured and reported below)
+    # the decode launches go through the C entry points with their arguments
+    # taken beforehand: the tensor wrappers' checks cost the host more time
+    # than a decode launch takes on the GPU, and a host-bound loop would time
+    # the host (the submission cost is measured and reported below).  The
+    # step's decode: one dq_gemv_batched per token over its five matrices.
     lib = dq.load()
     decode_calls = [(lib.dq_gemv, (xt.data_ptr(), 1, pt.data_ptr(), st.data_ptr(), DECODE["N"],
                                    DECODE["K"], b, yt.data_ptr(), stream.cuda_stream))
                     for xt, pt, st, b, yt in decode]
+    token_items = []
+    for t in range(DECODE["tokens"]):
+        arr = (dq.DQGemvItem * len(W2))()
+        for i, b in enumerate(W2):
+            arr[i] = dq.DQGemvItem(X1t[t].data_ptr(), P2t[t][b].data_ptr(), S2[b].data_ptr(),
+                                   Y1[b].data_ptr(), DECODE["N"], DECODE["K"], b)
+        token_items.append(arr)
+    batch_calls = [(lib.dq_gemv_batched, (ctypes.addressof(arr), len(W2), 1, stream.cuda_stream))
+                   for arr in token_items]
 
     def launch(fn, a):
         status = fn(*a)
         if status:
             raise dq.DQError(status, fn.__name__)
 
-    for (fn, a), (_, _, _, b, _) in zip(decode_calls, decode):
-        ops.append(("gemv_m1", b, lambda fn=fn, a=a: launch(fn, a)))
+    for fn, a in batch_calls:
+        ops.append(("gemv_m1", 0, lambda fn=fn, a=a: launch(fn, a)))
 
     # one HIP event at every group boundary (events between every launch would
     # add their own dispatch gaps to the tiny GEMV launches)
@@ -719,9 +800,9 @@ def main():
     for _ in range(5):
         dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4)
         t0 = time.perf_counter()
-        for fn, a in decode_calls:
+        for fn, a in batch_calls:
             launch(fn, a)
-        host_us.append((time.perf_counter() - t0) / len(decode_calls) * 1e6)
+        host_us.append((time.perf_counter() - t0) / len(batch_calls) * 1e6)
         torch.cuda.synchronize()
 
     Nd, Kd = DECODE["N"], DECODE["K"]
@@ -780,14 +861,16 @@ def main():
             "gemm": {"N": Np, "K": Kp, "M": Mp, "bits": list(PREFILL["bits"]),
                      "mfma_dtype": "bf16", "accumulate": "f32"},
             "step": "quantize+pack(5 decode) -> unpack(5) -> quantize+pack(4 prefill) -> "
-                    "gemm(4) -> decode 8 tokens x gemv(5), token t on copy t of the packed weights",
+                    "gemm(4) -> decode 8 tokens x one batched GEMV over the 5 matrices, token t on "
+                    "copy t of the packed weights",
             "timing": "HIP events at group boundaries on the launch stream; per-launch "
                       "figures are group time / launches (inter-launch gaps included); decode "
                       "launches through the C entry point with prepared arguments",
         },
         "roofline": {
-            "kernel": "dq_gemv M=1 N=K=4096 (40 launches back to back: 8 tokens x b=4..8, "
-                      "each on its own copy of the weights)",
+            "kernel": "dq_gemv_batched M=1 N=K=4096 (gemv_xres_batch_kernel; 8 launches back to "
+                      "back, one per token, each over that token's five matrices b=4..8 on its "
+                      "own copy of the weights)",
             "bound": "hbm",
             "achieved": round(value, 2),
             "peak": HBM_PEAK_GBS,
@@ -835,13 +918,22 @@ def main():
     b6 = PREFILL["bits"][1]
     out["roofline"]["attainable_read"] = attainable_read(
         torch, dq, dev, stream,
-        lambda: [launch(fn, a) for fn, a in decode_calls],
-        [pt for _, pt, _, _, _ in decode],
-        lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps))
-    # cache-hot figure, labelled as such: the same 40 launches with every token
+        lambda: [launch(fn, a) for fn, a in batch_calls],
+        tok_bufs,
+        lambda: dq.gemm(X4, P4[b6], S4[b6], PREFILL["K"], b6, Y4), reps=max(5, args.steps),
+        per_matrix_group=lambda: [launch(fn, a) for fn, a in decode_calls],
+        per_matrix_launches=len(decode_calls))
+    # cache-hot figure, labelled as such: the same 8 launches with every token
     # reading copy 0 (63 MB, inside the 256 MB last-level cache after the first token)
-    hot_calls = [(fn, (a[0], a[1], P2t[0][a[6]].data_ptr()) + a[3:])
-                 for fn, a in decode_calls]
+    hot_items = []
+    for t in range(DECODE["tokens"]):
+        arr = (dq.DQGemvItem * len(W2))()
+        for i, b in enumerate(W2):
+            arr[i] = dq.DQGemvItem(X1t[t].data_ptr(), P2t[0][b].data_ptr(), S2[b].data_ptr(),
+                                   Y1[b].data_ptr(), DECODE["N"], DECODE["K"], b)
+        hot_items.append(arr)
+    hot_calls = [(lib.dq_gemv_batched, (ctypes.addressof(arr), len(W2), 1, stream.cuda_stream))
+                 for arr in hot_items]
     hot_ms = []
     for _ in range(max(5, args.steps)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -855,8 +947,8 @@ def main():
     out["roofline"]["cache_hot"] = {
         "gbs": round(gemv_bytes / (hot * 1e-3) / 1e9, 1),
         "per_launch_us": round(hot / len(hot_calls) * 1e3, 3),
-        "what": "cache-hot: the 40 decode launches all on copy 0 of the five packed matrices "
-                "(63 MB, re-read from the last-level cache), median of the step count; "
+        "what": "cache-hot: the 8 batched decode launches all on copy 0 of the five packed "
+                "matrices (63 MB, re-read from the last-level cache), median of the step count; "
                 "context, not the value"}
     out["allocation"] = {"row_sumsq": row_sumsq_context(torch, dq, stream, list(W4.values()),
                                                         reps=max(5, args.steps))}

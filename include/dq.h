@@ -206,6 +206,36 @@ dq_status dq_unpack(const uint32_t* packed, const float* scales, int64_t N, int6
 dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                   int64_t N, int64_t K, int32_t bits, float* y, void* stream);
 
+/* Decode-shaped products of several matrices in one call (DynaQuant page,
+ * "自定义内核架构": the bit saving becomes decode speed on bandwidth-bound
+ * hardware; at decode sizes one launch per matrix costs about as much as the
+ * matrix's transfer, so the matrices a token multiplies share a launch).
+ * For each item i: y_i[m,n] = s_i[n] * sum_k x_i[m,k] q_i[n,k], exactly as
+ * dq_gemv on that item (same validation, layouts and tolerance).
+ *   items  in   HOST array of `count` descriptors, 1 <= count <=
+ *               DQ_GEMV_BATCH_MAX; read during the call only (the library
+ *               copies them into the kernel arguments)
+ *   M           rows of every item's x, 1 <= M <= DQ_GEMV_MAX_M
+ * Items may share x, packed and scales; no y may overlap another item's y or
+ * any input.  With M <= 2, every item whose K is a multiple of 32 and whose x
+ * fits the LDS (M * K / 32 * 80 bytes <= 48 KB) runs in ONE kernel launch
+ * (workgroups of all such items in one grid, widths mixed); each other item
+ * runs as its own dq_gemv launch.  With 3 <= M <= 16 each item runs as its
+ * own dq_gemv launch.  Argument errors in any item are returned before
+ * anything is enqueued. */
+#define DQ_GEMV_BATCH_MAX 32
+typedef struct {
+    const uint16_t* x;       /* device, [M, K] bf16 bits, 16-byte aligned        */
+    const uint32_t* packed;  /* device, [N, row_words] (dq_quantize_pack), 16 B  */
+    const float* scales;     /* device, [N] fp32, 4-byte aligned                  */
+    float* y;                /* device, [M, N] fp32 out, 4-byte aligned           */
+    int64_t N;
+    int64_t K;
+    int32_t bits;            /* 2 .. 15 */
+} dq_gemv_item;
+
+dq_status dq_gemv_batched(const dq_gemv_item* items, int32_t count, int64_t M, void* stream);
+
 /* Prefill-shaped product, any M >= 1 (tuned for M >= 256).  Same arguments
  * and result as dq_gemv.  Codes are expanded exactly to bf16 (for b >= 10 as
  * two exact bf16 halves, 64*hi + lo) and multiplied on the bf16 matrix cores

@@ -5,12 +5,13 @@ Two layers, both argument marshalling only (every step runs in the HIP
 kernels behind the C ABI declared in ``include/dq.h``):
 
 * ``dq_packed_row_bytes``, ``dq_quantize_pack``, ``dq_row_sumsq``,
-  ``dq_quantize_pack_sumsq``, ``dq_unpack``, ``dq_gemv``, ``dq_gemm``, ``dq_stream_read``,
+  ``dq_quantize_pack_sumsq``, ``dq_unpack``, ``dq_gemv``, ``dq_gemv_batched``, ``dq_gemm``,
+  ``dq_stream_read``,
   ``dq_sensitivity``, ``dq_allocate_bits`` -- the C entry points under their
   own names, taking integer addresses (device memory, host memory for the last
   two) and sizes; they return the ``dq_status`` code.
-* ``quantize_pack``, ``row_sumsq``, ``quantize_pack_sumsq``, ``unpack``, ``gemv``, ``gemm``,
-  ``stream_read`` -- the same calls on torch tensors (torch provides device
+* ``quantize_pack``, ``row_sumsq``, ``quantize_pack_sumsq``, ``unpack``, ``gemv``,
+  ``gemv_batched``, ``gemm``, ``stream_read`` -- the same calls on torch tensors (torch provides device
   memory and the current stream); they check device, dtype and contiguity,
   allocate outputs with torch and raise ``DQError`` on a non-zero status.
 * ``quantize_pack_asym``, ``unpack_asym``, ``gemv_asym``, ``gemm_asym`` --
@@ -43,7 +44,8 @@ __all__ = [
     "write_packed_file", "PackedFile", "dq_quantize_pack_asym", "dq_unpack_asym",
     "dq_gemv_asym", "dq_gemm_asym", "quantize_pack_asym", "unpack_asym", "gemv_asym",
     "gemm_asym", "dq_quantize_pack_group", "dq_unpack_group", "dq_gemv_group", "dq_gemm_group",
-    "quantize_pack_group", "unpack_group", "gemv_group", "gemm_group",
+    "quantize_pack_group", "unpack_group", "gemv_group", "gemm_group", "DQGemvItem",
+    "GEMV_BATCH_MAX", "dq_gemv_batched", "gemv_batched",
 ]
 
 (DQ_OK, DQ_ERR_NULL, DQ_ERR_BITS, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_DTYPE, DQ_ERR_HIP,
@@ -62,6 +64,16 @@ class DQFileMatrix(ctypes.Structure):
     """``dq_file_matrix`` of include/dq.h."""
     _fields_ = [("name", ctypes.c_char * 64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("bits", ctypes.c_int32), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class DQGemvItem(ctypes.Structure):
+    """``dq_gemv_item`` of include/dq.h (device addresses and sizes)."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("bits", ctypes.c_int32)]
+
+
+GEMV_BATCH_MAX = 32
 
 
 class DQError(RuntimeError):
@@ -93,6 +105,8 @@ def load():
     lib.dq_gemv.restype = st
     lib.dq_gemm.argtypes = [vp, i64, vp, vp, i64, i64, i32, vp, vp]
     lib.dq_gemm.restype = st
+    lib.dq_gemv_batched.argtypes = [vp, i32, i64, vp]
+    lib.dq_gemv_batched.restype = st
     lib.dq_stream_read.argtypes = [vp, i64, vp, i64, vp]
     lib.dq_stream_read.restype = st
     lib.dq_row_sumsq.argtypes = [vp, i32, i64, i64, vp, vp, vp]
@@ -225,6 +239,11 @@ def dq_unpack(packed: int, scales: int, N: int, K: int, bits: int, q_out: int, w
 def dq_gemv(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, y: int,
             stream: int = 0) -> int:
     return int(load().dq_gemv(x, M, packed, scales, N, K, bits, y, stream))
+
+
+def dq_gemv_batched(items: int, count: int, M: int, stream: int = 0) -> int:
+    """items: address of a host array of ``DQGemvItem``."""
+    return int(load().dq_gemv_batched(items, count, M, stream))
 
 
 def dq_gemm(x: int, M: int, packed: int, scales: int, N: int, K: int, bits: int, y: int,
@@ -561,6 +580,39 @@ def _matmul(fn, name, x, packed, scales, K: int, bits: int, y=None):
 def gemv(x, packed, scales, K: int, bits: int, y=None):
     """y[M, N] = x . dequant(W)^T for 1 <= M <= 16 (fp32 accumulate)."""
     return _matmul(dq_gemv, "dq_gemv", x, packed, scales, K, bits, y)
+
+
+def gemv_batched(items, ys=None):
+    """Several decode products in one call: items is a list of (x, packed,
+    scales, K, bits) (bf16 x [M, K] with the same M for all; x and weights may
+    be shared between items); returns the list of y [M, N] (or fills ``ys``).
+    Items that fit the resident-x kernel share one launch."""
+    torch = _torch()
+    if not 1 <= len(items) <= GEMV_BATCH_MAX:
+        raise ValueError("1 to %d items" % GEMV_BATCH_MAX)
+    arr = (DQGemvItem * len(items))()
+    out = []
+    M = None
+    for i, (x, packed, scales, K, bits) in enumerate(items):
+        _need(x, "x", (torch.bfloat16,), 2)
+        _need(packed, "packed", (torch.int32,), 2)
+        _need(scales, "scales", (torch.float32,), 1)
+        N = packed.shape[0]
+        if M is None:
+            M = x.shape[0]
+        if x.shape[0] != M or x.shape[1] != K or \
+                packed.shape[1] != packed_row_bytes(K, bits) // 4 or scales.shape[0] != N:
+            raise ValueError("item %d: shape mismatch between x, packed, scales, K and bits" % i)
+        y = ys[i] if ys is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+        _need(y, "y", (torch.float32,), 2)
+        if tuple(y.shape) != (M, N):
+            raise ValueError("item %d: y must be [M, N]" % i)
+        arr[i] = DQGemvItem(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), y.data_ptr(), N, K,
+                            bits)
+        out.append(y)
+    _check(dq_gemv_batched(ctypes.addressof(arr), len(items), M, _stream(items[0][0])),
+           "dq_gemv_batched")
+    return out
 
 
 def gemm(x, packed, scales, K: int, bits: int, y=None):

@@ -198,6 +198,25 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
                                       static_cast<hipStream_t>(stream)));
 }
 
+dq_status dq_gemv_batched(const dq_gemv_item* items, int32_t count, int64_t M, void* stream)
+{
+    if (!items) return DQ_ERR_NULL;
+    if (count < 1 || count > DQ_GEMV_BATCH_MAX || M < 1 || M > DQ_GEMV_MAX_M) return DQ_ERR_SHAPE;
+    static_assert(DQ_GEMV_BATCH_MAX == dq::kGemvBatchMax, "batch size");
+    dq::GemvItem g[DQ_GEMV_BATCH_MAX];
+    for (int32_t i = 0; i < count; ++i) {  // every item is checked before anything is enqueued
+        const dq_gemv_item& it = items[i];
+        if (!it.x || !it.packed || !it.scales || !it.y) return DQ_ERR_NULL;
+        const dq_status st = check_common(it.N, it.K, it.bits);
+        if (st != DQ_OK) return st;
+        if (!aligned(it.x, 16) || !aligned(it.packed, 16) || !aligned(it.scales, 4) ||
+            !aligned(it.y, 4))
+            return DQ_ERR_ALIGN;
+        g[i] = dq::GemvItem{it.x, it.packed, it.scales, it.y, it.N, it.K, it.bits};
+    }
+    return hip_status(dq::launch_gemv_batched(g, count, M, static_cast<hipStream_t>(stream)));
+}
+
 dq_status dq_gemv_asym(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        const int32_t* zeros, int64_t N, int64_t K, int32_t bits, float* y,
                        void* stream)

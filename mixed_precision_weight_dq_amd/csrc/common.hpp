@@ -135,12 +135,31 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t* __restrict__ ro
     }
 }
 
-// Wave-wide reductions through cross-lane shuffles.
+// Sum over the 64 lanes of a wave, returned to every lane, in a fixed order
+// (so the same inputs give the same bits on every call).  DPP steps: within
+// each row of 16 lanes an inclusive prefix sum by row_shr 1, 2, 4, 8 (lanes
+// shifted in from outside the row read 0), which leaves each row's total in
+// its lane 15; row_bcast:15 adds row 0's total into row 1 and row 2's into
+// row 3, row_bcast:31 adds rows 0 + 1 into rows 2 and 3; lane 63 then holds
+// the wave's total, which a readlane hands to every lane.  Seven VALU
+// instructions instead of the shuffle form's bounds-checked permutes.
+// v + (v moved by DPP control kCtrl in the rows of kRowMask; 0 elsewhere)
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    const int s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, true);
+    return v + __int_as_float(s);
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)

@@ -1,0 +1,234 @@
+// Decode-shaped products of several matrices in one launch:
+//   y_i[m, n] = s_i[n] * sum_k x_i[m, k] * q_i[n, k]   for items i = 0 .. count-1
+// DynaQuant page, "自定义内核架构" (the bit saving turns into decode speed on
+// bandwidth-bound hardware).  At M = 1 a 4096 x 4096 matrix is 8-17 MB of
+// codes, a transfer of 1-2 us at HBM speed, comparable to the fixed cost of
+// one kernel launch; a decode step multiplies the same activation by several
+// such matrices (the projections of a layer), so giving all of them to one
+// launch pays that cost once.
+//
+// The item descriptors travel by value in the kernel arguments (no device
+// memory is allocated or written besides the outputs).  Each workgroup finds
+// its item from a table of first-workgroup indices (a scalar scan over at most
+// 32 entries) and runs one of the bodies of gemv_kernels.hpp for the item's
+// width:
+//   * rows of at least 64 chunks (K >= 2048): the streaming body.  The host
+//     gives each item a share of one round of workgroups (as many as the GPU
+//     holds at once) in proportion to its bytes, so each wave streams several
+//     rows with its loads running ahead across row boundaries;
+//   * shorter rows: the resident-x body, one (or two) rows per wave.
+// Per chunk the arithmetic is that of the one-matrix resident-x kernel, so
+// every output is within the same bound; the summation order differs only in
+// that the streaming body adds each chunk's dot product to the row total
+// instead of chaining it.  Items of different widths and shapes mix freely;
+// the LDS per workgroup is sized for the largest x of the launch, and x is
+// staged with a fixed count of loads sized for the largest x the kernel
+// accepts (threads past an item's last piece load nothing).
+#include <algorithm>
+
+#include "common.hpp"
+#include "gemv_kernels.hpp"
+#include "launch.hpp"
+
+namespace dq {
+
+namespace {
+
+constexpr int kBatchWaves = 4;     // waves per workgroup, one (or two) rows each
+constexpr int kBatchXPieces = 10;  // x pieces per thread: covers kXResMax
+static_assert(kBatchXPieces * kBatchWaves * kWave >= kXResMax / (kXPitch * 2) * 4,
+              "x staging covers the largest x");
+
+// item modes
+constexpr int kModeRow = 0;     // one row per wave (resident-x body)
+constexpr int kModeTwoRows = 1; // two rows per wave (resident-x body)
+constexpr int kModeStream = 2;  // rpw rows per wave, streamed (K >= 2048)
+
+struct BatchItemArgs {
+    const uint16_t* x;
+    const uint32_t* packed;
+    const float* scales;
+    float* y;
+    int32_t N;
+    int32_t K;
+    int32_t row_words;
+    int32_t code;  // 4 * bits + mode
+    int32_t rpw;   // rows per wave (streaming mode)
+};
+
+struct BatchArgs {
+    BatchItemArgs item[kGemvBatchMax];
+    int32_t first[kGemvBatchMax + 1];  // first workgroup of each item; first[count] = grid
+    int32_t count;
+    int32_t M;
+};
+static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments stay within 4 KB");
+
+// The arguments are read through the kernel-argument segment pointer (the
+// struct is the only argument, at offset 0), so indexing them by the
+// run-time item number is a scalar load; indexing the by-value parameter
+// instead makes the compiler copy the whole struct into per-lane scratch.
+__device__ __forceinline__ const BatchArgs& batch_args()
+{
+    // an address-space cast of the constant kernel-argument pointer; the
+    // compiler infers the address space back and loads with scalar loads
+    return *(const BatchArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// kMaxB: the widest code the instance serves.  Launches whose items are all
+// at most 8 bits take the narrow instance, whose register count (and so its
+// occupancy) is not set by the wide codes' bodies.
+template <int MT, int kMaxB>
+__global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(const BatchArgs args)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+    (void)args;
+    auto& a = batch_args();
+    const int32_t bid = (int32_t)blockIdx.x;
+    int i = 0;
+    while (i + 1 < a.count && bid >= a.first[i + 1]) ++i;
+    auto& it = a.item[i];
+    const int64_t local = bid - a.first[i];
+    const NoZeroPoints zp{};
+    switch (it.code) {
+#define DQ_BATCH_CASE(B)                                                                          \
+    case 4 * B + kModeRow:                                                                        \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 1, true>(             \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
+                xs_dyn);                                                                          \
+        break;                                                                                    \
+    case 4 * B + kModeTwoRows:                                                                    \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 2, true>(             \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
+                xs_dyn);                                                                          \
+        break;                                                                                    \
+    case 4 * B + kModeStream:                                                                     \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_stream_body<B, MT, kBatchWaves, kBatchXPieces>(                                  \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
+                local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
+        break;
+        DQ_BATCH_CASE(2)
+        DQ_BATCH_CASE(3)
+        DQ_BATCH_CASE(4)
+        DQ_BATCH_CASE(5)
+        DQ_BATCH_CASE(6)
+        DQ_BATCH_CASE(7)
+        DQ_BATCH_CASE(8)
+        DQ_BATCH_CASE(9)
+        DQ_BATCH_CASE(10)
+        DQ_BATCH_CASE(11)
+        DQ_BATCH_CASE(12)
+        DQ_BATCH_CASE(13)
+        DQ_BATCH_CASE(14)
+        DQ_BATCH_CASE(15)
+#undef DQ_BATCH_CASE
+    default:
+        break;
+    }
+}
+
+// the resident-x kernel's two-rows-per-wave rule (see launch_gemv_xres)
+bool two_rows(int64_t nchunks)
+{
+    auto fill = [](int64_t c) { return (double)c / (double)(ceil_div(c, kSlice) * kSlice); };
+    return fill(2 * nchunks) > fill(nchunks) + 0.1;
+}
+
+}  // namespace
+
+bool gemv_batch_eligible(int64_t M, int64_t K)
+{
+    return M <= 2 && K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax;
+}
+
+hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipStream_t stream)
+{
+    // workgroups the GPU holds at once for this kernel (registers and LDS)
+    size_t lds = 0;
+    for (int i = 0; i < count; ++i)
+        if (gemv_batch_eligible(M, items[i].K))
+            lds = std::max(lds, (size_t)(M * (items[i].K / kChunk) * kXPitch * 2));
+    bool narrow = true;  // every item of the single launch at most 8 bits
+    for (int i = 0; i < count; ++i)
+        if (gemv_batch_eligible(M, items[i].K) && items[i].bits > 8) narrow = false;
+    const void* kernel =
+        M <= 1 ? (narrow ? reinterpret_cast<const void*>(&gemv_xres_batch_kernel<1, 8>)
+                         : reinterpret_cast<const void*>(&gemv_xres_batch_kernel<1, 15>))
+               : (narrow ? reinterpret_cast<const void*>(&gemv_xres_batch_kernel<2, 8>)
+                         : reinterpret_cast<const void*>(&gemv_xres_batch_kernel<2, 15>));
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBatchWaves * kWave, lds);
+    if (e != hipSuccess) return e;
+    const int64_t slots = (int64_t)std::max(1, cus) * std::max(1, per_cu);
+    double stream_bytes = 0;  // bytes of the streamed items, shared out over the slots
+    for (int i = 0; i < count; ++i)
+        if (gemv_batch_eligible(M, items[i].K) && items[i].K / kChunk >= kSlice)
+            stream_bytes += (double)items[i].N * packed_row_words(items[i].K, items[i].bits) * 4;
+
+    BatchArgs a;
+    a.M = (int32_t)M;
+    int n = 0;
+    int64_t blocks = 0;
+    auto flush = [&]() -> hipError_t {
+        if (n == 0) return hipSuccess;
+        a.count = n;
+        a.first[n] = (int32_t)blocks;
+        const dim3 grid((unsigned)blocks), block(kBatchWaves * kWave);
+        if (M <= 1 && narrow)
+            gemv_xres_batch_kernel<1, 8><<<grid, block, lds, stream>>>(a);
+        else if (M <= 1)
+            gemv_xres_batch_kernel<1, 15><<<grid, block, lds, stream>>>(a);
+        else if (narrow)
+            gemv_xres_batch_kernel<2, 8><<<grid, block, lds, stream>>>(a);
+        else
+            gemv_xres_batch_kernel<2, 15><<<grid, block, lds, stream>>>(a);
+        n = 0;
+        blocks = 0;
+        return hipGetLastError();
+    };
+    for (int i = 0; i < count; ++i) {
+        const GemvItem& g = items[i];
+        if (!gemv_batch_eligible(M, g.K)) {  // this item takes its own launch
+            e = launch_gemv(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.y, nullptr, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        const int64_t nchunks = g.K / kChunk;
+        const int64_t rw = packed_row_words(g.K, g.bits);
+        int mode, rpw = 1;
+        int64_t nb;
+        if (nchunks >= kSlice) {
+            // this item's share of one round of workgroups, in proportion to
+            // its bytes; a wave's rows stay below 2^31 bytes
+            const double share = (double)g.N * rw * 4 / stream_bytes;
+            const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
+            int64_t r = ceil_div(g.N, wgs * kBatchWaves);
+            r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4)));
+            rpw = (int)r;
+            mode = kModeStream;
+            nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
+        } else {
+            const bool two = two_rows(nchunks);
+            mode = two ? kModeTwoRows : kModeRow;
+            nb = ceil_div(g.N, kBatchWaves * (two ? 2 : 1));
+        }
+        if (blocks + nb > 0x7fffffffLL) {  // the grid's index space is full: launch what we have
+            e = flush();
+            if (e != hipSuccess) return e;
+        }
+        a.item[n] = BatchItemArgs{g.x, g.packed, g.scales, g.y, (int32_t)g.N, (int32_t)g.K,
+                                  (int32_t)rw, 4 * g.bits + mode, rpw};
+        a.first[n] = (int32_t)blocks;
+        blocks += nb;
+        ++n;
+    }
+    return flush();
+}
+
+}  // namespace dq

@@ -41,6 +41,22 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, con
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* packed, const float* scales,
                        int64_t N, int64_t K, int bits, float* y, const int32_t* zeros,
                        hipStream_t stream);
+// One matrix of a batched decode product (arguments as for launch_gemv).
+struct GemvItem {
+    const uint16_t* x;
+    const uint32_t* packed;
+    const float* scales;
+    float* y;
+    int64_t N;
+    int64_t K;
+    int bits;
+};
+constexpr int kGemvBatchMax = 32;  // items per call (DQ_GEMV_BATCH_MAX)
+// Whether an item of this shape joins the single launch (else it gets its own).
+bool gemv_batch_eligible(int64_t M, int64_t K);
+// Symmetric per-row products of `count` matrices sharing M (<= 2 for the
+// single launch; items outside it run one launch each).
+hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipStream_t stream);
 hipError_t launch_quantize_pack_asym(const void* w, bool bf16, int64_t N, int64_t K, int bits,
                                      uint32_t* packed, float* scales, int32_t* zeros,
                                      hipStream_t stream);

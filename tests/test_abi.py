@@ -203,3 +203,34 @@ def test_group_arguments_rejected():
     assert dq.dq_gemv_group(MIS, 1, A, A, 4, 64, 6, 32, A) == dq.DQ_ERR_ALIGN
     assert dq.dq_gemm_group(A, 1, A, 0, 4, 64, 6, 32, A) == dq.DQ_ERR_NULL
     assert dq.dq_gemm_group(A, 0, A, A, 4, 64, 6, 32, A) == dq.DQ_ERR_SHAPE
+
+
+def _items(n, **over):
+    arr = (dq.DQGemvItem * n)()
+    for i in range(n):
+        arr[i] = dq.DQGemvItem(A, A, A, A + 64 * i, 4, 64, 6)
+    for k, v in over.items():
+        i, field = k.split("_", 1)
+        setattr(arr[int(i)], field, v)
+    return arr
+
+
+def test_gemv_batched_arguments_rejected():
+    """Every item is checked on the host before anything is enqueued (the fake
+    device addresses are never touched)."""
+    f = dq.dq_gemv_batched
+    addr = ctypes.addressof
+    assert f(0, 1, 1) == dq.DQ_ERR_NULL
+    assert f(addr(_items(1)), 0, 1) == dq.DQ_ERR_SHAPE
+    assert f(addr(_items(33)), 33, 1) == dq.DQ_ERR_SHAPE
+    assert f(addr(_items(2)), 2, 0) == dq.DQ_ERR_SHAPE
+    assert f(addr(_items(2)), 2, 17) == dq.DQ_ERR_SHAPE
+    # a bad last item is found before the good ones run
+    for field, value, status in (("x", None, dq.DQ_ERR_NULL), ("packed", None, dq.DQ_ERR_NULL),
+                                 ("scales", None, dq.DQ_ERR_NULL), ("y", None, dq.DQ_ERR_NULL),
+                                 ("bits", 1, dq.DQ_ERR_BITS), ("bits", 16, dq.DQ_ERR_BITS),
+                                 ("N", 0, dq.DQ_ERR_SHAPE), ("K", 0, dq.DQ_ERR_SHAPE),
+                                 ("K", (1 << 22) + 1, dq.DQ_ERR_SHAPE), ("N", 1 << 31, dq.DQ_ERR_SHAPE),
+                                 ("x", MIS, dq.DQ_ERR_ALIGN), ("packed", MIS, dq.DQ_ERR_ALIGN),
+                                 ("scales", A + 2, dq.DQ_ERR_ALIGN), ("y", A + 2, dq.DQ_ERR_ALIGN)):
+        assert f(addr(_items(5, **{"4_" + field: value})), 5, 1) == status, (field, value)

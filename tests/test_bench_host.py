@@ -1,6 +1,6 @@
 """Host logic of bench.py that runs without a GPU: the one-GPU guard, and the
-rule that counter-derived traffic is reported only while the GEMV source it
-was taken on is unchanged (whole-line comments aside)."""
+rule that counter-derived traffic is reported only while the batched decode
+kernel's source it was taken on is unchanged (whole-line comments aside)."""
 from __future__ import annotations
 
 import json
@@ -32,7 +32,7 @@ def test_digest_ignores_comment_lines_only(tmp_path, monkeypatch):
     csrc = _copy_tree(tmp_path)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     base = bench.kernel_source_digest()
-    gemv = csrc / "gemv.hip"
+    gemv = csrc / "gemv_batch.hip"
     text = gemv.read_text()
     gemv.write_text("// a comment line\n" + text)
     assert bench.kernel_source_digest() == base

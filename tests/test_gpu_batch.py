@@ -1,0 +1,143 @@
+"""Parity of the batched decode product (dq_gemv_batched): several matrices
+of mixed widths and shapes in one call, each output within 1e-4 * sum_k
+|x * w_hat| of the oracle's fp64 product.  Items on the one-row-per-wave path
+(rows under 64 chunks) and items outside the single launch (K not a multiple
+of 32, x too large for LDS, M >= 3) are bit-identical to dq_gemv; streamed
+items (rows of 64 chunks or more) add each chunk's sum into the row total,
+so they are checked against the oracle and for the same bits on every call.
+Covered: every width, rows that end inside a slice (65, 160, 544 chunks per
+row), rows per wave from 1 up, ragged last workgroups and waves without rows,
+the largest batch, shared activations, and the decode and layer shapes of
+the workloads (sampled rows against the oracle).
+
+Source: DynaQuant page (zingnex.cn), "自定义内核架构" (the packed codes'
+bandwidth saving becomes decode speed); BPDQ article, section 3.2 (the fused
+dequantizing product)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import mixed_precision_weight_dq_amd as dq
+import oracle
+import workload
+from gpu_util import bf16_gpu, f32_bits, report, torch, weights_gpu
+from pins import within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+# (N, K, bits): every width, K multiples of 32 (one launch) and not (own
+# launch), one-row and two-rows-per-wave shapes, a ragged last workgroup
+MIXED = [(300, 4096, 4), (37, 1000, 5), (70, 2048, 15), (1, 32, 2), (40, 6144, 6),
+         (33, 5152, 9), (8, 17408, 7), (5, 5120, 3), (129, 2080, 8), (17, 224, 10),
+         (2, 96, 11), (9, 4096 + 37, 12), (64, 256, 13), (3, 8192, 14)]
+
+
+def quantized(seed, N, K, bits):
+    w = workload.weights(61, seed, N, K, dtype="bf16")
+    P, S = dq.quantize_pack(weights_gpu(w), bits)
+    return P, S
+
+
+def streamed(M, K):
+    return M <= 2 and K % 32 == 0 and K // 32 >= 64 and M * (K // 32) * 80 <= 48 * 1024
+
+
+def assert_batch(items_np, M, seed, check_oracle=True):
+    """items_np: list of (N, K, bits, x_key); items with the same x_key share x."""
+    xs = {}
+    items, meta = [], []
+    for i, (N, K, bits, xk) in enumerate(items_np):
+        if (xk, K) not in xs:
+            xs[(xk, K)] = workload.activations(62, seed * 100 + xk + K, M, K)
+        P, S = quantized(seed * 1000 + i, N, K, bits)
+        items.append((bf16_gpu(xs[(xk, K)]), P, S, K, bits))
+        meta.append((N, K, bits, xs[(xk, K)]))
+    report("gemv_batched M=%d items=%d seed=%d" % (M, len(items), seed))
+    ys = dq.gemv_batched(items)
+    again = dq.gemv_batched(items)
+    singles = [dq.gemv(x, P, S, K, b) for (x, P, S, K, b) in items]
+    torch().cuda.synchronize()
+    for i, ((N, K, bits, x), y, y2, y1, it) in enumerate(zip(meta, ys, again, singles, items)):
+        assert np.array_equal(f32_bits(y), f32_bits(y2)), "item %d not deterministic" % i
+        if not streamed(M, K):
+            assert np.array_equal(f32_bits(y), f32_bits(y1)), "item %d differs from dq_gemv" % i
+        if check_oracle:
+            o_p = it[1].cpu().numpy().view(np.uint32)
+            o_s = it[2].cpu().numpy()
+            y_ref, bound = oracle.matmul(x, o_p, o_s, N, K, bits)
+            assert within_tolerance(y.cpu().numpy(), y_ref, bound).all(), "item %d" % i
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+def test_batched_mixed_widths(M):
+    items = [(N, K, b, i % 3) for i, (N, K, b) in enumerate(MIXED)]
+    assert_batch(items, M, seed=M)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_batched_stream_row_boundaries(M):
+    """Streamed rows that end inside a slice (65, 160, 544 chunks), exactly a
+    slice (64), many rows per wave next to few, ragged last workgroups."""
+    items = [(1000, 2048, 6, 0), (77, 2080, 5, 1), (3, 5120, 7, 2), (4097, 5120, 4, 2),
+             (250, 17408, 8, 3), (513, 4096, 15, 4), (2, 2080, 2, 1), (1, 4096, 9, 4)]
+    assert_batch(items, M, seed=50 + M)
+
+
+def test_batched_largest_batch_and_one_item():
+    items = [(N, K, b, 0) for (N, K, b) in MIXED] * 3
+    assert_batch(items[:dq.GEMV_BATCH_MAX], 1, seed=40)
+    assert_batch(items[:1], 1, seed=41)
+    assert_batch([(3, 1 << 22, 5, 0), (70, 2048, 6, 0)], 1, seed=42)  # x too large for LDS
+
+
+def test_batched_decode_workload():
+    """The decode workload's five 4096 x 4096 matrices (b = 4 .. 8, one
+    activation) as one launch: the same bits on every call, sampled rows
+    within the tolerance of the oracle."""
+    N = K = 4096
+    x = workload.activations(2, 0, 1, K)
+    X = bf16_gpu(x)
+    items, packs = [], []
+    for b in (4, 5, 6, 7, 8):
+        w = workload.weights(2, b, N, K, outlier_frac=0.001)
+        P, S = dq.quantize_pack(weights_gpu(w), b)
+        items.append((X, P, S, K, b))
+    report("gemv_batched decode workload")
+    ys = dq.gemv_batched(items)
+    again = dq.gemv_batched(items)
+    torch().cuda.synchronize()
+    rows = np.random.default_rng(3).choice(N, 64, replace=False)
+    for (X_, P, S, K_, b), y, y2 in zip(items, ys, again):
+        assert np.array_equal(f32_bits(y), f32_bits(y2))
+        o_p = P.cpu().numpy().view(np.uint32)[rows]
+        o_s = S.cpu().numpy()[rows]
+        y_ref, bound = oracle.matmul(x, o_p, o_s, len(rows), K, b)
+        assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()
+
+
+def test_batched_layer_shapes():
+    """One layer of the 448-matrix stack (4 x 5120^2, 2 x 17408 x 5120,
+    5120 x 17408) at widths 5 .. 8 in one call, M = 1: the same bits on
+    every call, sampled rows against the oracle."""
+    t = torch()
+    shapes = [(5120, 5120, 6), (5120, 5120, 5), (5120, 5120, 6), (5120, 5120, 7),
+              (17408, 5120, 6), (17408, 5120, 8), (5120, 17408, 5)]
+    g = t.Generator(device="cuda")
+    g.manual_seed(7)
+    items = []
+    for i, (N, K, b) in enumerate(shapes):
+        W = (t.randn((N, K), generator=g, device="cuda") * 0.02).to(t.bfloat16)
+        P, S = dq.quantize_pack(W, b)
+        x = workload.activations(63, i, 1, K)
+        items.append((bf16_gpu(x), P, S, K, b, x))
+    report("gemv_batched layer shapes")
+    ys = dq.gemv_batched([it[:5] for it in items])
+    again = dq.gemv_batched([it[:5] for it in items])
+    t.cuda.synchronize()
+    for (X, P, S, K, b, x), y, y2 in zip(items, ys, again):
+        assert np.array_equal(f32_bits(y), f32_bits(y2))
+        rows = np.random.default_rng(K + b).choice(P.shape[0], 32, replace=False)
+        o_p = P.cpu().numpy().view(np.uint32)[rows]
+        y_ref, bound = oracle.matmul(x, o_p, S.cpu().numpy()[rows], len(rows), K, b)
+        assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()
