@@ -11,7 +11,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace dq {
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+// in order: a loop over pipeline stages whose index stays a compile-time
+// constant, so each stage's registers are named statically.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kWave = 64;
 constexpr int kChunk = 32;  // codes per chunk; a chunk is exactly B words

@@ -34,7 +34,7 @@ namespace dq {
 
 namespace {
 
-constexpr int kBatchWaves = 4;     // waves per workgroup, one (or two) rows each
+constexpr int kBatchWaves = 4;     // waves per workgroup
 constexpr int kBatchXPieces = 10;  // x pieces per thread: covers kXResMax
 static_assert(kBatchXPieces * kBatchWaves * kWave >= kXResMax / (kXPitch * 2) * 4,
               "x staging covers the largest x");
@@ -42,7 +42,8 @@ static_assert(kBatchXPieces * kBatchWaves * kWave >= kXResMax / (kXPitch * 2) * 
 // item modes
 constexpr int kModeRow = 0;     // one row per wave (resident-x body)
 constexpr int kModeTwoRows = 1; // two rows per wave (resident-x body)
-constexpr int kModeStream = 2;  // rpw rows per wave, streamed (K >= 2048)
+constexpr int kModeStream = 2;    // rpw rows per wave, streamed (K >= 2048)
+constexpr int kModeRowSlice = 3;  // rpw rows per wave in whole-row slices (K % 2048 == 0)
 
 struct BatchItemArgs {
     const uint16_t* x;
@@ -109,6 +110,12 @@ __global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(co
             gemv_stream_body<B, MT, kBatchWaves, kBatchXPieces>(                                  \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
                 local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
+        break;                                                                                    \
+    case 4 * B + kModeRowSlice:                                                                   \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces>(                                \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
+                local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
         break;
         DQ_BATCH_CASE(2)
         DQ_BATCH_CASE(3)
@@ -136,6 +143,12 @@ bool two_rows(int64_t nchunks)
     auto fill = [](int64_t c) { return (double)c / (double)(ceil_div(c, kSlice) * kSlice); };
     return fill(2 * nchunks) > fill(nchunks) + 0.1;
 }
+
+// Whether a streamed item takes the row-sliced body: its rows are a whole
+// number of slices (K a multiple of 2048), so no lane idles.  Other rows take
+// the streaming body, whose per-lane bookkeeping costs less than lanes idling
+// in each row's last slice.
+bool row_sliced(int64_t nchunks) { return nchunks % kSlice == 0; }
 
 }  // namespace
 
@@ -205,13 +218,13 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
         int64_t nb;
         if (nchunks >= kSlice) {
             // this item's share of one round of workgroups, in proportion to
-            // its bytes; a wave's rows stay below 2^31 bytes
+            // its bytes; a workgroup's rows stay below 2^31 bytes
             const double share = (double)g.N * rw * 4 / stream_bytes;
             const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
             int64_t r = ceil_div(g.N, wgs * kBatchWaves);
-            r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4)));
+            r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
             rpw = (int)r;
-            mode = kModeStream;
+            mode = row_sliced(nchunks) ? kModeRowSlice : kModeStream;
             nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
         } else {
             const bool two = two_rows(nchunks);

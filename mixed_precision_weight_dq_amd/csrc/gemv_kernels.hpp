@@ -412,12 +412,13 @@ __device__ __forceinline__ void gemv_xres_body(
     }
 }
 
-
 // ---------------------------------------------------------------------------
 // Streaming resident-x body (1 <= M <= 2, K a multiple of 32 with at least
 // 64 chunks per row, x resident in LDS): the workgroup owns rows
-// [row0, row0 + kWaves * rpw) of the matrix, wave w the rpw rows from
-// row0 + w * rpw.  A wave reads its rows' codes as one stream of chunks
+// [row0, row0 + kWaves * rpw) of the matrix, dealt to its waves in turn (wave
+// w takes rows row0 + w, row0 + w + kWaves, ...), so at any time the
+// workgroup reads one contiguous block of rows.  A wave reads its rows' codes
+// as one stream of chunks
 // (lane l takes chunk l, l + 64, ... of the stream; the row changes inside a
 // slice when a row's chunk count is not a multiple of 64) with the loads of
 // two slices in flight ahead of the one being computed, across row
@@ -426,7 +427,7 @@ __device__ __forceinline__ void gemv_xres_body(
 // (a slice holds at most two rows, as a row has at least 64 chunks); when a
 // slice completes a row, the wave reduces that row's accumulator, stores it
 // and clears it.  The arithmetic per chunk is that of the resident-x body.
-// The wave's rows must span less than 2^31 bytes of packed words.
+// The workgroup's rows must span less than 2^31 bytes of packed words.
 template <int B, int MT, int kWaves, int kR>
 __device__ __forceinline__ void gemv_stream_body(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
@@ -438,13 +439,16 @@ __device__ __forceinline__ void gemv_stream_body(
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int32_t nchunks = (int32_t)(K / kChunk);
-    const int64_t wrow0 = row0 + (int64_t)wave * rpw;
-    const int32_t wrows = (int32_t)(wrow0 < N ? (N - wrow0 < rpw ? N - wrow0 : rpw) : 0);
-    // the wave's stream: wrows * nchunks chunks (below 2^31 bytes, so 32-bit
-    // counters and byte offsets hold it)
+    const int64_t wrow0 = row0 + wave;  // the wave's first row; then every kWaves-th
+    const int64_t wend = row0 + kWaves * rpw < N ? row0 + kWaves * rpw : N;
+    const int32_t wrows = (int32_t)(wrow0 < wend ? (wend - wrow0 + kWaves - 1) / kWaves : 0);
+    // the wave's stream: wrows * nchunks chunks, within the workgroup's rows
+    // (below 2^31 bytes, so 32-bit counters and byte offsets hold it)
     const int32_t nslices = (int32_t)ceil_div((int64_t)wrows * nchunks, kSlice);
-    const BufRef wbuf = uniform_buf(packed + (wrows > 0 ? wrow0 : 0) * row_words,
-                                    (uint32_t)(wrows * row_words * 4));
+    const uint32_t row_bytes = (uint32_t)(row_words * 4);
+    const BufRef wbuf =
+        uniform_buf(packed + (wrows > 0 ? wrow0 : 0) * row_words,
+                    wrows > 0 ? (uint32_t)((wrows - 1) * kWaves + 1) * row_bytes : 0u);
     const BufRef xall = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
 
     // x staged once per workgroup, as in gemv_xres_body (exact piece count)
@@ -460,8 +464,9 @@ __device__ __forceinline__ void gemv_stream_body(
 
     // load position: lane's (row, chunk) in the stream and its byte offset,
     // advanced one slice per load (a row has at least 64 chunks, so at most
-    // one row boundary is crossed; the row's padding bytes are skipped then)
-    const uint32_t pad = (uint32_t)(row_words * 4 - (int64_t)nchunks * B * 4);
+    // one row boundary is crossed; the row's padding bytes and the other
+    // waves' rows are skipped then)
+    const uint32_t pad = row_bytes - (uint32_t)(nchunks * B * 4) + (kWaves - 1) * row_bytes;
     int32_t lr = 0, lc = lane;
     uint32_t loff = (uint32_t)(lane * B * 4);
     uint32_t w[3][B];
@@ -540,7 +545,7 @@ __device__ __forceinline__ void gemv_stream_body(
             // the scale at a wave-uniform address in uniform control flow: a
             // scalar load, which leaves the vector loads in flight alone (a
             // vector load here would be followed by a wait for all of them)
-            const int64_t n = wrow0 + next_row;
+            const int64_t n = wrow0 + (int64_t)next_row * kWaves;
             const float s = scales[n];
             if (lane == 0) {
 #pragma unroll
@@ -559,6 +564,136 @@ __device__ __forceinline__ void gemv_stream_body(
     }
     if (sl < nslices) step(std::integral_constant<int, 0>{}, sl);
     if (sl + 1 < nslices) step(std::integral_constant<int, 1>{}, sl + 1);
+}
+
+// Streaming GEMV, row-sliced: the workgroup's rows row0 .. row0 + kWaves * rpw
+// are dealt to its waves in turn (wave w takes rows row0 + w, row0 + w +
+// kWaves, ...), so at any time the workgroup reads one contiguous block of
+// kWaves rows; each row is cut into slices of 64 chunks that never span two
+// rows (a row is ceil(K / 2048) slices; in a row's last slice the lanes past
+// its end idle).
+// Everything that locates a slice -- its row, its place in the row, its byte
+// offset -- is wave-uniform, so the per-chunk work is the load, the x reads
+// and the dot products; each lane's chunk adds into one running total per
+// row, reduced across the wave when the row's last slice is done.  Loads run
+// two slices ahead of the arithmetic, across row boundaries.  For rows that
+// are a whole number of slices (K a multiple of 2048) no lane ever idles.
+template <int B, int MT, int kWaves, int kR, int kStages = 3>
+__device__ __forceinline__ void gemv_rowslice_body(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y, int64_t row0, int64_t rpw, uint16_t* __restrict__ xs_dyn)
+{
+    constexpr int kThreads = kWaves * kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int32_t nchunks = (int32_t)(K / kChunk);
+    const int32_t spr = (int32_t)ceil_div((int64_t)nchunks, kSlice);  // slices per row
+    const int64_t wrow0 = row0 + wave;  // the wave's first row; then every kWaves-th
+    const int64_t wend = row0 + kWaves * rpw < N ? row0 + kWaves * rpw : N;
+    const int32_t wrows = (int32_t)(wrow0 < wend ? (wend - wrow0 + kWaves - 1) / kWaves : 0);
+    // the workgroup's rows span below 2^31 bytes, so 32-bit offsets hold them
+    const int32_t nslices = wrows * spr;
+    const uint32_t row_bytes = (uint32_t)(row_words * 4);
+    const BufRef wbuf =
+        uniform_buf(packed + (wrows > 0 ? wrow0 : 0) * row_words,
+                    wrows > 0 ? (uint32_t)((wrows - 1) * kWaves + 1) * row_bytes : 0u);
+    const BufRef xall = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+
+    // x staged once per workgroup, as in gemv_xres_body (exact piece count)
+    const int pieces = (int)(MT * nchunks * 4);
+    uint4 xv[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int p = tid + r * kThreads;
+        const uint32_t off = (uint32_t)((p >> 2) * kChunk * 2 + (p & 3) * 16);
+        const u32x4v_t d = buf_load_b128(xall, p < pieces ? off : kOutsideOffset, 0u);
+        xv[r] = make_uint4(d.x, d.y, d.z, d.w);
+    }
+
+    // load position, wave-uniform: slices issued, the next slice's place in
+    // its row and the byte offset of its first chunk
+    const uint32_t lane_off = (uint32_t)(lane * B * 4);
+    int32_t ld_n = 0, ld_sir = 0;
+    uint32_t ld_row = 0, ld_off = 0;
+    uint32_t w[kStages][B];
+    int32_t sir_of[kStages];
+    auto load_w = [&](auto S) {
+        constexpr int st = decltype(S)::value;
+        const bool live = ld_n < nslices && lane < nchunks - ld_sir * kSlice;
+        buf_load_words<B>(wbuf, live ? ld_off + lane_off : kOutsideOffset, 0u, w[st]);
+        sir_of[st] = ld_sir;
+        ++ld_n;
+        if (++ld_sir == spr) {
+            ld_sir = 0;
+            ld_row += kWaves * row_bytes;
+            ld_off = ld_row;
+        } else {
+            ld_off += kSlice * B * 4;
+        }
+    };
+    static_for<kStages - 1>([&](auto S) { load_w(S); });
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int p = tid + r * kThreads;
+        if (p < pieces)
+            *reinterpret_cast<uint4*>(xs_dyn + (p >> 2) * kXPitch + (p & 3) * 8) = xv[r];
+    }
+    __syncthreads();
+
+    constexpr float kUnscale = product_unscale<B, false>();
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    int32_t row = 0;  // the row of the slice being multiplied
+    const uint16_t* xlane = xs_dyn + lane * kXPitch;
+    auto step = [&](auto S) {
+        constexpr int st = decltype(S)::value;
+        load_w(std::integral_constant<int, (st + kStages - 1) % kStages>{});
+        const int32_t sir = sir_of[st];
+        if (lane < nchunks - sir * kSlice) {
+            uint32_t xw[MT][16];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(xlane + (m * nchunks + sir * kSlice) * kXPitch);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 d = src[i];
+                    xw[m][4 * i + 0] = d.x;
+                    xw[m][4 * i + 1] = d.y;
+                    xw[m][4 * i + 2] = d.z;
+                    xw[m][4 * i + 3] = d.w;
+                }
+            }
+            chunk_product<B, MT, false>(w[st], 0, xw, acc);
+        }
+        if (sir == spr - 1) {  // the row's last slice: reduce, scale, store
+            float v[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                v[m] = wave_sum(acc[m]);
+                acc[m] = 0.0f;
+            }
+            // the scale at a wave-uniform address in uniform control flow: a
+            // scalar load, which leaves the vector loads in flight alone
+            const int64_t n = wrow0 + (int64_t)row * kWaves;
+            const float s = scales[n];
+            if (lane == 0) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (m < M) y[(int64_t)m * N + n] = s * (v[m] * kUnscale);
+            }
+            ++row;
+        }
+    };
+    int32_t sl = 0;
+    for (; sl + kStages <= nslices; sl += kStages) static_for<kStages>([&](auto S) { step(S); });
+    static_for<kStages - 1>([&](auto S) {
+        if (sl + decltype(S)::value < nslices) step(S);
+    });
 }
 
 }  // namespace
