@@ -219,8 +219,9 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
  * Items may share x, packed and scales; no y may overlap another item's y or
  * any input.  With M <= 2, every item whose K is a multiple of 32 and whose x
  * fits the LDS (M * K / 32 * 80 bytes <= 48 KB) runs in ONE kernel launch
- * (workgroups of all such items in one grid, widths mixed); each other item
- * runs as its own dq_gemv launch.  With 3 <= M <= 16 each item runs as its
+ * (workgroups of all such items in one grid, widths mixed); with
+ * 3 <= M <= 16, every item whose K is a multiple of 32 does (each item's
+ * outputs then equal dq_gemv's bit for bit).  Each other item runs as its
  * own dq_gemv launch.  Argument errors in any item are returned before
  * anything is enqueued. */
 #define DQ_GEMV_BATCH_MAX 32

@@ -11,12 +11,16 @@
 // memory is allocated or written besides the outputs).  Each workgroup finds
 // its item from a table of first-workgroup indices (a scalar scan over at most
 // 32 entries) and runs one of the bodies of gemv_kernels.hpp for the item's
-// width:
-//   * rows of at least 64 chunks (K >= 2048): the streaming body.  The host
+// width.  At M <= 2:
+//   * rows of at least 64 chunks (K >= 2048): a streaming body.  The host
 //     gives each item a share of one round of workgroups (as many as the GPU
 //     holds at once) in proportion to its bytes, so each wave streams several
-//     rows with its loads running ahead across row boundaries;
+//     rows with its loads running ahead across row boundaries (the row-sliced
+//     body when K is a multiple of 2048);
 //   * shorter rows: the resident-x body, one (or two) rows per wave.
+// At 3 <= M <= 16: the matrix-core body, one workgroup per row tile, as in
+// dq_gemv (so a layer's 5120-row matrices, 160 tiles each, fill the GPU
+// together where one alone leaves CUs idle).
 // Per chunk the arithmetic is that of the one-matrix resident-x kernel, so
 // every output is within the same bound; the summation order differs only in
 // that the streaming body adds each chunk's dot product to the row total
@@ -53,8 +57,8 @@ struct BatchItemArgs {
     int32_t N;
     int32_t K;
     int32_t row_words;
-    int32_t code;  // 4 * bits + mode
-    int32_t rpw;   // rows per wave (streaming mode)
+    int32_t code;  // M <= 2: 4 * bits + mode; M >= 3: 2 * bits + row tiles - 1
+    int32_t rpw;   // rows per wave (streaming modes)
 };
 
 struct BatchArgs {
@@ -137,6 +141,73 @@ __global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(co
     }
 }
 
+// 3 <= M <= 16: the matrix-core body of dq_gemv, one workgroup per tile of
+// 16 or 32 rows of an item (item code 2 * bits + kNT - 1, the tile height
+// dq_gemv picks for that item), so every output equals dq_gemv's bit for bit.
+// kMR: x rows staged, 8 (two steps of loads ahead) or 16 (one step ahead),
+// as dq_gemv picks by M.  The LDS is sized for the widest code the instance
+// serves; launches whose items are all at most 8 bits take the narrow one.
+template <int kMR>
+constexpr int mfma_batch_depth() { return kMR == 8 ? 2 : 1; }
+
+template <int kMR, int... Bm2>
+constexpr size_t mfma_batch_lds_of(std::integer_sequence<int, Bm2...>)
+{
+    size_t m = 0;
+    ((m = std::max(m, mfma_xlds_lds_bytes<Bm2 + 2, 2, mfma_batch_depth<kMR>(), kMR, false>())), ...);
+    return m;
+}
+template <int kMR, int kMaxB>
+constexpr size_t mfma_batch_lds()
+{
+    return mfma_batch_lds_of<kMR>(std::make_integer_sequence<int, kMaxB - 1>{});
+}
+
+template <int kMR, int kMaxB>
+__global__ __launch_bounds__(kGemvMfmaWaves * kWave) void gemv_mfma_batch_kernel(const BatchArgs args)
+{
+    constexpr int kDepth = mfma_batch_depth<kMR>();
+    __shared__ __attribute__((aligned(16))) unsigned char lds[mfma_batch_lds<kMR, kMaxB>()];
+    (void)args;
+    auto& a = batch_args();
+    const int32_t bid = (int32_t)blockIdx.x;
+    int i = 0;
+    while (i + 1 < a.count && bid >= a.first[i + 1]) ++i;
+    auto& it = a.item[i];
+    const int64_t tile = bid - a.first[i];
+    const NoZeroPoints zp{};
+    switch (it.code) {
+#define DQ_MFMA_BATCH_CASE(B)                                                                     \
+    case 2 * B:                                                                                   \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_mfma_xlds_body<B, 1, kDepth, kMR, NoZeroPoints>(                                 \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, tile, lds);  \
+        break;                                                                                    \
+    case 2 * B + 1:                                                                               \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_mfma_xlds_body<B, 2, kDepth, kMR, NoZeroPoints>(                                 \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, tile, lds);  \
+        break;
+        DQ_MFMA_BATCH_CASE(2)
+        DQ_MFMA_BATCH_CASE(3)
+        DQ_MFMA_BATCH_CASE(4)
+        DQ_MFMA_BATCH_CASE(5)
+        DQ_MFMA_BATCH_CASE(6)
+        DQ_MFMA_BATCH_CASE(7)
+        DQ_MFMA_BATCH_CASE(8)
+        DQ_MFMA_BATCH_CASE(9)
+        DQ_MFMA_BATCH_CASE(10)
+        DQ_MFMA_BATCH_CASE(11)
+        DQ_MFMA_BATCH_CASE(12)
+        DQ_MFMA_BATCH_CASE(13)
+        DQ_MFMA_BATCH_CASE(14)
+        DQ_MFMA_BATCH_CASE(15)
+#undef DQ_MFMA_BATCH_CASE
+    default:
+        break;
+    }
+}
+
 // the resident-x kernel's two-rows-per-wave rule (see launch_gemv_xres)
 bool two_rows(int64_t nchunks)
 {
@@ -154,11 +225,67 @@ bool row_sliced(int64_t nchunks) { return nchunks % kSlice == 0; }
 
 bool gemv_batch_eligible(int64_t M, int64_t K)
 {
-    return M <= 2 && K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax;
+    if (M > 2) return M <= 16 && K % kChunk == 0;
+    return K % kChunk == 0 && M * (K / kChunk) * kXPitch * 2 <= kXResMax;
 }
+
+namespace {
+
+// 3 <= M <= 16: eligible items' tiles in one grid (each item's tile height as
+// dq_gemv picks it), the rest one dq_gemv launch each
+hipError_t launch_gemv_batched_mfma(const GemvItem* items, int count, int64_t M, hipStream_t stream)
+{
+    bool narrow = true;
+    for (int i = 0; i < count; ++i)
+        if (gemv_batch_eligible(M, items[i].K) && items[i].bits > 8) narrow = false;
+    BatchArgs a;
+    a.M = (int32_t)M;
+    int n = 0;
+    int64_t blocks = 0;
+    auto flush = [&]() -> hipError_t {
+        if (n == 0) return hipSuccess;
+        a.count = n;
+        a.first[n] = (int32_t)blocks;
+        const dim3 grid((unsigned)blocks), block(kGemvMfmaWaves * kWave);
+        if (M <= 8 && narrow)
+            gemv_mfma_batch_kernel<8, 8><<<grid, block, 0, stream>>>(a);
+        else if (M <= 8)
+            gemv_mfma_batch_kernel<8, 15><<<grid, block, 0, stream>>>(a);
+        else if (narrow)
+            gemv_mfma_batch_kernel<16, 8><<<grid, block, 0, stream>>>(a);
+        else
+            gemv_mfma_batch_kernel<16, 15><<<grid, block, 0, stream>>>(a);
+        n = 0;
+        blocks = 0;
+        return hipGetLastError();
+    };
+    for (int i = 0; i < count; ++i) {
+        const GemvItem& g = items[i];
+        if (!gemv_batch_eligible(M, g.K)) {  // this item takes its own launch
+            const hipError_t e = launch_gemv(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.y, nullptr, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        const int nt = gemv_mfma_rows(g.N, g.K) / 16;
+        const int64_t nb = ceil_div(g.N, (int64_t)16 * nt);
+        if (blocks + nb > 0x7fffffffLL) {  // the grid's index space is full: launch what we have
+            const hipError_t e = flush();
+            if (e != hipSuccess) return e;
+        }
+        a.item[n] = BatchItemArgs{g.x, g.packed, g.scales, g.y, (int32_t)g.N, (int32_t)g.K,
+                                  (int32_t)packed_row_words(g.K, g.bits), 2 * g.bits + nt - 1, 0};
+        a.first[n] = (int32_t)blocks;
+        blocks += nb;
+        ++n;
+    }
+    return flush();
+}
+
+}  // namespace
 
 hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipStream_t stream)
 {
+    if (M > 2) return launch_gemv_batched_mfma(items, count, M, stream);
     // workgroups the GPU holds at once for this kernel (registers and LDS)
     size_t lds = 0;
     for (int i = 0; i < count; ++i)

@@ -25,6 +25,7 @@ constexpr uint32_t kOutsideOffset = 0xfffff000u;
 // A slice is 64 chunks (2048 codes), one per lane of a wave; x sits in LDS
 // one 80-byte slot per chunk (64 bytes of bf16 plus 16 bytes of padding).
 constexpr int kSlice = 64;            // chunks per slice (one per lane)
+constexpr int kGemvMfmaWaves = 4;     // waves of a matrix-core GEMV workgroup
 constexpr int kXPitch = 40;           // LDS slot per chunk in bf16 units (64 B + 16 B pad)
 
 // E (8 or 4) consecutive x elements of each of the MT rows starting at element
@@ -694,6 +695,254 @@ __device__ __forceinline__ void gemv_rowslice_body(
     static_for<kStages - 1>([&](auto S) {
         if (sl + decltype(S)::value < nslices) step(S);
     });
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core body, 3 <= M <= 16 and K a multiple of 32 (one workgroup of
+// kGemvMfmaWaves waves per tile of 16 kNT rows, the waves taking the K steps
+// in turn and adding their sums in LDS at the end).  The codes are expanded
+// to exact bf16 operands of v_mfma_f32_16x16x32_bf16, so the vector work per
+// code does not grow with M.  Loaded straight into registers in the MFMA lane
+// layout, each load instruction would spread its lanes over 16 rows (lane
+// 16 g + c: row c, chunk g) and x would cost as much as the code stream (each
+// lane needs 64 bytes of one row, so a 16-byte load touches 64 cache lines,
+// and lanes of rows past M load too).  Instead each wave copies the codes and x of its own steps
+// straight into a ring of LDS stages of its own (buffer_load ... lds): the
+// codes row by row (a step is 4 chunks = 16 B bytes of each of the 16 kNT
+// rows, so row r fills slots r B .. r B + B - 1), x for rows below kMR only
+// (4 rows of 256 bytes per instruction).  Lanes then read their chunk's B
+// words and the A operands (ds_read_b128) back.  x piece p of row i sits at
+// slot 16 i + (p ^ i), so the 16 lanes of a read that take the same piece of
+// 16 rows hit distinct banks.  The ring is private to the wave, so the loop
+// has no barriers; an explicit vmcnt wait before each step covers the LDS
+// copies, which the compiler does not track.  x pieces past K (the last step
+// of a K not a multiple of 128) and rows past M read an offset outside the x
+// buffer, which loads zeros; codes past a row's end meet those zeros, and
+// rows past N read zeros.
+template <int B, int kNT, int kDepth, int kMR, bool kAsym>
+struct MfmaXldsLayout {
+    static constexpr int kStages = kDepth + 1;
+    static constexpr int kSlots = kMR * 16;  // 16-byte x pieces of one step
+    static constexpr int kCodeSlots = (16 * kNT * B + 63) / 64 * 64;  // 16-byte code pieces of one step
+    // byte offsets: x ring (stage, wave, slot), code ring (stage, wave, slot),
+    // the waves' sums (wave - 1, row tile, register, lane)
+    static constexpr size_t kXBytes = (size_t)kStages * kGemvMfmaWaves * kSlots * 16;
+    static constexpr size_t kCodeBytes = (size_t)kStages * kGemvMfmaWaves * kCodeSlots * 16;
+    static constexpr size_t kRedBytes = (size_t)(kGemvMfmaWaves - 1) * kNT * 4 * kWave * 4;
+    static constexpr size_t kBytes = kXBytes + kCodeBytes + kRedBytes;
+};
+
+// LDS bytes of one workgroup of gemv_mfma_xlds_body
+template <int B, int kNT, int kDepth, int kMR, bool kAsym>
+__host__ __device__ constexpr size_t mfma_xlds_lds_bytes()
+{
+    return MfmaXldsLayout<B, kNT, kDepth, kMR, kAsym>::kBytes;
+}
+
+// Tile `tile` (rows 16 kNT tile ..) of y = s * (x q^T); lds holds
+// mfma_xlds_lds_bytes() bytes, 16-byte aligned.
+template <int B, int kNT, int kDepth, int kMR, class ZP>
+__device__ __forceinline__ void gemv_mfma_xlds_body(
+    const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
+    float* __restrict__ y, ZP zp, int64_t tile, unsigned char* __restrict__ lds)
+{
+    using L = MfmaXldsLayout<B, kNT, kDepth, kMR, ZP::kAsym>;
+    typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
+    typedef float f32x4m_t __attribute__((ext_vector_type(4)));
+    constexpr bool kSplit = split_codes<B, ZP::kAsym>();
+    constexpr int kStages = L::kStages;
+    constexpr int kXCopies = kMR / 4;
+    constexpr int kCodeSlots = L::kCodeSlots;
+    constexpr int kCodeCopies = kCodeSlots / 64;
+    // group-wise scales (groups of whole 128-code steps): each step's scales of
+    // this lane's rows come into registers with the step's codes (kNT more
+    // loads).  Not through the LDS ring: the fold that reads them is plain
+    // arithmetic the compiler may sink past the next step's copies, and a copy
+    // into a slot whose read is still in flight would race with it.
+    constexpr bool kGroup = is_group_scales<ZP>::value;
+    constexpr int kPerStage = kCodeCopies + kXCopies + (kGroup ? kNT : 0);
+    constexpr int kSlots = L::kSlots;
+    static_assert(kDepth >= 1 && kDepth <= 2, "one or two steps ahead");
+    static_assert(kMR == 8 || kMR == 16, "x rows staged: 8 or 16");
+    static_assert(kDepth * kPerStage < 64, "vmcnt holds at most 63");
+    uint4* const xs = reinterpret_cast<uint4*>(lds);
+    uint4* const cs = reinterpret_cast<uint4*>(lds + L::kXBytes);
+    float* const red = reinterpret_cast<float*>(lds + L::kXBytes + L::kCodeBytes);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    auto cring = [&](auto S) -> uint4* {
+        return cs + (decltype(S)::value * kGemvMfmaWaves + wave) * kCodeSlots;
+    };
+    auto ring = [&](auto S) -> uint4* { return xs + (decltype(S)::value * kGemvMfmaWaves + wave) * kSlots; };
+    auto red_at = [&](int w, int j, int r) -> float* { return red + ((w * kNT + j) * 4 + r) * kWave; };
+
+    const int64_t n0 = tile * 16 * kNT;
+    const int64_t nchunks = K / kChunk;
+    const int64_t nsteps = ceil_div(nchunks, 4);
+    const int64_t nrows = N - n0 < 16 * kNT ? N - n0 : 16 * kNT;
+    const BufRef wb = uniform_buf(packed + n0 * row_words, (uint32_t)(nrows * row_words * 4));
+    const BufRef xb = uniform_buf(x, (uint32_t)((int64_t)M * K * 2));
+    constexpr uint32_t kOutside = 0xfffff000u;
+
+    // copy instruction q: lane l fills slot 64 q + l = row r, position l % 16,
+    // which holds piece p = (l % 16) ^ r of that row (chunk 4 ks + p / 4)
+    uint32_t xbase[kXCopies];
+    int xchunk[kXCopies];
+#pragma unroll
+    for (int q = 0; q < kXCopies; ++q) {
+        const int r = 4 * q + (lane >> 4);
+        const int pc = (lane & 15) ^ r;
+        xbase[q] = r < M ? (uint32_t)(r * K * 2 + 16 * pc) : kOutside;
+        xchunk[q] = pc >> 2;
+    }
+    // A operand of substep t: row c (rows past kMR repeat rows below it; their
+    // sums land in output rows that are never stored), piece 4 g + t
+    const int ar = c & (kMR - 1);
+    int aslot[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aslot[t] = 16 * ar + ((4 * g + t) ^ ar);
+
+    // codes: copy q fills slot s = 64 q + l with piece s % B of row s / B of
+    // the step (16-byte pieces; slots past the tile's rows get zeros)
+    uint32_t cbase[kCodeCopies];
+#pragma unroll
+    for (int q = 0; q < kCodeCopies; ++q) {
+        const int sl = 64 * q + lane;
+        const int r = sl / B, pc = sl % B;
+        cbase[q] = r < 16 * kNT ? (uint32_t)(r * row_words * 4 + pc * 16) : kOutside;
+    }
+    int32_t zr[kNT];  // zero point of this lane's row in each row tile
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) zr[j] = zp.zero(n0 + 16 * j + c < N ? n0 + 16 * j + c : N - 1);
+    [[maybe_unused]] BufRef sb{};
+    [[maybe_unused]] int gshift = 0;  // log2 of the 128-code steps per group
+    if constexpr (kGroup) {
+        sb = uniform_buf(zp.scales + n0 * zp.G, (uint32_t)(nrows * zp.G * 4));
+        gshift = __builtin_ctzll((unsigned long long)(zp.group / 128));
+    }
+    float gsc[kGroup ? kStages : 1][kGroup ? kNT : 1];  // group scales by stage
+    auto load = [&](auto P, int64_t ks) {
+        if constexpr (kGroup) {  // the scale of row 16 j + c for step ks's group
+            const int64_t gi = ks >> gshift;
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                const bool in = 16 * j + c < nrows && gi < zp.G;
+                uint32_t t[1];
+                buf_load_words<1>(sb, in ? (uint32_t)(((16 * j + c) * zp.G + gi) * 4) : kOutside, 0u, t);
+                gsc[kGroup ? decltype(P)::value : 0][kGroup ? j : 0] = __uint_as_float(t[0]);
+            }
+        }
+        uint4* cdst = cring(P);
+#pragma unroll
+        for (int q = 0; q < kCodeCopies; ++q)
+            buf_load_lds16(wb, cdst + 64 * q, cbase[q] != kOutside ? cbase[q] + (uint32_t)(ks * 16 * B) : kOutside, 0u);
+        uint4* dst = ring(P);
+#pragma unroll
+        for (int q = 0; q < kXCopies; ++q) {
+            const bool in = xbase[q] != kOutside && 4 * ks + xchunk[q] < nchunks;
+            buf_load_lds16(xb, dst + 64 * q, in ? xbase[q] + (uint32_t)(ks * 256) : kOutside, 0u);
+        }
+    };
+    f32x4m_t acc[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
+    // vmcnt(n) with expcnt and lgkmcnt left at their maxima
+    auto compute = [&](auto P, auto Wait) {
+        constexpr int n = decltype(Wait)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+        const uint4* src = ring(P);
+        // this lane's chunk (chunk g of the step) of row c of each row tile
+        uint32_t wl[kNT][B];
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(cring(P));
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int i = 0; i < B; ++i) wl[j][i] = cw[(16 * j + c) * 4 * B + g * B + i];
+        f32x4m_t part[kNT];  // group-wise scales: this step's sums, scaled below
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) part[j] = (f32x4m_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8m_t a = __builtin_bit_cast(bf16x8m_t, src[aslot[t]]);
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                bf16x8_t bh, bl;
+                expand8z<B, ZP::kAsym>(wl[j], zr[j], t, bh, bl);
+                f32x4m_t& d = kGroup ? part[j] : acc[j];
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, d, 0, 0, 0);
+                if constexpr (kSplit) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, d, 0, 0, 0);
+            }
+        }
+        if constexpr (kGroup) {
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) {
+                const float sg = gsc[kGroup ? decltype(P)::value : 0][kGroup ? j : 0];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sg, part[j][r], acc[j][r]);
+            }
+        }
+    };
+
+    // Stage i of the ring holds step ks + i kW; each step's loads are issued
+    // before the computation of the step kDepth before it.
+    constexpr int64_t kW = kGemvMfmaWaves;
+    int64_t ks = wave;
+    load(std::integral_constant<int, 0>{}, ks);
+    if constexpr (kDepth > 1) load(std::integral_constant<int, 1>{}, ks + kW);
+    if constexpr (kDepth > 2) load(std::integral_constant<int, 2>{}, ks + 2 * kW);
+    __builtin_amdgcn_sched_barrier(0);
+    auto stage = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        load(std::integral_constant<int, (i + kDepth) % kStages>{}, ks + (i + kDepth) * kW);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(I, std::integral_constant<int, kDepth * kPerStage>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; ks + kDepth * kW < nsteps; ks += kStages * kW) {
+        stage(std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 1>{});
+        if constexpr (kStages > 2) stage(std::integral_constant<int, 2>{});
+        if constexpr (kStages > 3) stage(std::integral_constant<int, 3>{});
+    }
+    // the last loads in flight are those of stages 0 .. kDepth-1, in order
+    if (ks < nsteps) compute(std::integral_constant<int, 0>{}, std::integral_constant<int, (kDepth - 1) * kPerStage>{});
+    if constexpr (kDepth > 1)
+        if (ks + kW < nsteps) compute(std::integral_constant<int, 1>{}, std::integral_constant<int, (kDepth - 2) * kPerStage>{});
+    if constexpr (kDepth > 2)
+        if (ks + 2 * kW < nsteps) compute(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
+    // copies past the last step may still be in flight: drain them before
+    // the workgroup's LDS can be handed to another workgroup
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red_at(wave - 1, j, r)[lane] = acc[j][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr float kUnscale = 1.0f / expand8_scale<B, ZP::kAsym>();
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+            const int64_t n = n0 + 16 * j + c;
+            if (n >= N) continue;
+            const float s = kGroup ? 1.0f : scales[n];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = acc[j][r];
+#pragma unroll
+                for (int q = 0; q < kGemvMfmaWaves - 1; ++q) v += red_at(q, j, r)[lane];
+                const int m = 4 * g + r;
+                if (m < M) y[(int64_t)m * N + n] = s * (v * kUnscale);
+            }
+        }
+    }
 }
 
 }  // namespace

@@ -54,6 +54,8 @@ struct GemvItem {
 constexpr int kGemvBatchMax = 32;  // items per call (DQ_GEMV_BATCH_MAX)
 // Whether an item of this shape joins the single launch (else it gets its own).
 bool gemv_batch_eligible(int64_t M, int64_t K);
+// rows per workgroup of the matrix-core GEMV (3 <= M <= 16) for an N x K matrix
+int gemv_mfma_rows(int64_t N, int64_t K);
 // Symmetric per-row products of `count` matrices sharing M (<= 2 for the
 // single launch; items outside it run one launch each).
 hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipStream_t stream);

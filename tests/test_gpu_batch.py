@@ -1,8 +1,10 @@
 """Parity of the batched decode product (dq_gemv_batched): several matrices
 of mixed widths and shapes in one call, each output within 1e-4 * sum_k
 |x * w_hat| of the oracle's fp64 product.  Items on the one-row-per-wave path
-(rows under 64 chunks) and items outside the single launch (K not a multiple
-of 32, x too large for LDS, M >= 3) are bit-identical to dq_gemv; streamed
+(rows under 64 chunks), items at 3 <= M <= 16 (the matrix-core body of
+dq_gemv, one launch for all items with K a multiple of 32) and items outside
+the single launch (K not a multiple of 32, x too large for LDS) are
+bit-identical to dq_gemv; streamed
 items (rows of 64 chunks or more) add each chunk's sum into the row total,
 so they are checked against the oracle and for the same bits on every call.
 Covered: every width, rows that end inside a slice (65, 160, 544 chunks per
@@ -75,20 +77,24 @@ def test_batched_mixed_widths(M):
     assert_batch(items, M, seed=M)
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 8, 16])
 def test_batched_stream_row_boundaries(M):
-    """Streamed rows that end inside a slice (65, 160, 544 chunks), exactly a
-    slice (64), many rows per wave next to few, ragged last workgroups."""
+    """M <= 2: streamed rows that end inside a slice (65, 160, 544 chunks),
+    exactly a slice (64), whole slices (2048 and 4096 codes), many rows per
+    wave next to few, ragged last workgroups.  M >= 3: the same items as
+    16- and 32-row tiles (ragged last tiles), bit for bit as dq_gemv."""
     items = [(1000, 2048, 6, 0), (77, 2080, 5, 1), (3, 5120, 7, 2), (4097, 5120, 4, 2),
              (250, 17408, 8, 3), (513, 4096, 15, 4), (2, 2080, 2, 1), (1, 4096, 9, 4)]
     assert_batch(items, M, seed=50 + M)
 
 
-def test_batched_largest_batch_and_one_item():
+@pytest.mark.parametrize("M", [1, 16])
+def test_batched_largest_batch_and_one_item(M):
     items = [(N, K, b, 0) for (N, K, b) in MIXED] * 3
-    assert_batch(items[:dq.GEMV_BATCH_MAX], 1, seed=40)
-    assert_batch(items[:1], 1, seed=41)
-    assert_batch([(3, 1 << 22, 5, 0), (70, 2048, 6, 0)], 1, seed=42)  # x too large for LDS
+    assert_batch(items[:dq.GEMV_BATCH_MAX], M, seed=40)
+    assert_batch(items[:1], M, seed=41)
+    if M == 1:
+        assert_batch([(3, 1 << 22, 5, 0), (70, 2048, 6, 0)], M, seed=42)  # x too large for LDS
 
 
 def test_batched_decode_workload():
@@ -116,10 +122,11 @@ def test_batched_decode_workload():
         assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()
 
 
-def test_batched_layer_shapes():
+@pytest.mark.parametrize("M", [1, 8])
+def test_batched_layer_shapes(M):
     """One layer of the 448-matrix stack (4 x 5120^2, 2 x 17408 x 5120,
-    5120 x 17408) at widths 5 .. 8 in one call, M = 1: the same bits on
-    every call, sampled rows against the oracle."""
+    5120 x 17408) at widths 5 .. 8 in one call: the same bits on every call,
+    sampled rows against the oracle; at M = 8 the same bits as dq_gemv."""
     t = torch()
     shapes = [(5120, 5120, 6), (5120, 5120, 5), (5120, 5120, 6), (5120, 5120, 7),
               (17408, 5120, 6), (17408, 5120, 8), (5120, 17408, 5)]
@@ -129,14 +136,16 @@ def test_batched_layer_shapes():
     for i, (N, K, b) in enumerate(shapes):
         W = (t.randn((N, K), generator=g, device="cuda") * 0.02).to(t.bfloat16)
         P, S = dq.quantize_pack(W, b)
-        x = workload.activations(63, i, 1, K)
+        x = workload.activations(63, i, M, K)
         items.append((bf16_gpu(x), P, S, K, b, x))
-    report("gemv_batched layer shapes")
+    report("gemv_batched layer shapes M=%d" % M)
     ys = dq.gemv_batched([it[:5] for it in items])
     again = dq.gemv_batched([it[:5] for it in items])
+    singles = [dq.gemv(X, P, S, K, b) for (X, P, S, K, b, _) in items] if M > 2 else ys
     t.cuda.synchronize()
-    for (X, P, S, K, b, x), y, y2 in zip(items, ys, again):
+    for (X, P, S, K, b, x), y, y2, y1 in zip(items, ys, again, singles):
         assert np.array_equal(f32_bits(y), f32_bits(y2))
+        assert np.array_equal(f32_bits(y), f32_bits(y1))
         rows = np.random.default_rng(K + b).choice(P.shape[0], 32, replace=False)
         o_p = P.cpu().numpy().view(np.uint32)[rows]
         y_ref, bound = oracle.matmul(x, o_p, S.cpu().numpy()[rows], len(rows), K, b)
