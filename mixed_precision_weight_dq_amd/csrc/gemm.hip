@@ -16,10 +16,14 @@
 // codes in LDS (k contiguous for both), and each wave issues
 // v_mfma_f32_16x16x32_bf16 over its 64 x 64 sub-tile.  That is the simple
 // fallback (K not a multiple of 64); the main kernels below pipeline the
-// codes through registers and x through LDS.  Variants: asymmetric codes add
-// a zero-point term in the epilogues (ZeroPoints / TileZeroPoints policies);
-// group-wise scales fold each group's sum in as it ends (GroupScales in the
-// 128-row kernel; gemm_group_kernel for groups of 32 codes).
+// codes through registers and x through LDS.  Variants: asymmetric codes
+// have the row's zero point taken off each code before expansion, so every
+// product stays exact (ZeroPoints policy); group-wise scales fold each
+// group's sum in as it ends (GroupScales in the 128-row kernel, whose two
+// waves per SIMD hide the fold's vector work behind each other's matrix
+// work; gemm_group_kernel for groups of 32 codes).  The wide kernel holds no
+// group-wise variant: its accumulators fill the accumulation registers, so a
+// second set for the group's sum would not fit beside them.
 #include <type_traits>
 
 #include "common.hpp"

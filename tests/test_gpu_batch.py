@@ -23,7 +23,7 @@ import pytest
 import mixed_precision_weight_dq_amd as dq
 import oracle
 import workload
-from gpu_util import bf16_gpu, f32_bits, report, torch, weights_gpu
+from gpu_util import bf16_gpu, f32_bits, report, torch, u32, weights_gpu
 from pins import within_tolerance
 
 pytestmark = pytest.mark.gpu
@@ -36,9 +36,24 @@ MIXED = [(300, 4096, 4), (37, 1000, 5), (70, 2048, 15), (1, 32, 2), (40, 6144, 6
 
 
 def quantized(seed, N, K, bits):
+    """Packed codes and scales by the oracle (CPU), uploaded: (packed, scales)
+    on the GPU and the same arrays on the host."""
     w = workload.weights(61, seed, N, K, dtype="bf16")
-    P, S = dq.quantize_pack(weights_gpu(w), bits)
-    return P, S
+    o_packed, o_scales, _ = oracle.quantize_pack(w, bits)
+    t = torch()
+    P = t.from_numpy(o_packed.view(np.int32)).cuda()
+    S = t.from_numpy(o_scales).cuda()
+    return P, S, o_packed, o_scales
+
+
+def oracle_rows(w_rows, rows, P, S, bits):
+    """The oracle's packed codes and scales of the sampled rows (w_rows: their
+    bf16 bits), which must equal the GPU's rows of P and S."""
+    o_packed, o_scales, _ = oracle.quantize_pack(np.ascontiguousarray(w_rows), bits)
+    idx = torch().from_numpy(np.asarray(rows)).cuda()
+    assert np.array_equal(u32(P.index_select(0, idx)), o_packed), "packed rows differ"
+    assert np.array_equal(f32_bits(S.index_select(0, idx)), o_scales.view(np.uint32))
+    return o_packed, o_scales
 
 
 def streamed(M, K):
@@ -52,21 +67,19 @@ def assert_batch(items_np, M, seed, check_oracle=True):
     for i, (N, K, bits, xk) in enumerate(items_np):
         if (xk, K) not in xs:
             xs[(xk, K)] = workload.activations(62, seed * 100 + xk + K, M, K)
-        P, S = quantized(seed * 1000 + i, N, K, bits)
+        P, S, o_p, o_s = quantized(seed * 1000 + i, N, K, bits)
         items.append((bf16_gpu(xs[(xk, K)]), P, S, K, bits))
-        meta.append((N, K, bits, xs[(xk, K)]))
+        meta.append((N, K, bits, xs[(xk, K)], o_p, o_s))
     report("gemv_batched M=%d items=%d seed=%d" % (M, len(items), seed))
     ys = dq.gemv_batched(items)
     again = dq.gemv_batched(items)
     singles = [dq.gemv(x, P, S, K, b) for (x, P, S, K, b) in items]
     torch().cuda.synchronize()
-    for i, ((N, K, bits, x), y, y2, y1, it) in enumerate(zip(meta, ys, again, singles, items)):
+    for i, ((N, K, bits, x, o_p, o_s), y, y2, y1) in enumerate(zip(meta, ys, again, singles)):
         assert np.array_equal(f32_bits(y), f32_bits(y2)), "item %d not deterministic" % i
         if not streamed(M, K):
             assert np.array_equal(f32_bits(y), f32_bits(y1)), "item %d differs from dq_gemv" % i
         if check_oracle:
-            o_p = it[1].cpu().numpy().view(np.uint32)
-            o_s = it[2].cpu().numpy()
             y_ref, bound = oracle.matmul(x, o_p, o_s, N, K, bits)
             assert within_tolerance(y.cpu().numpy(), y_ref, bound).all(), "item %d" % i
 
@@ -104,20 +117,20 @@ def test_batched_decode_workload():
     N = K = 4096
     x = workload.activations(2, 0, 1, K)
     X = bf16_gpu(x)
-    items, packs = [], []
+    items, w_rows = [], []
+    rows = np.random.default_rng(3).choice(N, 64, replace=False)
     for b in (4, 5, 6, 7, 8):
         w = workload.weights(2, b, N, K, outlier_frac=0.001)
         P, S = dq.quantize_pack(weights_gpu(w), b)
         items.append((X, P, S, K, b))
+        w_rows.append(w[rows])
     report("gemv_batched decode workload")
     ys = dq.gemv_batched(items)
     again = dq.gemv_batched(items)
     torch().cuda.synchronize()
-    rows = np.random.default_rng(3).choice(N, 64, replace=False)
-    for (X_, P, S, K_, b), y, y2 in zip(items, ys, again):
+    for (X_, P, S, K_, b), y, y2, wr in zip(items, ys, again, w_rows):
         assert np.array_equal(f32_bits(y), f32_bits(y2))
-        o_p = P.cpu().numpy().view(np.uint32)[rows]
-        o_s = S.cpu().numpy()[rows]
+        o_p, o_s = oracle_rows(wr, rows, P, S, b)
         y_ref, bound = oracle.matmul(x, o_p, o_s, len(rows), K, b)
         assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()
 
@@ -132,12 +145,17 @@ def test_batched_layer_shapes(M):
               (17408, 5120, 6), (17408, 5120, 8), (5120, 17408, 5)]
     g = t.Generator(device="cuda")
     g.manual_seed(7)
-    items = []
+    items, W_rows = [], {}
     for i, (N, K, b) in enumerate(shapes):
         W = (t.randn((N, K), generator=g, device="cuda") * 0.02).to(t.bfloat16)
         P, S = dq.quantize_pack(W, b)
+        rows = np.random.default_rng(K + b).choice(N, 32, replace=False)
+        # the sampled rows' bf16 bits, for the oracle
+        W_rows[(K, b, P.data_ptr())] = W.index_select(0, t.from_numpy(rows).cuda()).view(t.int16) \
+            .cpu().numpy().view(np.uint16)
         x = workload.activations(63, i, M, K)
         items.append((bf16_gpu(x), P, S, K, b, x))
+        del W
     report("gemv_batched layer shapes M=%d" % M)
     ys = dq.gemv_batched([it[:5] for it in items])
     again = dq.gemv_batched([it[:5] for it in items])
@@ -147,6 +165,6 @@ def test_batched_layer_shapes(M):
         assert np.array_equal(f32_bits(y), f32_bits(y2))
         assert np.array_equal(f32_bits(y), f32_bits(y1))
         rows = np.random.default_rng(K + b).choice(P.shape[0], 32, replace=False)
-        o_p = P.cpu().numpy().view(np.uint32)[rows]
-        y_ref, bound = oracle.matmul(x, o_p, S.cpu().numpy()[rows], len(rows), K, b)
+        o_p, o_s = oracle_rows(W_rows[(K, b, P.data_ptr())], rows, P, S, b)
+        y_ref, bound = oracle.matmul(x, o_p, o_s, len(rows), K, b)
         assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()

@@ -129,6 +129,37 @@ def test_gemm_group_parity(bits):
             assert_group_product("gemm", M, N, K, bits, g, bits * 1000 + 500 + i + g)
 
 
+@pytest.mark.parametrize("bits", [2, 6, 9, 10, 15])
+def test_gemm_group_prefill_shapes(bits):
+    """Prefill-sized group-wise GEMMs (M = 256 .. 512, N up to 32768): the
+    pipelined 128-row kernel with the group fold over hundreds of tiles
+    (groups of one, two, eight and sixteen 64-code steps; ragged last row and
+    column tiles), sampled weight rows (first and last included) against the
+    oracle, every m."""
+    t = torch()
+    for i, (M, N, K, g) in enumerate(((512, 16384, 1024, 64), (300, 16300, 1024, 128),
+                                      (256, 32768, 512, 512), (512, 16384, 1024, 1024))):
+        seed = bits * 100 + 70 + i
+        w = group_weights(seed, N, K, g)
+        w[2] = workload.bf16_from_f32(np.full(K, 0.01, np.float32))  # no infinity in products
+        x = workload.activations(52, seed, M, K)
+        o_packed, o_scales, _ = oracle.quantize_pack_group(w, bits, g)
+        report("gemm_group prefill M=%d N=%d K=%d g=%d b=%d" % (M, N, K, g, bits))
+        y = dq.gemm_group(bf16_gpu(x), t.from_numpy(o_packed.view(np.int32)).cuda(),
+                          t.from_numpy(o_scales).cuda(), K, bits, g)
+        t.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.random.default_rng(seed).choice(N, 62, replace=False),
+                                         [0, 1, 2, N - 1]]))
+        y_ref, bound = oracle.matmul_group(x, np.ascontiguousarray(o_packed[rows]),
+                                           np.ascontiguousarray(o_scales[rows]), len(rows), K, bits, g)
+        got = y.cpu().numpy()[:, rows]
+        ok = within_tolerance(got, y_ref, bound)
+        if not ok.all():
+            m, j = np.argwhere(~ok)[0]
+            pytest.fail("gemm_group prefill M=%d N=%d K=%d g=%d b=%d: y[%d,%d]=%r ref %r bound %r" % (
+                M, N, K, g, bits, m, rows[j], got[m, j], y_ref[m, j], bound[m, j]))
+
+
 @pytest.mark.parametrize("kind", ["gemv", "gemm"])
 @pytest.mark.parametrize("bits", [2, 6, 9, 10, 15])
 def test_group_one_hot_is_exact(kind, bits):
