@@ -13,8 +13,8 @@
 // 32 entries) and runs one of the bodies of gemv_kernels.hpp for the item's
 // width.  At M <= 2:
 //   * rows of at least 64 chunks (K >= 2048): a streaming body.  The host
-//     gives each item a share of one round of workgroups (as many as the GPU
-//     holds at once) in proportion to its bytes, so each wave streams several
+//     gives each item a share of two rounds of workgroups (twice as many as
+//     the GPU holds at once) in proportion to its bytes, so each wave streams several
 //     rows with its loads running ahead across row boundaries (the row-sliced
 //     body when K is a multiple of 2048);
 //   * shorter rows: the resident-x body, one (or two) rows per wave.
@@ -305,7 +305,9 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBatchWaves * kWave, lds);
     if (e != hipSuccess) return e;
-    const int64_t slots = (int64_t)std::max(1, cus) * std::max(1, per_cu);
+    // two rounds of the workgroups the GPU holds at once: the second round
+    // starts as the first one's workgroups end, which evens out their finish
+    const int64_t slots = (int64_t)std::max(1, cus) * std::max(1, per_cu) * 2;
     double stream_bytes = 0;  // bytes of the streamed items, shared out over the slots
     for (int i = 0; i < count; ++i)
         if (gemv_batch_eligible(M, items[i].K) && items[i].K / kChunk >= kSlice)
@@ -344,8 +346,8 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
         int mode, rpw = 1;
         int64_t nb;
         if (nchunks >= kSlice) {
-            // this item's share of one round of workgroups, in proportion to
-            // its bytes; a workgroup's rows stay below 2^31 bytes
+            // this item's share of the workgroups, in proportion to its
+            // bytes; a workgroup's rows stay below 2^31 bytes
             const double share = (double)g.N * rw * 4 / stream_bytes;
             const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
             int64_t r = ceil_div(g.N, wgs * kBatchWaves);
