@@ -586,7 +586,8 @@ def gemv_batched(items, ys=None):
     """Several decode products in one call: items is a list of (x, packed,
     scales, K, bits) (bf16 x [M, K] with the same M for all; x and weights may
     be shared between items); returns the list of y [M, N] (or fills ``ys``).
-    Items that fit the resident-x kernel share one launch."""
+    Items with K a multiple of 32 share one launch (at M <= 2 also x within
+    the LDS); the others run as one dq_gemv launch each."""
     torch = _torch()
     if not 1 <= len(items) <= GEMV_BATCH_MAX:
         raise ValueError("1 to %d items" % GEMV_BATCH_MAX)
