@@ -38,8 +38,12 @@ namespace dq {
 
 namespace {
 
-constexpr int kBatchWaves = 4;     // waves per workgroup
-constexpr int kBatchXPieces = 10;  // x pieces per thread: covers kXResMax
+// waves per workgroup: x is copied into LDS once per workgroup, so eight
+// waves share each copy (the copies of a launch halve against four waves:
+// decode 3.7 -> 4.2 TB/s; twelve or sixteen waves leave fewer workgroups per
+// CU than the registers allow and ran slower)
+constexpr int kBatchWaves = 8;
+constexpr int kBatchXPieces = 5;  // x pieces per thread: covers kXResMax
 static_assert(kBatchXPieces * kBatchWaves * kWave >= kXResMax / (kXPitch * 2) * 4,
               "x staging covers the largest x");
 
