@@ -178,6 +178,20 @@ __device__ __forceinline__ float wave_sum(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sums over the two halves of a wave (lanes 0 .. 31 and 32 .. 63), in a fixed
+// order: the first five steps of wave_sum leave the first half's total in
+// lane 31 and the second half's in lane 63.
+__device__ __forceinline__ void half_sums(float v, float& lo, float& hi)
+{
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
 #pragma unroll

@@ -52,6 +52,7 @@ constexpr int kModeRow = 0;     // one row per wave (resident-x body)
 constexpr int kModeTwoRows = 1; // two rows per wave (resident-x body)
 constexpr int kModeStream = 2;    // rpw rows per wave, streamed (K >= 2048)
 constexpr int kModeRowSlice = 3;  // rpw rows per wave in whole-row slices (K % 2048 == 0)
+constexpr int kModeRowSlice2 = 4; // the same, two rows per slice (K % 1024 == 0)
 
 struct BatchItemArgs {
     const uint16_t* x;
@@ -61,7 +62,7 @@ struct BatchItemArgs {
     int32_t N;
     int32_t K;
     int32_t row_words;
-    int32_t code;  // M <= 2: 4 * bits + mode; M >= 3: 2 * bits + row tiles - 1
+    int32_t code;  // M <= 2: 8 * bits + mode; M >= 3: 2 * bits + row tiles - 1
     int32_t rpw;   // rows per wave (streaming modes)
 };
 
@@ -101,27 +102,33 @@ __global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(co
     const NoZeroPoints zp{};
     switch (it.code) {
 #define DQ_BATCH_CASE(B)                                                                          \
-    case 4 * B + kModeRow:                                                                        \
+    case 8 * B + kModeRow:                                                                        \
         if constexpr (B <= kMaxB)                                                                 \
             gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 1, true>(             \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
                 xs_dyn);                                                                          \
         break;                                                                                    \
-    case 4 * B + kModeTwoRows:                                                                    \
+    case 8 * B + kModeTwoRows:                                                                    \
         if constexpr (B <= kMaxB)                                                                 \
             gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 2, true>(             \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
                 xs_dyn);                                                                          \
         break;                                                                                    \
-    case 4 * B + kModeStream:                                                                     \
+    case 8 * B + kModeStream:                                                                     \
         if constexpr (B <= kMaxB)                                                                 \
             gemv_stream_body<B, MT, kBatchWaves, kBatchXPieces>(                                  \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
                 local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
         break;                                                                                    \
-    case 4 * B + kModeRowSlice:                                                                   \
+    case 8 * B + kModeRowSlice:                                                                   \
         if constexpr (B <= kMaxB)                                                                 \
-            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces>(                                \
+            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 1>(                             \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
+                local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
+        break;                                                                                    \
+    case 8 * B + kModeRowSlice2:                                                                  \
+        if constexpr (B <= kMaxB)                                                                 \
+            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 2>(                             \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
                 local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
         break;
@@ -219,11 +226,16 @@ bool two_rows(int64_t nchunks)
     return fill(2 * nchunks) > fill(nchunks) + 0.1;
 }
 
-// Whether a streamed item takes the row-sliced body: its rows are a whole
-// number of slices (K a multiple of 2048), so no lane idles.  Other rows take
-// the streaming body, whose per-lane bookkeeping costs less than lanes idling
-// in each row's last slice.
-bool row_sliced(int64_t nchunks) { return nchunks % kSlice == 0; }
+// The body a streamed item takes: row-sliced when its rows are a whole number
+// of slices of one row (K a multiple of 2048) or of two rows (K a multiple of
+// 1024), so no lane idles; else the stream body, whose per-lane bookkeeping
+// costs less than lanes idling in each row's last slice.
+int stream_mode(int64_t nchunks)
+{
+    if (nchunks % kSlice == 0) return kModeRowSlice;
+    if (nchunks % (kSlice / 2) == 0) return kModeRowSlice2;
+    return kModeStream;
+}
 
 }  // namespace
 
@@ -356,8 +368,10 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
             const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
             int64_t r = ceil_div(g.N, wgs * kBatchWaves);
             r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
+            mode = stream_mode(nchunks);
+            if (mode == kModeRowSlice2 && r > 1 && (r & 1))  // whole pairs of rows per wave
+                r = std::min<int64_t>(r + 1, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
             rpw = (int)r;
-            mode = row_sliced(nchunks) ? kModeRowSlice : kModeStream;
             nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
         } else {
             const bool two = two_rows(nchunks);
@@ -369,7 +383,7 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
             if (e != hipSuccess) return e;
         }
         a.item[n] = BatchItemArgs{g.x, g.packed, g.scales, g.y, (int32_t)g.N, (int32_t)g.K,
-                                  (int32_t)rw, 4 * g.bits + mode, rpw};
+                                  (int32_t)rw, 8 * g.bits + mode, rpw};
         a.first[n] = (int32_t)blocks;
         blocks += nb;
         ++n;

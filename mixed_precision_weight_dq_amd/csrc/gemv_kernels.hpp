@@ -570,16 +570,19 @@ __device__ __forceinline__ void gemv_stream_body(
 // Streaming GEMV, row-sliced: the workgroup's rows row0 .. row0 + kWaves * rpw
 // are dealt to its waves in turn (wave w takes rows row0 + w, row0 + w +
 // kWaves, ...), so at any time the workgroup reads one contiguous block of
-// kWaves rows; each row is cut into slices of 64 chunks that never span two
-// rows (a row is ceil(K / 2048) slices; in a row's last slice the lanes past
-// its end idle).
-// Everything that locates a slice -- its row, its place in the row, its byte
-// offset -- is wave-uniform, so the per-chunk work is the load, the x reads
-// and the dot products; each lane's chunk adds into one running total per
-// row, reduced across the wave when the row's last slice is done.  Loads run
-// two slices ahead of the arithmetic, across row boundaries.  For rows that
-// are a whole number of slices (K a multiple of 2048) no lane ever idles.
-template <int B, int MT, int kWaves, int kR, int kStages = 3>
+// kWaves rows.  A wave works on kRPS of its rows at a time, each on 64 / kRPS
+// of its lanes (kRPS = 1: the whole wave on one row; kRPS = 2: lanes 0 .. 31
+// on one row and 32 .. 63 on the next), and cuts them into slices of 64 /
+// kRPS chunks per row that never span two rows (in a row's last slice the
+// lanes past its end idle).
+// Everything that locates a slice -- its rows, its place in them, its byte
+// offset -- is wave-uniform (each lane adds a constant), so the per-chunk work
+// is the load, the x reads and the dot products; each lane's chunk adds into
+// one running total, reduced across the row's lanes when the row's last slice
+// is done.  Loads run two slices ahead of the arithmetic, across row
+// boundaries.  No lane ever idles when the row's chunk count is a multiple of
+// 64 / kRPS (K a multiple of 2048 for kRPS = 1, of 1024 for kRPS = 2).
+template <int B, int MT, int kWaves, int kR, int kRPS = 1, int kStages = 3>
 __device__ __forceinline__ void gemv_rowslice_body(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
@@ -589,13 +592,18 @@ __device__ __forceinline__ void gemv_rowslice_body(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    static_assert(kRPS == 1 || kRPS == 2, "one or two rows per slice");
+    constexpr int kRowLanes = kWave / kRPS;  // lanes (and chunks per slice) of one row
+    const int half = lane / kRowLanes;       // which of the slice's rows this lane serves
+    const int rlane = lane % kRowLanes;
     const int32_t nchunks = (int32_t)(K / kChunk);
-    const int32_t spr = (int32_t)ceil_div((int64_t)nchunks, kSlice);  // slices per row
+    const int32_t spr = (int32_t)ceil_div((int64_t)nchunks, kRowLanes);  // slices per row
     const int64_t wrow0 = row0 + wave;  // the wave's first row; then every kWaves-th
     const int64_t wend = row0 + kWaves * rpw < N ? row0 + kWaves * rpw : N;
     const int32_t wrows = (int32_t)(wrow0 < wend ? (wend - wrow0 + kWaves - 1) / kWaves : 0);
+    const int32_t ngroups = (wrows + kRPS - 1) / kRPS;  // groups of kRPS rows
     // the workgroup's rows span below 2^31 bytes, so 32-bit offsets hold them
-    const int32_t nslices = wrows * spr;
+    const int32_t nslices = ngroups * spr;
     const uint32_t row_bytes = (uint32_t)(row_words * 4);
     const BufRef wbuf =
         uniform_buf(packed + (wrows > 0 ? wrow0 : 0) * row_words,
@@ -613,25 +621,28 @@ __device__ __forceinline__ void gemv_rowslice_body(
         xv[r] = make_uint4(d.x, d.y, d.z, d.w);
     }
 
-    // load position, wave-uniform: slices issued, the next slice's place in
-    // its row and the byte offset of its first chunk
-    const uint32_t lane_off = (uint32_t)(lane * B * 4);
-    int32_t ld_n = 0, ld_sir = 0;
+    // load position, wave-uniform: slices issued, the next slice's row group
+    // and place in its rows, and the byte offset of its first chunk (each lane
+    // adds its row's and its chunk's constant offset)
+    const uint32_t lane_off = (uint32_t)(half * kWaves) * row_bytes + (uint32_t)(rlane * B * 4);
+    int32_t ld_n = 0, ld_sir = 0, ld_grp = 0;
     uint32_t ld_row = 0, ld_off = 0;
     uint32_t w[kStages][B];
     int32_t sir_of[kStages];
     auto load_w = [&](auto S) {
         constexpr int st = decltype(S)::value;
-        const bool live = ld_n < nslices && lane < nchunks - ld_sir * kSlice;
+        const bool live = ld_n < nslices && rlane < nchunks - ld_sir * kRowLanes &&
+                          ld_grp * kRPS + half < wrows;
         buf_load_words<B>(wbuf, live ? ld_off + lane_off : kOutsideOffset, 0u, w[st]);
         sir_of[st] = ld_sir;
         ++ld_n;
         if (++ld_sir == spr) {
             ld_sir = 0;
-            ld_row += kWaves * row_bytes;
+            ++ld_grp;
+            ld_row += kRPS * kWaves * row_bytes;
             ld_off = ld_row;
         } else {
-            ld_off += kSlice * B * 4;
+            ld_off += kRowLanes * B * 4;
         }
     };
     static_for<kStages - 1>([&](auto S) { load_w(S); });
@@ -648,18 +659,18 @@ __device__ __forceinline__ void gemv_rowslice_body(
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    int32_t row = 0;  // the row of the slice being multiplied
-    const uint16_t* xlane = xs_dyn + lane * kXPitch;
+    int32_t grp = 0;  // the row group of the slice being multiplied
+    const uint16_t* xlane = xs_dyn + rlane * kXPitch;
     auto step = [&](auto S) {
         constexpr int st = decltype(S)::value;
         load_w(std::integral_constant<int, (st + kStages - 1) % kStages>{});
         const int32_t sir = sir_of[st];
-        if (lane < nchunks - sir * kSlice) {
+        if (rlane < nchunks - sir * kRowLanes) {
             uint32_t xw[MT][16];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const uint4* src =
-                    reinterpret_cast<const uint4*>(xlane + (m * nchunks + sir * kSlice) * kXPitch);
+                    reinterpret_cast<const uint4*>(xlane + (m * nchunks + sir * kRowLanes) * kXPitch);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint4 d = src[i];
@@ -671,23 +682,32 @@ __device__ __forceinline__ void gemv_rowslice_body(
             }
             chunk_product<B, MT, false>(w[st], 0, xw, acc);
         }
-        if (sir == spr - 1) {  // the row's last slice: reduce, scale, store
-            float v[MT];
+        if (sir == spr - 1) {  // the rows' last slice: reduce, scale, store
+            float v[kRPS][MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                v[m] = wave_sum(acc[m]);
+                if constexpr (kRPS == 1)
+                    v[0][m] = wave_sum(acc[m]);
+                else
+                    half_sums(acc[m], v[0][m], v[kRPS - 1][m]);
                 acc[m] = 0.0f;
             }
-            // the scale at a wave-uniform address in uniform control flow: a
-            // scalar load, which leaves the vector loads in flight alone
-            const int64_t n = wrow0 + (int64_t)row * kWaves;
-            const float s = scales[n];
-            if (lane == 0) {
+            // the scales at wave-uniform addresses in uniform control flow:
+            // scalar loads, which leave the vector loads in flight alone
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    if (m < M) y[(int64_t)m * N + n] = s * (v[m] * kUnscale);
+            for (int h = 0; h < kRPS; ++h) {
+                const int32_t r = grp * kRPS + h;
+                if (r < wrows) {
+                    const int64_t n = wrow0 + (int64_t)r * kWaves;
+                    const float s = scales[n];
+                    if (lane == 0) {
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+                            if (m < M) y[(int64_t)m * N + n] = s * (v[h][m] * kUnscale);
+                    }
+                }
             }
-            ++row;
+            ++grp;
         }
     };
     int32_t sl = 0;
