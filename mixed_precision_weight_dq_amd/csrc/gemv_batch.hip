@@ -369,7 +369,7 @@ hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipS
             int64_t r = ceil_div(g.N, wgs * kBatchWaves);
             r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
             mode = stream_mode(nchunks);
-            if (mode == kModeRowSlice2 && r > 1 && (r & 1))  // whole pairs of rows per wave
+            if (mode == kModeRowSlice2 && (r & 1))  // whole pairs of rows per wave (else half idles)
                 r = std::min<int64_t>(r + 1, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
             rpw = (int)r;
             nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
