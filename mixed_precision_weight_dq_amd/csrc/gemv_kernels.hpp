@@ -573,15 +573,15 @@ __device__ __forceinline__ void gemv_stream_body(
 // kWaves rows.  A wave works on kRPS of its rows at a time, each on 64 / kRPS
 // of its lanes (kRPS = 1: the whole wave on one row; kRPS = 2: lanes 0 .. 31
 // on one row and 32 .. 63 on the next), and cuts them into slices of 64 /
-// kRPS chunks per row that never span two rows (in a row's last slice the
-// lanes past its end idle).
+// kRPS chunks per row that never span two rows.  The row's chunk count must
+// be a multiple of 64 / kRPS (K a multiple of 2048 for kRPS = 1, of 1024 for
+// kRPS = 2), so every lane has a chunk in every slice.
 // Everything that locates a slice -- its rows, its place in them, its byte
 // offset -- is wave-uniform (each lane adds a constant), so the per-chunk work
 // is the load, the x reads and the dot products; each lane's chunk adds into
 // one running total, reduced across the row's lanes when the row's last slice
 // is done.  Loads run two slices ahead of the arithmetic, across row
-// boundaries.  No lane ever idles when the row's chunk count is a multiple of
-// 64 / kRPS (K a multiple of 2048 for kRPS = 1, of 1024 for kRPS = 2).
+// boundaries.
 template <int B, int MT, int kWaves, int kR, int kRPS = 1, int kStages = 3>
 __device__ __forceinline__ void gemv_rowslice_body(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
@@ -631,8 +631,7 @@ __device__ __forceinline__ void gemv_rowslice_body(
     int32_t sir_of[kStages];
     auto load_w = [&](auto S) {
         constexpr int st = decltype(S)::value;
-        const bool live = ld_n < nslices && rlane < nchunks - ld_sir * kRowLanes &&
-                          ld_grp * kRPS + half < wrows;
+        const bool live = ld_n < nslices && ld_grp * kRPS + half < wrows;
         buf_load_words<B>(wbuf, live ? ld_off + lane_off : kOutsideOffset, 0u, w[st]);
         sir_of[st] = ld_sir;
         ++ld_n;
@@ -665,7 +664,7 @@ __device__ __forceinline__ void gemv_rowslice_body(
         constexpr int st = decltype(S)::value;
         load_w(std::integral_constant<int, (st + kStages - 1) % kStages>{});
         const int32_t sir = sir_of[st];
-        if (rlane < nchunks - sir * kRowLanes) {
+        {
             uint32_t xw[MT][16];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
