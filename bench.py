@@ -257,6 +257,20 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
         for fn, a in calls:
             fn(*a)
 
+    # the same products as one dq_gemv_batched launch per token
+    tables = []
+    for t, X in enumerate(X1t):
+        arr = (dq.DQGemvItem * len(copies[t]))()
+        for i, (b, (P, S, Z)) in enumerate(copies[t].items()):
+            arr[i] = dq.DQGemvItem(X.data_ptr(), P.data_ptr(), S.data_ptr(), ys[b].data_ptr(), Nd, Kd,
+                                   b, 0, Z.data_ptr())
+        tables.append(arr)
+
+    def decode_batched():
+        for arr in tables:
+            if lib.dq_gemv_batched(ctypes.addressof(arr), len(arr), 1, cs):
+                raise RuntimeError("dq_gemv_batched failed")
+
     b6 = 6
     P6, S6, Z6 = dq.quantize_pack_asym(W4[b6], b6)
     Y = torch.empty((X4.shape[0], P6.shape[0]), dtype=torch.float32, device=X4.device)
@@ -265,18 +279,22 @@ def asym_context(torch, dq, stream, W2, X1t, W4, X4, reps: int):
         dq.gemm_asym(X4, P6, S6, Z6, X4.shape[1], b6, y=Y)
 
     t_q, t_d, t_g = timed(quant), timed(decode), timed(gemm)
+    t_b = timed(decode_batched)
     dec_bytes = len(X1t) * sum(Nd * Kd * b // 8 for b in W2)
     q_bytes = sum(Nd * Kd * (16 + b) // 8 for b in W2)
     M, K = X4.shape
     N = P6.shape[0]
     return {"quantize_pack_4096_gbs": round(q_bytes / (t_q * 1e-3) / 1e9, 1),
-            "gemv_m1_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
-            "gemv_m1_per_launch_us": round(t_d / (len(X1t) * len(W2)) * 1e3, 3),
+            "gemv_m1_gbs": round(dec_bytes / (t_b * 1e-3) / 1e9, 1),
+            "gemv_m1_per_launch_us": round(t_b / len(X1t) * 1e3, 3),
+            "gemv_m1_per_matrix_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
             "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
             "what": "asymmetric scheme on the step's inputs: quantize+pack (read + write bytes), "
-                    "decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed-weight "
-                    "GB/s), prefill GEMM M=2048 b=6; the products subtract each row's zero "
-                    "point from its codes; median of the step count, outside the timed steps"}
+                    "decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies, one "
+                    "dq_gemv_batched launch per token (packed-weight GB/s; per_matrix: one "
+                    "dq_gemv_asym launch per matrix), prefill GEMM M=2048 b=6; the products "
+                    "subtract each row's zero point from its codes; median of the step count, "
+                    "outside the timed steps"}
 
 
 def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 128):
@@ -326,6 +344,20 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
         for fn, a in calls:
             fn(*a)
 
+    # the same products as one dq_gemv_batched launch per token
+    tables = []
+    for t, X in enumerate(X1t):
+        arr = (dq.DQGemvItem * len(copies[t]))()
+        for i, (b, (P, S)) in enumerate(copies[t].items()):
+            arr[i] = dq.DQGemvItem(X.data_ptr(), P.data_ptr(), S.data_ptr(), ys[b].data_ptr(), Nd, Kd,
+                                   b, group, 0)
+        tables.append(arr)
+
+    def decode_batched():
+        for arr in tables:
+            if lib.dq_gemv_batched(ctypes.addressof(arr), len(arr), 1, cs):
+                raise RuntimeError("dq_gemv_batched failed")
+
     def decode16():
         for fn, a in calls16:
             fn(*a)
@@ -341,6 +373,7 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
         dq.gemm_group(X4, P6, S6, X4.shape[1], 6, group, Y)
 
     t_q, t_d, t_g = timed(quant), timed(decode), timed(gemm)
+    t_b = timed(decode_batched)
     t_16, t_16s = timed(decode16), timed(decode16_sym)
     G = -(-Kd // group)
     dec_bytes = len(X1t) * sum(Nd * (Kd * b // 8 + G * 4) for b in W2)
@@ -350,14 +383,16 @@ def group_context(torch, dq, stream, W2, X1t, W4, X4, reps: int, group: int = 12
     N = P6.shape[0]
     return {"group": group,
             "quantize_pack_4096_gbs": round(q_bytes / (t_q * 1e-3) / 1e9, 1),
-            "gemv_m1_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
-            "gemv_m1_per_launch_us": round(t_d / len(calls) * 1e3, 3),
+            "gemv_m1_gbs": round(dec_bytes / (t_b * 1e-3) / 1e9, 1),
+            "gemv_m1_per_launch_us": round(t_b / len(tables) * 1e3, 3),
+            "gemv_m1_per_matrix_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
             "gemv_m16_packed_gbs": round(payload / (t_16 * 1e-3) / 1e9, 1),
             "gemv_m16_per_row_scales_packed_gbs": round(payload / (t_16s * 1e-3) / 1e9, 1),
             "gemm_2048_b6_tflops": round(2.0 * M * N * K / (t_g * 1e-3) / 1e12, 1),
             "what": "group-wise scales (g=128) on the step's inputs: quantize+pack (read + write "
-                    "bytes), decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies (packed "
-                    "words + group scales per second), the same at M=16 (packed words per second; "
+                    "bytes), decode GEMV M=1 over 8 tokens x b=4..8 on rotated copies, one "
+                    "dq_gemv_batched launch per token (packed words + group scales per second; "
+                    "per_matrix: one dq_gemv_group launch per matrix), the same at M=16 (packed words per second; "
                     "beside it the per-row scheme on the same matrices), prefill GEMM M=2048 b=6 (pipelined 128-row tiles, each group folded in as it ends); "
                     "median of the step count, outside the timed steps"}
 

@@ -211,28 +211,36 @@ dq_status dq_gemv(const uint16_t* x, int64_t M, const uint32_t* packed, const fl
  * hardware; at decode sizes one launch per matrix costs about as much as the
  * matrix's transfer, so the matrices a token multiplies share a launch).
  * For each item i: y_i[m,n] = s_i[n] * sum_k x_i[m,k] q_i[n,k], exactly as
- * dq_gemv on that item (same validation, layouts and tolerance).
+ * dq_gemv on that item (same validation, layouts and tolerance); an item with
+ * zero points (`zeros` non-NULL) is served as dq_gemv_asym, one with group
+ * scales (`group` non-zero) as dq_gemv_group.
  *   items  in   HOST array of `count` descriptors, 1 <= count <=
  *               DQ_GEMV_BATCH_MAX; read during the call only (the library
  *               copies them into the kernel arguments)
  *   M           rows of every item's x, 1 <= M <= DQ_GEMV_MAX_M
  * Items may share x, packed and scales; no y may overlap another item's y or
- * any input.  With M <= 2, every item whose K is a multiple of 32 and whose x
- * fits the LDS (M * K / 32 * 80 bytes <= 48 KB) runs in ONE kernel launch
- * (workgroups of all such items in one grid, widths mixed); with
- * 3 <= M <= 16, every item whose K is a multiple of 32 does (each item's
- * outputs then equal dq_gemv's bit for bit).  Each other item runs as its
- * own dq_gemv launch.  Argument errors in any item are returned before
+ * any input.  With M <= 2, the items of one scheme (symmetric, zero points,
+ * group scales) whose K is a multiple of 32 and whose x fits the LDS
+ * (M * K / 32 * 80 bytes <= 48 KB) run in ONE kernel launch per scheme
+ * (workgroups of all such items in one grid, widths mixed), except items with
+ * zero points or group scales whose rows hold 64 chunks or more but not a
+ * multiple of 32 chunks; with 3 <= M <= 16, every symmetric item whose K is a
+ * multiple of 32 does (its outputs then equal dq_gemv's bit for bit).  Each
+ * other item runs as its own launch of the matching one-matrix entry point.
+ * Argument errors in any item (including a `group` that is not 0 or a power of
+ * two in [32, 2048], or `zeros` and `group` both set) are returned before
  * anything is enqueued. */
 #define DQ_GEMV_BATCH_MAX 32
 typedef struct {
     const uint16_t* x;       /* device, [M, K] bf16 bits, 16-byte aligned        */
-    const uint32_t* packed;  /* device, [N, row_words] (dq_quantize_pack), 16 B  */
-    const float* scales;     /* device, [N] fp32, 4-byte aligned                  */
+    const uint32_t* packed;  /* device, [N, row_words] (a dq_quantize_pack* call), 16 B */
+    const float* scales;     /* device, [N] fp32 ([N, ceil(K / group)] with group), 4 B */
     float* y;                /* device, [M, N] fp32 out, 4-byte aligned           */
     int64_t N;
     int64_t K;
     int32_t bits;            /* 2 .. 15 */
+    int32_t group;           /* 0: a scale per row; else codes per group scale    */
+    const int32_t* zeros;    /* NULL, or device [N] zero points (dq_quantize_pack_asym) */
 } dq_gemv_item;
 
 dq_status dq_gemv_batched(const dq_gemv_item* items, int32_t count, int64_t M, void* stream);

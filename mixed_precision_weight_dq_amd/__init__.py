@@ -70,7 +70,7 @@ class DQGemvItem(ctypes.Structure):
     """``dq_gemv_item`` of include/dq.h (device addresses and sizes)."""
     _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("bits", ctypes.c_int32)]
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("zeros", ctypes.c_void_p)]
 
 
 GEMV_BATCH_MAX = 32
@@ -584,32 +584,47 @@ def gemv(x, packed, scales, K: int, bits: int, y=None):
 
 def gemv_batched(items, ys=None):
     """Several decode products in one call: items is a list of (x, packed,
-    scales, K, bits) (bf16 x [M, K] with the same M for all; x and weights may
-    be shared between items); returns the list of y [M, N] (or fills ``ys``).
-    Items with K a multiple of 32 share one launch (at M <= 2 also x within
-    the LDS); the others run as one dq_gemv launch each."""
+    scales, K, bits), optionally followed by zeros (int32 [N] zero points of
+    asymmetric codes, or None) and group (codes per group scale, scales then
+    [N, ceil(K / group)]; 0 for a scale per row); bf16 x [M, K] with the same
+    M for all; x and weights may be shared between items.  Returns the list of
+    y [M, N] (or fills ``ys``).  The items of each scheme that fit one launch
+    share it; the others run as one launch each of their scheme's entry point."""
     torch = _torch()
     if not 1 <= len(items) <= GEMV_BATCH_MAX:
         raise ValueError("1 to %d items" % GEMV_BATCH_MAX)
     arr = (DQGemvItem * len(items))()
     out = []
     M = None
-    for i, (x, packed, scales, K, bits) in enumerate(items):
+    for i, item in enumerate(items):
+        if not 5 <= len(item) <= 7:
+            raise ValueError("item %d: (x, packed, scales, K, bits[, zeros[, group]])" % i)
+        x, packed, scales, K, bits = item[:5]
+        zeros = item[5] if len(item) > 5 else None
+        group = item[6] if len(item) > 6 else 0
         _need(x, "x", (torch.bfloat16,), 2)
         _need(packed, "packed", (torch.int32,), 2)
-        _need(scales, "scales", (torch.float32,), 1)
         N = packed.shape[0]
+        if group:
+            _need(scales, "scales", (torch.float32,), 2)
+            ok_scales = tuple(scales.shape) == (N, -(-K // group))
+        else:
+            _need(scales, "scales", (torch.float32,), 1)
+            ok_scales = scales.shape[0] == N
+        if zeros is not None:
+            _need(zeros, "zeros", (torch.int32,), 1)
+            ok_scales = ok_scales and zeros.shape[0] == N
         if M is None:
             M = x.shape[0]
         if x.shape[0] != M or x.shape[1] != K or \
-                packed.shape[1] != packed_row_bytes(K, bits) // 4 or scales.shape[0] != N:
-            raise ValueError("item %d: shape mismatch between x, packed, scales, K and bits" % i)
+                packed.shape[1] != packed_row_bytes(K, bits) // 4 or not ok_scales:
+            raise ValueError("item %d: shape mismatch between x, packed, scales, zeros, K and bits" % i)
         y = ys[i] if ys is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
         _need(y, "y", (torch.float32,), 2)
         if tuple(y.shape) != (M, N):
             raise ValueError("item %d: y must be [M, N]" % i)
         arr[i] = DQGemvItem(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), y.data_ptr(), N, K,
-                            bits)
+                            bits, group, zeros.data_ptr() if zeros is not None else 0)
         out.append(y)
     _check(dq_gemv_batched(ctypes.addressof(arr), len(items), M, _stream(items[0][0])),
            "dq_gemv_batched")

@@ -209,10 +209,11 @@ dq_status dq_gemv_batched(const dq_gemv_item* items, int32_t count, int64_t M, v
         if (!it.x || !it.packed || !it.scales || !it.y) return DQ_ERR_NULL;
         const dq_status st = check_common(it.N, it.K, it.bits);
         if (st != DQ_OK) return st;
+        if (it.group != 0 && (!valid_group(it.group) || it.zeros)) return DQ_ERR_SHAPE;
         if (!aligned(it.x, 16) || !aligned(it.packed, 16) || !aligned(it.scales, 4) ||
-            !aligned(it.y, 4))
+            !aligned(it.y, 4) || !aligned(it.zeros, 4))
             return DQ_ERR_ALIGN;
-        g[i] = dq::GemvItem{it.x, it.packed, it.scales, it.y, it.N, it.K, it.bits};
+        g[i] = dq::GemvItem{it.x, it.packed, it.scales, it.y, it.N, it.K, it.bits, it.group, it.zeros};
     }
     return hip_status(dq::launch_gemv_batched(g, count, M, static_cast<hipStream_t>(stream)));
 }

@@ -57,13 +57,16 @@ constexpr int kModeRowSlice2 = 4; // the same, two rows per slice (K % 1024 == 0
 struct BatchItemArgs {
     const uint16_t* x;
     const uint32_t* packed;
-    const float* scales;
+    const float* scales;   // [N], or [N, G] group scales
     float* y;
+    const int32_t* zeros;  // [N] zero points (asymmetric items)
     int32_t N;
     int32_t K;
     int32_t row_words;
-    int32_t code;  // M <= 2: 8 * bits + mode; M >= 3: 2 * bits + row tiles - 1
-    int32_t rpw;   // rows per wave (streaming modes)
+    int32_t code;   // M <= 2: 8 * bits + mode; M >= 3: 2 * bits + row tiles - 1
+    int32_t rpw;    // rows per wave (streaming modes)
+    int32_t G;      // group scales per row (group-scale items)
+    int32_t group;  // codes per group (group-scale items)
 };
 
 struct BatchArgs {
@@ -85,10 +88,31 @@ __device__ __forceinline__ const BatchArgs& batch_args()
     return *(const BatchArgs*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
+// The item's policy for the bodies: symmetric codes with a row scale,
+// asymmetric codes (a zero point per row) or group-wise scales.
+template <class ZP>
+__device__ __forceinline__ ZP item_policy(const BatchItemArgs& it);
+template <>
+__device__ __forceinline__ NoZeroPoints item_policy<NoZeroPoints>(const BatchItemArgs&)
+{
+    return NoZeroPoints{};
+}
+template <>
+__device__ __forceinline__ ZeroPoints item_policy<ZeroPoints>(const BatchItemArgs& it)
+{
+    return ZeroPoints{it.zeros};
+}
+template <>
+__device__ __forceinline__ GroupScales item_policy<GroupScales>(const BatchItemArgs& it)
+{
+    return GroupScales{it.scales, it.G, it.group};
+}
+
 // kMaxB: the widest code the instance serves.  Launches whose items are all
 // at most 8 bits take the narrow instance, whose register count (and so its
-// occupancy) is not set by the wide codes' bodies.
-template <int MT, int kMaxB>
+// occupancy) is not set by the wide codes' bodies.  ZP: the items' scheme (one
+// launch per scheme); the two-rows and stream modes serve symmetric items only.
+template <int MT, int kMaxB, class ZP>
 __global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(const BatchArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
@@ -99,38 +123,39 @@ __global__ __launch_bounds__(kBatchWaves * kWave) void gemv_xres_batch_kernel(co
     while (i + 1 < a.count && bid >= a.first[i + 1]) ++i;
     auto& it = a.item[i];
     const int64_t local = bid - a.first[i];
-    const NoZeroPoints zp{};
+    const ZP zp = item_policy<ZP>(it);
+    constexpr bool kSym = std::is_same<ZP, NoZeroPoints>::value;
     switch (it.code) {
 #define DQ_BATCH_CASE(B)                                                                          \
     case 8 * B + kModeRow:                                                                        \
         if constexpr (B <= kMaxB)                                                                 \
-            gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 1, true>(             \
+            gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, ZP, 1, true>(                       \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
                 xs_dyn);                                                                          \
         break;                                                                                    \
     case 8 * B + kModeTwoRows:                                                                    \
-        if constexpr (B <= kMaxB)                                                                 \
+        if constexpr (B <= kMaxB && kSym)                                                         \
             gemv_xres_body<B, MT, kBatchWaves, kBatchXPieces, NoZeroPoints, 2, true>(             \
-                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, zp, local,       \
-                xs_dyn);                                                                          \
+                it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y, NoZeroPoints{},  \
+                local, xs_dyn);                                                                   \
         break;                                                                                    \
     case 8 * B + kModeStream:                                                                     \
-        if constexpr (B <= kMaxB)                                                                 \
+        if constexpr (B <= kMaxB && kSym)                                                         \
             gemv_stream_body<B, MT, kBatchWaves, kBatchXPieces>(                                  \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
                 local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
         break;                                                                                    \
     case 8 * B + kModeRowSlice:                                                                   \
         if constexpr (B <= kMaxB)                                                                 \
-            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 1>(                             \
+            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 1, ZP>(                         \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
-                local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
+                local * kBatchWaves * it.rpw, it.rpw, xs_dyn, zp);                                \
         break;                                                                                    \
     case 8 * B + kModeRowSlice2:                                                                  \
         if constexpr (B <= kMaxB)                                                                 \
-            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 2>(                             \
+            gemv_rowslice_body<B, MT, kBatchWaves, kBatchXPieces, 2, ZP>(                         \
                 it.x, a.M, it.packed, it.scales, it.N, it.K, it.row_words, it.y,                  \
-                local * kBatchWaves * it.rpw, it.rpw, xs_dyn);                                    \
+                local * kBatchWaves * it.rpw, it.rpw, xs_dyn, zp);                                \
         break;
         DQ_BATCH_CASE(2)
         DQ_BATCH_CASE(3)
@@ -247,13 +272,32 @@ bool gemv_batch_eligible(int64_t M, int64_t K)
 
 namespace {
 
-// 3 <= M <= 16: eligible items' tiles in one grid (each item's tile height as
-// dq_gemv picks it), the rest one dq_gemv launch each
+// an item's scheme
+enum Scheme { kSymmetric = 0, kAsymmetric = 1, kGrouped = 2 };
+Scheme scheme_of(const GemvItem& g) { return g.zeros ? kAsymmetric : (g.group ? kGrouped : kSymmetric); }
+
+// an item on its own: the one-matrix entry point of its scheme
+hipError_t launch_alone(const GemvItem& g, int64_t M, hipStream_t stream)
+{
+    if (g.group) return launch_gemv_group(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.group, g.y, stream);
+    return launch_gemv(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.y, g.zeros, stream);
+}
+
+BatchItemArgs item_args(const GemvItem& g, int32_t code, int32_t rpw)
+{
+    return BatchItemArgs{g.x, g.packed, g.scales, g.y, g.zeros, (int32_t)g.N, (int32_t)g.K,
+                         (int32_t)packed_row_words(g.K, g.bits), code, rpw,
+                         (int32_t)(g.group ? ceil_div(g.K, g.group) : 0), (int32_t)g.group};
+}
+
+// 3 <= M <= 16: symmetric items with K a multiple of 32 in one grid (each
+// item's tile height as dq_gemv picks it), the rest one launch each
 hipError_t launch_gemv_batched_mfma(const GemvItem* items, int count, int64_t M, hipStream_t stream)
 {
+    auto joins = [&](const GemvItem& g) { return scheme_of(g) == kSymmetric && gemv_batch_eligible(M, g.K); };
     bool narrow = true;
     for (int i = 0; i < count; ++i)
-        if (gemv_batch_eligible(M, items[i].K) && items[i].bits > 8) narrow = false;
+        if (joins(items[i]) && items[i].bits > 8) narrow = false;
     BatchArgs a;
     a.M = (int32_t)M;
     int n = 0;
@@ -277,8 +321,8 @@ hipError_t launch_gemv_batched_mfma(const GemvItem* items, int count, int64_t M,
     };
     for (int i = 0; i < count; ++i) {
         const GemvItem& g = items[i];
-        if (!gemv_batch_eligible(M, g.K)) {  // this item takes its own launch
-            const hipError_t e = launch_gemv(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.y, nullptr, stream);
+        if (!joins(g)) {  // this item takes its own launch
+            const hipError_t e = launch_alone(g, M, stream);
             if (e != hipSuccess) return e;
             continue;
         }
@@ -288,8 +332,114 @@ hipError_t launch_gemv_batched_mfma(const GemvItem* items, int count, int64_t M,
             const hipError_t e = flush();
             if (e != hipSuccess) return e;
         }
-        a.item[n] = BatchItemArgs{g.x, g.packed, g.scales, g.y, (int32_t)g.N, (int32_t)g.K,
-                                  (int32_t)packed_row_words(g.K, g.bits), 2 * g.bits + nt - 1, 0};
+        a.item[n] = item_args(g, 2 * g.bits + nt - 1, 0);
+        a.first[n] = (int32_t)blocks;
+        blocks += nb;
+        ++n;
+    }
+    return flush();
+}
+
+template <int MT, class ZP>
+const void* xres_batch_kernel(bool narrow)
+{
+    return narrow ? reinterpret_cast<const void*>(&gemv_xres_batch_kernel<MT, 8, ZP>)
+                  : reinterpret_cast<const void*>(&gemv_xres_batch_kernel<MT, 15, ZP>);
+}
+
+// M <= 2: the items of one scheme (indices idx[0 .. count)) that fit the
+// launch, in one grid; the others one launch each
+template <class ZP>
+hipError_t launch_batched_xres(const GemvItem* items, const int* idx, int count, int64_t M,
+                               hipStream_t stream)
+{
+    constexpr bool kSym = std::is_same<ZP, NoZeroPoints>::value;
+    // the mode an item takes in the launch, or -1 for a launch of its own
+    auto mode_of = [&](const GemvItem& g) -> int {
+        if (!gemv_batch_eligible(M, g.K)) return -1;
+        const int64_t nchunks = g.K / kChunk;
+        if (nchunks < kSlice) return kSym && two_rows(nchunks) ? kModeTwoRows : kModeRow;
+        const int mode = stream_mode(nchunks);
+        return kSym || mode != kModeStream ? mode : -1;  // the stream body is symmetric only
+    };
+    // workgroups the GPU holds at once for this kernel (registers and LDS)
+    size_t lds = 0;
+    bool narrow = true;  // every item of the single launch at most 8 bits
+    for (int k = 0; k < count; ++k) {
+        const GemvItem& g = items[idx[k]];
+        if (mode_of(g) < 0) continue;
+        lds = std::max(lds, (size_t)(M * (g.K / kChunk) * kXPitch * 2));
+        if (g.bits > 8) narrow = false;
+    }
+    const void* kernel = M <= 1 ? xres_batch_kernel<1, ZP>(narrow) : xres_batch_kernel<2, ZP>(narrow);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBatchWaves * kWave, lds);
+    if (e != hipSuccess) return e;
+    // two rounds of the workgroups the GPU holds at once: the second round
+    // starts as the first one's workgroups end, which evens out their finish
+    const int64_t slots = (int64_t)std::max(1, cus) * std::max(1, per_cu) * 2;
+    double stream_bytes = 0;  // bytes of the streamed items, shared out over the slots
+    for (int k = 0; k < count; ++k) {
+        const GemvItem& g = items[idx[k]];
+        const int mode = mode_of(g);
+        if (mode == kModeStream || mode == kModeRowSlice || mode == kModeRowSlice2)
+            stream_bytes += (double)g.N * packed_row_words(g.K, g.bits) * 4;
+    }
+
+    BatchArgs a;
+    a.M = (int32_t)M;
+    int n = 0;
+    int64_t blocks = 0;
+    auto flush = [&]() -> hipError_t {
+        if (n == 0) return hipSuccess;
+        a.count = n;
+        a.first[n] = (int32_t)blocks;
+        const dim3 grid((unsigned)blocks), block(kBatchWaves * kWave);
+        if (M <= 1 && narrow)
+            gemv_xres_batch_kernel<1, 8, ZP><<<grid, block, lds, stream>>>(a);
+        else if (M <= 1)
+            gemv_xres_batch_kernel<1, 15, ZP><<<grid, block, lds, stream>>>(a);
+        else if (narrow)
+            gemv_xres_batch_kernel<2, 8, ZP><<<grid, block, lds, stream>>>(a);
+        else
+            gemv_xres_batch_kernel<2, 15, ZP><<<grid, block, lds, stream>>>(a);
+        n = 0;
+        blocks = 0;
+        return hipGetLastError();
+    };
+    for (int k = 0; k < count; ++k) {
+        const GemvItem& g = items[idx[k]];
+        const int mode = mode_of(g);
+        if (mode < 0) {  // this item takes its own launch
+            e = launch_alone(g, M, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        const int64_t rw = packed_row_words(g.K, g.bits);
+        int rpw = 1;
+        int64_t nb;
+        if (mode == kModeStream || mode == kModeRowSlice || mode == kModeRowSlice2) {
+            // this item's share of the workgroups, in proportion to its
+            // bytes; a workgroup's rows stay below 2^31 bytes
+            const double share = (double)g.N * rw * 4 / stream_bytes;
+            const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
+            const int64_t rmax = std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves));
+            int64_t r = std::min<int64_t>(ceil_div(g.N, wgs * kBatchWaves), rmax);
+            if (mode == kModeRowSlice2 && (r & 1))  // whole pairs of rows per wave (else half idles)
+                r = std::min<int64_t>(r + 1, rmax);
+            rpw = (int)r;
+            nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
+        } else {
+            nb = ceil_div(g.N, kBatchWaves * (mode == kModeTwoRows ? 2 : 1));
+        }
+        if (blocks + nb > 0x7fffffffLL) {  // the grid's index space is full: launch what we have
+            e = flush();
+            if (e != hipSuccess) return e;
+        }
+        a.item[n] = item_args(g, 8 * g.bits + mode, rpw);
         a.first[n] = (int32_t)blocks;
         blocks += nb;
         ++n;
@@ -302,93 +452,20 @@ hipError_t launch_gemv_batched_mfma(const GemvItem* items, int count, int64_t M,
 hipError_t launch_gemv_batched(const GemvItem* items, int count, int64_t M, hipStream_t stream)
 {
     if (M > 2) return launch_gemv_batched_mfma(items, count, M, stream);
-    // workgroups the GPU holds at once for this kernel (registers and LDS)
-    size_t lds = 0;
-    for (int i = 0; i < count; ++i)
-        if (gemv_batch_eligible(M, items[i].K))
-            lds = std::max(lds, (size_t)(M * (items[i].K / kChunk) * kXPitch * 2));
-    bool narrow = true;  // every item of the single launch at most 8 bits
-    for (int i = 0; i < count; ++i)
-        if (gemv_batch_eligible(M, items[i].K) && items[i].bits > 8) narrow = false;
-    const void* kernel =
-        M <= 1 ? (narrow ? reinterpret_cast<const void*>(&gemv_xres_batch_kernel<1, 8>)
-                         : reinterpret_cast<const void*>(&gemv_xres_batch_kernel<1, 15>))
-               : (narrow ? reinterpret_cast<const void*>(&gemv_xres_batch_kernel<2, 8>)
-                         : reinterpret_cast<const void*>(&gemv_xres_batch_kernel<2, 15>));
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBatchWaves * kWave, lds);
-    if (e != hipSuccess) return e;
-    // two rounds of the workgroups the GPU holds at once: the second round
-    // starts as the first one's workgroups end, which evens out their finish
-    const int64_t slots = (int64_t)std::max(1, cus) * std::max(1, per_cu) * 2;
-    double stream_bytes = 0;  // bytes of the streamed items, shared out over the slots
-    for (int i = 0; i < count; ++i)
-        if (gemv_batch_eligible(M, items[i].K) && items[i].K / kChunk >= kSlice)
-            stream_bytes += (double)items[i].N * packed_row_words(items[i].K, items[i].bits) * 4;
-
-    BatchArgs a;
-    a.M = (int32_t)M;
-    int n = 0;
-    int64_t blocks = 0;
-    auto flush = [&]() -> hipError_t {
-        if (n == 0) return hipSuccess;
-        a.count = n;
-        a.first[n] = (int32_t)blocks;
-        const dim3 grid((unsigned)blocks), block(kBatchWaves * kWave);
-        if (M <= 1 && narrow)
-            gemv_xres_batch_kernel<1, 8><<<grid, block, lds, stream>>>(a);
-        else if (M <= 1)
-            gemv_xres_batch_kernel<1, 15><<<grid, block, lds, stream>>>(a);
-        else if (narrow)
-            gemv_xres_batch_kernel<2, 8><<<grid, block, lds, stream>>>(a);
-        else
-            gemv_xres_batch_kernel<2, 15><<<grid, block, lds, stream>>>(a);
-        n = 0;
-        blocks = 0;
-        return hipGetLastError();
-    };
+    // one launch per scheme present, items in their given order within it
+    int idx[3][kGemvBatchMax];
+    int cnt[3] = {0, 0, 0};
     for (int i = 0; i < count; ++i) {
-        const GemvItem& g = items[i];
-        if (!gemv_batch_eligible(M, g.K)) {  // this item takes its own launch
-            e = launch_gemv(g.x, M, g.packed, g.scales, g.N, g.K, g.bits, g.y, nullptr, stream);
-            if (e != hipSuccess) return e;
-            continue;
-        }
-        const int64_t nchunks = g.K / kChunk;
-        const int64_t rw = packed_row_words(g.K, g.bits);
-        int mode, rpw = 1;
-        int64_t nb;
-        if (nchunks >= kSlice) {
-            // this item's share of the workgroups, in proportion to its
-            // bytes; a workgroup's rows stay below 2^31 bytes
-            const double share = (double)g.N * rw * 4 / stream_bytes;
-            const int64_t wgs = std::max<int64_t>(1, (int64_t)(share * (double)slots));
-            int64_t r = ceil_div(g.N, wgs * kBatchWaves);
-            r = std::min<int64_t>(r, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
-            mode = stream_mode(nchunks);
-            if (mode == kModeRowSlice2 && (r & 1))  // whole pairs of rows per wave (else half idles)
-                r = std::min<int64_t>(r + 1, std::max<int64_t>(1, 0x7fffffffLL / (rw * 4 * kBatchWaves)));
-            rpw = (int)r;
-            nb = ceil_div(g.N, (int64_t)kBatchWaves * rpw);
-        } else {
-            const bool two = two_rows(nchunks);
-            mode = two ? kModeTwoRows : kModeRow;
-            nb = ceil_div(g.N, kBatchWaves * (two ? 2 : 1));
-        }
-        if (blocks + nb > 0x7fffffffLL) {  // the grid's index space is full: launch what we have
-            e = flush();
-            if (e != hipSuccess) return e;
-        }
-        a.item[n] = BatchItemArgs{g.x, g.packed, g.scales, g.y, (int32_t)g.N, (int32_t)g.K,
-                                  (int32_t)rw, 8 * g.bits + mode, rpw};
-        a.first[n] = (int32_t)blocks;
-        blocks += nb;
-        ++n;
+        const int sc = scheme_of(items[i]);
+        idx[sc][cnt[sc]++] = i;
     }
-    return flush();
+    hipError_t e = hipSuccess;
+    if (cnt[kSymmetric]) e = launch_batched_xres<NoZeroPoints>(items, idx[kSymmetric], cnt[kSymmetric], M, stream);
+    if (e == hipSuccess && cnt[kAsymmetric])
+        e = launch_batched_xres<ZeroPoints>(items, idx[kAsymmetric], cnt[kAsymmetric], M, stream);
+    if (e == hipSuccess && cnt[kGrouped])
+        e = launch_batched_xres<GroupScales>(items, idx[kGrouped], cnt[kGrouped], M, stream);
+    return e;
 }
 
 }  // namespace dq

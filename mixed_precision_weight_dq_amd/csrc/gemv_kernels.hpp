@@ -581,13 +581,19 @@ __device__ __forceinline__ void gemv_stream_body(
 // is the load, the x reads and the dot products; each lane's chunk adds into
 // one running total, reduced across the row's lanes when the row's last slice
 // is done.  Loads run two slices ahead of the arithmetic, across row
-// boundaries.
-template <int B, int MT, int kWaves, int kR, int kRPS = 1, int kStages = 3>
+// boundaries.  The policy ZP: NoZeroPoints (the row scale times the reduced
+// sum), ZeroPoints (each code's row zero point, loaded with the slice's codes,
+// is taken off before it meets x) or GroupScales (each chunk's sum times its
+// group's scale, loaded with the codes; no row scale).
+template <int B, int MT, int kWaves, int kR, int kRPS = 1, class ZP = NoZeroPoints, int kStages = 3>
 __device__ __forceinline__ void gemv_rowslice_body(
     const uint16_t* __restrict__ x, int M, const uint32_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t N, int64_t K, int64_t row_words,
-    float* __restrict__ y, int64_t row0, int64_t rpw, uint16_t* __restrict__ xs_dyn)
+    float* __restrict__ y, int64_t row0, int64_t rpw, uint16_t* __restrict__ xs_dyn,
+    ZP zp = ZP{})
 {
+    constexpr bool kAsym = ZP::kAsym;
+    constexpr bool kGroup = is_group_scales<ZP>::value;
     constexpr int kThreads = kWaves * kWave;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -629,10 +635,27 @@ __device__ __forceinline__ void gemv_rowslice_body(
     uint32_t ld_row = 0, ld_off = 0;
     uint32_t w[kStages][B];
     int32_t sir_of[kStages];
+    // per lane, the zero point of its row (ZeroPoints) or the scale of its
+    // chunk's group (GroupScales), loaded with the slice's codes
+    [[maybe_unused]] uint32_t pol[kStages];
+    [[maybe_unused]] int gshift = 0;  // log2 of the chunks per group
+    if constexpr (kGroup) gshift = __builtin_ctzll((unsigned long long)(zp.group / kChunk));
     auto load_w = [&](auto S) {
         constexpr int st = decltype(S)::value;
         const bool live = ld_n < nslices && ld_grp * kRPS + half < wrows;
         buf_load_words<B>(wbuf, live ? ld_off + lane_off : kOutsideOffset, 0u, w[st]);
+        if constexpr (kAsym || kGroup) {
+            // the lane's row (one of the wave's; a row of the matrix when not live)
+            const int32_t r = live ? ld_grp * kRPS + half : 0;
+            const int64_t nr = wrow0 + (int64_t)r * kWaves;
+            const int64_t n = nr < N ? nr : N - 1;
+            if constexpr (kAsym) {
+                pol[st] = (uint32_t)zp.zero(n);
+            } else {
+                const int32_t c = ld_sir * kRowLanes + rlane;  // the lane's chunk in the row
+                pol[st] = __float_as_uint(zp.scales[n * zp.G + (c >> gshift)]);
+            }
+        }
         sir_of[st] = ld_sir;
         ++ld_n;
         if (++ld_sir == spr) {
@@ -654,7 +677,7 @@ __device__ __forceinline__ void gemv_rowslice_body(
     }
     __syncthreads();
 
-    constexpr float kUnscale = product_unscale<B, false>();
+    constexpr float kUnscale = product_unscale<B, kAsym>();
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
@@ -679,7 +702,19 @@ __device__ __forceinline__ void gemv_rowslice_body(
                     xw[m][4 * i + 3] = d.w;
                 }
             }
-            chunk_product<B, MT, false>(w[st], 0, xw, acc);
+            if constexpr (kGroup) {  // the chunk's sum, scaled by its group's scale
+                float part[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) part[m] = 0.0f;
+                chunk_product<B, MT, false>(w[st], 0, xw, part);
+                const float sg = __uint_as_float(pol[st]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = fmaf(part[m], sg, acc[m]);
+            } else if constexpr (kAsym) {
+                chunk_product<B, MT, true>(w[st], (int32_t)pol[st], xw, acc);
+            } else {
+                chunk_product<B, MT, false>(w[st], 0, xw, acc);
+            }
         }
         if (sir == spr - 1) {  // the rows' last slice: reduce, scale, store
             float v[kRPS][MT];
@@ -698,7 +733,7 @@ __device__ __forceinline__ void gemv_rowslice_body(
                 const int32_t r = grp * kRPS + h;
                 if (r < wrows) {
                     const int64_t n = wrow0 + (int64_t)r * kWaves;
-                    const float s = scales[n];
+                    const float s = kGroup ? 1.0f : scales[n];
                     if (lane == 0) {
 #pragma unroll
                         for (int m = 0; m < MT; ++m)

@@ -50,6 +50,8 @@ struct GemvItem {
     int64_t N;
     int64_t K;
     int bits;
+    int64_t group;          // 0: a scale per row; else codes per group (scales [N, ceil(K / group)])
+    const int32_t* zeros;  // nullptr, or [N] zero points (asymmetric codes; group 0)
 };
 constexpr int kGemvBatchMax = 32;  // items per call (DQ_GEMV_BATCH_MAX)
 // Whether an item of this shape joins the single launch (else it gets its own).

@@ -232,5 +232,18 @@ def test_gemv_batched_arguments_rejected():
                                  ("N", 0, dq.DQ_ERR_SHAPE), ("K", 0, dq.DQ_ERR_SHAPE),
                                  ("K", (1 << 22) + 1, dq.DQ_ERR_SHAPE), ("N", 1 << 31, dq.DQ_ERR_SHAPE),
                                  ("x", MIS, dq.DQ_ERR_ALIGN), ("packed", MIS, dq.DQ_ERR_ALIGN),
-                                 ("scales", A + 2, dq.DQ_ERR_ALIGN), ("y", A + 2, dq.DQ_ERR_ALIGN)):
+                                 ("scales", A + 2, dq.DQ_ERR_ALIGN), ("y", A + 2, dq.DQ_ERR_ALIGN),
+                                 ("group", 16, dq.DQ_ERR_SHAPE), ("group", 96, dq.DQ_ERR_SHAPE),
+                                 ("group", 4096, dq.DQ_ERR_SHAPE), ("zeros", A + 2, dq.DQ_ERR_ALIGN)):
         assert f(addr(_items(5, **{"4_" + field: value})), 5, 1) == status, (field, value)
+    # zero points and group scales together: no such scheme
+    assert f(addr(_items(3, **{"2_group": 64, "2_zeros": A})), 3, 1) == dq.DQ_ERR_SHAPE
+
+
+def test_gemv_item_layout():
+    """dq_gemv_item's fields sit where include/dq.h puts them (the binding's
+    ctypes mirror of the struct)."""
+    off = {name: getattr(dq.DQGemvItem, name).offset for name, _ in dq.DQGemvItem._fields_}
+    assert off == {"x": 0, "packed": 8, "scales": 16, "y": 24, "N": 32, "K": 40, "bits": 48,
+                   "group": 52, "zeros": 56}
+    assert ctypes.sizeof(dq.DQGemvItem) == 64

@@ -168,3 +168,94 @@ def test_batched_layer_shapes(M):
         o_p, o_s = oracle_rows(W_rows[(K, b, P.data_ptr())], rows, P, S, b)
         y_ref, bound = oracle.matmul(x, o_p, o_s, len(rows), K, b)
         assert within_tolerance(y.cpu().numpy()[:, rows], y_ref, bound).all()
+
+
+# (N, K, bits, scheme, group): scheme "a" zero points, "g" group scales, "s"
+# symmetric; the row-sliced bodies (one and two rows per slice), the
+# resident-x body, wide codes and items that take a launch of their own
+VARIANTS = [(200, 4096, 5, "a", 0), (130, 5120, 7, "a", 0), (64, 1024, 4, "a", 0),
+            (50, 2080, 6, "a", 0), (20, 4096, 12, "a", 0), (91, 3072, 8, "a", 0),
+            (200, 4096, 6, "g", 128), (130, 5120, 5, "g", 64), (64, 1024, 8, "g", 256),
+            (50, 2080, 6, "g", 32), (40, 6144, 9, "g", 2048), (33, 4096, 15, "g", 32),
+            (300, 4096, 6, "s", 0), (77, 2080, 5, "s", 0)]
+
+
+def variant_weights(seed, N, K, scheme):
+    """bf16 weights: for zero points, rows moved off zero (every fifth
+    non-negative) with every third row sparse -- one positive element, the rest
+    zero (z = 0), where a fold through sum_k x would cancel; returns the
+    weights and the sparse rows' non-zero positions."""
+    rng = np.random.default_rng(seed)
+    wf = workload.bf16_to_f32(workload.weights(65, seed, N, K, dtype="bf16"))
+    pos = {}
+    if scheme == "a":
+        wf = wf + rng.uniform(-0.04, 0.04, N).astype(np.float32)[:, None]
+        wf[::5] = np.abs(wf[::5])
+        for n in range(1, N, 3):
+            p = int(rng.integers(0, K))
+            v = abs(float(wf[n, p])) + 0.01
+            wf[n] = 0.0
+            wf[n, p] = v
+            pos[n] = p
+    return workload.bf16_from_f32(wf.astype(np.float32)), pos
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_batched_zero_points_and_group_scales(M):
+    """Items with zero points and with group scales beside symmetric ones in
+    one call (one launch per scheme): each output within the bar of the
+    oracle's own product (sparse asymmetric rows with small activations at
+    their one non-zero included), the same bits on every call, and the same
+    bits as the scheme's one-matrix entry point for the items that do not
+    stream."""
+    t = torch()
+    items, meta = [], []
+    for i, (N, K, bits, scheme, g) in enumerate(VARIANTS):
+        seed = 7000 + 100 * M + i
+        w, pos = variant_weights(seed, N, K, scheme)
+        x = workload.activations(66, seed, M, K)
+        if pos:  # small activations at the sparse rows' non-zeros
+            cols = np.array(sorted(set(pos.values())))
+            xf = workload.bf16_to_f32(x)
+            rng = np.random.default_rng(seed)
+            xf[:, cols] = (rng.uniform(0.005, 0.05, (M, len(cols))) *
+                           rng.choice([-1.0, 1.0], (M, len(cols)))).astype(np.float32)
+            x = workload.bf16_from_f32(xf)
+        X = bf16_gpu(x)
+        if scheme == "a":
+            o_p, o_s, o_z, _ = oracle.quantize_pack_asym(w, bits)
+            Z = t.from_numpy(o_z).cuda()
+            item = (X, t.from_numpy(o_p.view(np.int32)).cuda(), t.from_numpy(o_s).cuda(), K, bits, Z)
+            ref = oracle.matmul_asym(x, o_p, o_s, o_z, N, K, bits)
+        elif scheme == "g":
+            o_p, o_s, _ = oracle.quantize_pack_group(w, bits, g)
+            item = (X, t.from_numpy(o_p.view(np.int32)).cuda(), t.from_numpy(o_s).cuda(), K, bits, None, g)
+            ref = oracle.matmul_group(x, o_p, o_s, N, K, bits, g)
+        else:
+            o_p, o_s, _ = oracle.quantize_pack(w, bits)
+            item = (X, t.from_numpy(o_p.view(np.int32)).cuda(), t.from_numpy(o_s).cuda(), K, bits)
+            ref = oracle.matmul(x, o_p, o_s, N, K, bits)
+        items.append(item)
+        meta.append((N, K, bits, scheme, g, ref))
+    report("gemv_batched schemes M=%d items=%d" % (M, len(items)))
+    ys = dq.gemv_batched(items)
+    again = dq.gemv_batched(items)
+    singles = []
+    for (X, P, S, K, bits, *rest), (_, _, _, scheme, g, _) in zip(items, meta):
+        if scheme == "a":
+            singles.append(dq.gemv_asym(X, P, S, rest[0], K, bits))
+        elif scheme == "g":
+            singles.append(dq.gemv_group(X, P, S, K, bits, g))
+        else:
+            singles.append(dq.gemv(X, P, S, K, bits))
+    t.cuda.synchronize()
+    for i, ((N, K, bits, scheme, g, (y_ref, bound)), y, y2, y1) in enumerate(zip(meta, ys, again, singles)):
+        assert np.array_equal(f32_bits(y), f32_bits(y2)), "item %d not deterministic" % i
+        nch = K // 32
+        fits = M * nch * 80 <= 48 * 1024
+        streams = fits and nch >= 64 and (nch % 32 == 0 if scheme != "s" else True)
+        if not streams:
+            assert np.array_equal(f32_bits(y), f32_bits(y1)), "item %d differs from its entry point" % i
+        ok = within_tolerance(y.cpu().numpy(), y_ref, bound)
+        assert ok.all(), "item %d (%s b=%d N=%d K=%d g=%d): %d outputs out of tolerance" % (
+            i, scheme, bits, N, K, g, int((~ok).sum()))
