@@ -285,7 +285,8 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     for (int t = 0; t < 4; ++t) abase[t] = c * 8 + ((4 * h + t) ^ xswz(c));
 
     f32x16_t acc[kMT][kNT];
-    // group-wise scales: the current group's MFMAs accumulate here
+    // group-wise scales: the current group's MFMAs accumulate here (the
+    // group's first step starts them from zero)
     f32x16_t part[kGroup ? kMT : 1][kGroup ? kNT : 1];
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
@@ -293,14 +294,6 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if constexpr (kGroup) {
-#pragma unroll
-        for (int i = 0; i < kMT; ++i)
-#pragma unroll
-            for (int j = 0; j < kNT; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-    }
 
     // codes, ping-pong by step parity: stage st holds step ks (loaded during
     // step ks-1) and is expanded to MFMA operands at the top of step ks while
@@ -324,8 +317,17 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < kNT; ++j) buf_load_words<B>(wbuf, woff[j], (uint32_t)(ks * 8 * B), w[st][j]);
     };
-    auto step = [&](auto S, int64_t ks) {  // MFMAs of step ks from stage S
+    // group-wise scales: a group is 2^gsh whole steps (the group size is a
+    // power of two of at least 64 codes here)
+    [[maybe_unused]] int gsh = 0;
+    if constexpr (kGroup) gsh = __builtin_ctzll((unsigned long long)(zp.group / 64));
+    [[maybe_unused]] const int64_t gmask = ((int64_t)1 << gsh) - 1;
+    // kFirst: step ks opens a group, so its first MFMAs start from zero
+    // instead of the group sum (which therefore never needs clearing)
+    auto step = [&](auto S, int64_t ks, auto kFirst) __attribute__((always_inline)) {
+        // MFMAs of step ks from stage S
         constexpr int st = decltype(S)::value;
+        constexpr bool first = decltype(kFirst)::value;
         __syncthreads();  // step ks in LDS for every wave; stage st^1 free again
         // this step's group scales, loaded every step (unconditional loads
         // keep the compiler's waits counted) before the next step's prefetch
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < kNT; ++j) {
                 const int64_t n = n0 + wave * 32 * kNT + j * 32 + c;
-                sg[j] = zp.scales[(n < N ? n : N - 1) * zp.G + ks / (zp.group / 64)];
+                sg[j] = zp.scales[(n < N ? n : N - 1) * zp.G + (ks >> gsh)];
             }
         }
         bf16x8_t bh[4][kNT], bl[4][kNT];
@@ -365,24 +367,34 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
 #pragma unroll
                 for (int j = 0; j < kNT; ++j) {
                     f32x16_t& d = kGroup ? part[kGroup ? i : 0][kGroup ? j : 0] : acc[i][j];
-                    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[t][j], d, 0, 0, 0);
+                    const f32x16_t d0 = first && t == 0 ? f32x16_t{} : d;
+                    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bh[t][j], d0, 0, 0, 0);
                     if constexpr (kSplit)
                         d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t & 1][i], bl[t][j], d, 0, 0, 0);
                 }
         }
         store_x(std::integral_constant<int, st ^ 1>{});
         if constexpr (kGroup) {  // the group ends with this step: fold it in
-            if ((ks + 1) % (zp.group / 64) == 0 || ks + 1 == nk) {
+            if (((ks + 1) & gmask) == 0 || ks + 1 == nk) {
 #pragma unroll
                 for (int i = 0; i < kMT; ++i)
 #pragma unroll
                     for (int j = 0; j < kNT; ++j)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
+                        for (int r = 0; r < 16; ++r)
                             acc[i][j][r] = fmaf(sg[j], part[i][j][r], acc[i][j][r]);
-                            part[i][j][r] = 0.0f;
-                        }
             }
+        }
+    };
+    // step ks from stage S, as a group's first step when it opens one
+    auto run = [&](auto S, int64_t ks) __attribute__((always_inline)) {
+        if constexpr (kGroup) {
+            if ((ks & gmask) == 0)
+                step(S, ks, std::true_type{});
+            else
+                step(S, ks, std::false_type{});
+        } else {
+            step(S, ks, std::false_type{});
         }
     };
 
@@ -391,10 +403,10 @@ __global__ __launch_bounds__(256, kOcc) void gemm_mfma_kernel(
     store_x(std::integral_constant<int, 0>{});
     int64_t ks = 0;
     for (; ks + 2 <= nk; ks += 2) {
-        step(std::integral_constant<int, 0>{}, ks);
-        step(std::integral_constant<int, 1>{}, ks + 1);
+        run(std::integral_constant<int, 0>{}, ks);
+        run(std::integral_constant<int, 1>{}, ks + 1);
     }
-    if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
+    if (ks < nk) run(std::integral_constant<int, 0>{}, ks);
 
     // epilogue: lane (c, h) holds column c of each tile, rows 8*(r/4) + 4*h + r%4;
     // whole tiles store without bounds checks, as streaming stores
