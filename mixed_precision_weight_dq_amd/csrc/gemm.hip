@@ -746,7 +746,7 @@ hipError_t launch_gemm_b(const uint16_t* x, int64_t M, const uint32_t* packed, c
     if (K % 64 == 0) {
         // 256-row tiles with one workgroup per CU when they fill the 256 CUs
         // in whole rounds (at least 80 % of the last round busy)
-        constexpr int kWideNT = B <= 8 ? 2 : 1;
+        constexpr int kWideNT = 2;
         const int64_t wide = ceil_div(M, 256) * ceil_div(N, WideTile<kWideNT>::BN);
         if (M >= 256 && wide >= 256 && wide * 5 >= ceil_div(wide, 256) * 256 * 4)
             return launch_gemm_wide<B, kWideNT, DQ_WIDE_DEPTH>(x, M, packed, scales, N, K, y, zp, stream);

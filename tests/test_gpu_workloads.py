@@ -234,8 +234,8 @@ def test_big_gemm_ragged(bits):
 
 
 WIDE_CASES = [
-    # (M, N, K): 8 x 32 (or 8 x 64) tiles of 256 rows with ragged last row and
-    # column tiles and 7 or 8 K steps (one or two steps after the 3-step loop);
+    # (M, N, K): 8 x 32 tiles of 256 x 256 with ragged last row and column
+    # tiles and 7 or 8 K steps (one or two steps after the 3-step loop);
     # 6 x 42 tiles (no 4-tile grouping, tile count not a multiple of 8) and 9 steps
     (2000, 8100, 64 * 7),
     (2000, 8100, 64 * 8),
