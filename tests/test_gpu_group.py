@@ -123,9 +123,11 @@ def test_group_largest_k(bits):
 
 @pytest.mark.parametrize("bits", range(2, 16))
 def test_gemm_group_parity(bits):
+    # K = 320: five 64-code steps, so the pipelined kernel's last step runs
+    # after its two-step loop and g = 128, 2048 end in a partial group
     for g in (32, 64, 128, 2048):
         for i, (M, N, K) in enumerate([(1, 64, 64), (7, 129, 100), (200, 259, 517),
-                                       (257, 300, 2048)]):
+                                       (257, 300, 2048), (130, 200, 320)]):
             assert_group_product("gemm", M, N, K, bits, g, bits * 1000 + 500 + i + g)
 
 
