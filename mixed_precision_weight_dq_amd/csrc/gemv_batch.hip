@@ -11,16 +11,22 @@
 // memory is allocated or written besides the outputs).  Each workgroup finds
 // its item from a table of first-workgroup indices (a scalar scan over at most
 // 32 entries) and runs one of the bodies of gemv_kernels.hpp for the item's
-// width.  At M <= 2:
+// width.  At M <= 2 there is one launch per scheme present among the items
+// (per-row scales, zero points, group scales), the scheme a template policy of
+// the bodies:
 //   * rows of at least 64 chunks (K >= 2048): a streaming body.  The host
 //     gives each item a share of two rounds of workgroups (twice as many as
 //     the GPU holds at once) in proportion to its bytes, so each wave streams several
-//     rows with its loads running ahead across row boundaries (the row-sliced
-//     body when K is a multiple of 2048);
-//   * shorter rows: the resident-x body, one (or two) rows per wave.
+//     rows with its loads running ahead across row boundaries: the row-sliced
+//     body when K is a multiple of 2048 (one row per slice) or of 1024 (two
+//     rows per slice), else the stream body (per-row scales only; items of
+//     the other schemes with such K take a launch of their own);
+//   * shorter rows: the resident-x body, one (or, per-row scales, two) rows
+//     per wave.
 // At 3 <= M <= 16: the matrix-core body, one workgroup per row tile, as in
 // dq_gemv (so a layer's 5120-row matrices, 160 tiles each, fill the GPU
-// together where one alone leaves CUs idle).
+// together where one alone leaves CUs idle); items with zero points or group
+// scales take a launch of their own.
 // Per chunk the arithmetic is that of the one-matrix resident-x kernel, so
 // every output is within the same bound; the summation order differs only in
 // that the streaming body adds each chunk's dot product to the row total
