@@ -857,21 +857,28 @@ def main():
 
     # context for the GEMM figure, outside the timed steps: the plain bf16
     # library GEMM (torch.matmul -> hipBLASLt) on the same shape and GPU, with
-    # the dense bf16 weights the prefill matrices were quantized from
-    WT = W4[PREFILL["bits"][1]].t().contiguous()
-    for _ in range(3):
-        torch.matmul(X4, WT)
-    torch.cuda.synchronize()
-    lib_ms = []
-    for _ in range(7):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        torch.matmul(X4, WT)
-        e1.record(stream)
+    # the dense bf16 weights the prefill matrices were quantized from, in the
+    # operand layout of the packed weights (each output's weights contiguous
+    # along K: x @ W^T as a transposed view of W [N, K]) and, beside it, with
+    # W^T made contiguous ([K, N]), which the library runs with other kernels
+    def library_tflops(b_operand):
+        for _ in range(3):
+            torch.matmul(X4, b_operand)
         torch.cuda.synchronize()
-        lib_ms.append(e0.elapsed_time(e1))
-    lib_tflops = 2.0 * PREFILL["M"] * PREFILL["N"] * PREFILL["K"] / (float(np.median(lib_ms)) * 1e-3) / 1e12
-    del WT
+        lib_ms = []
+        for _ in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.matmul(X4, b_operand)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lib_ms.append(e0.elapsed_time(e1))
+        return 2.0 * PREFILL["M"] * PREFILL["N"] * PREFILL["K"] / (float(np.median(lib_ms)) * 1e-3) / 1e12
+    W6 = W4[PREFILL["bits"][1]]
+    lib_tflops = library_tflops(W6.t())
+    WT = W6.t().contiguous()
+    lib_nn_tflops = library_tflops(WT)
+    del WT, W6
 
     def gbs(kind, bits, N, K, read_bits, write_bits):
         """(read + write) bytes of the group's launches over the group time"""
@@ -938,8 +945,11 @@ def main():
             "per_launch_us": round(gemm_le9_ms * 1e3, 2),
             "library_bf16_reference": {
                 "tflops": round(lib_tflops, 1),
-                "what": "torch.matmul bf16 x[2048,8192] @ W^T[8192,8192] (hipBLASLt, bf16 output) on "
-                        "the same GPU in the same run, untimed by the steps",
+                "what": "torch.matmul bf16 x[2048,8192] @ W^T (W [8192,8192] row-major, the packed "
+                        "weights' layout, passed as a transposed view; hipBLASLt, bf16 output) on the "
+                        "same GPU in the same run, untimed by the steps",
+                "w_t_contiguous_tflops": round(lib_nn_tflops, 1),
+                "w_t_contiguous_what": "the same product with W^T made contiguous [8192,8192] first",
             },
         },
         "groups_ms": {kind: round(group_ms[kind], 5) for kind in kinds},
